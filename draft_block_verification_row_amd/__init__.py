@@ -1,0 +1,210 @@
+"""Python binding of libdspark_verify.so (gfx950 DSpark verify sampler).
+
+Argument marshalling only: every step of the verify path runs in the HIP
+kernels behind the C ABI of ``include/dspark_verify.h``.  PyTorch supplies
+device memory and the current stream.  There is no fallback: if the built
+library is missing, importing a function raises.
+
+bf16 tensors may be passed as ``torch.bfloat16`` or as 16-bit integer tensors
+holding the bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdspark_verify.so")
+
+DSPARK_F32 = 0
+DSPARK_BF16 = 1
+RACE_GROUP = 256
+MAX_K = 32
+
+
+class VerifyProblem(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("k", ctypes.c_int32), ("V", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("target_logits", ctypes.c_void_p), ("draft_logits", ctypes.c_void_p),
+        ("draft_tokens", ctypes.c_void_p), ("num_drafts", ctypes.c_void_p),
+        ("temperature", ctypes.c_void_p), ("W1", ctypes.c_void_p), ("W2t", ctypes.c_void_p),
+        ("anchor_tokens", ctypes.c_void_p), ("R", ctypes.c_int32), ("step", ctypes.c_uint32),
+        ("seed", ctypes.c_uint64),
+    ]
+
+
+class VerifyOutputs(ctypes.Structure):
+    _fields_ = [("accepted_len", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p), ("diag", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (built by ``python -m draft_block_verification_row_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m draft_block_verification_row_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i32, u32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_uint32
+        L.dspark_workspace_bytes.argtypes = [ctypes.POINTER(VerifyProblem)]
+        L.dspark_workspace_bytes.restype = sz
+        for name in ("dspark_verify_tokenwise", "dspark_verify_block"):
+            f = getattr(L, name)
+            f.argtypes = [ctypes.POINTER(VerifyProblem), ctypes.POINTER(VerifyOutputs), vp, sz, vp]
+            f.restype = i32
+        L.dspark_markov_bias.argtypes = [vp, vp, i32, i32, vp, i32, vp, i32, vp, vp]
+        L.dspark_markov_bias.restype = i32
+        L.dspark_adaptive_k.argtypes = [vp, vp, ctypes.c_float, i32, i32, i32, vp, i32, vp, vp, vp, vp]
+        L.dspark_adaptive_k.restype = i32
+        L.dspark_status_string.argtypes = [i32]
+        L.dspark_status_string.restype = ctypes.c_char_p
+        del u32
+        _lib = L
+    return _lib
+
+
+class DsparkError(RuntimeError):
+    pass
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise DsparkError(f"dspark status {status}: {lib().dspark_status_string(status).decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, shape, dtypes, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _problem(target, draft, draft_tokens, num_drafts, temperature, W1, W2t, anchor, seed, step):
+    if target.dim() != 3:
+        raise ValueError("target_logits must be [B, k+1, V]")
+    B, k1, V = target.shape
+    k = k1 - 1
+    dev = target.device
+    if target.dtype == torch.float32:
+        dt, dts = DSPARK_F32, (torch.float32,)
+    elif target.dtype in _BF16:
+        dt, dts = DSPARK_BF16, _BF16
+    else:
+        raise ValueError("logits must be float32 or bf16")
+    _need(target, "target_logits", (B, k + 1, V), dts, dev)
+    _need(draft, "draft_logits", (B, k, V), dts, dev)
+    _need(draft_tokens, "draft_tokens", (B, k), (torch.int32,), dev)
+    if num_drafts is not None:
+        _need(num_drafts, "num_drafts", (B,), (torch.int32,), dev)
+    if temperature is not None:
+        _need(temperature, "temperature", (B,), (torch.float32,), dev)
+    R = 0
+    if W1 is not None:
+        if W2t is None:
+            raise ValueError("W2t is required with W1")
+        R = int(W1.shape[1])
+        _need(W1, "W1", (V, R), _BF16, dev)
+        _need(W2t, "W2t", (V, R), _BF16, dev)
+    if anchor is not None:
+        _need(anchor, "anchor_tokens", (B,), (torch.int32,), dev)
+    p = VerifyProblem(B=B, k=k, V=V, dtype=dt, target_logits=_ptr(target), draft_logits=_ptr(draft),
+                      draft_tokens=_ptr(draft_tokens), num_drafts=_ptr(num_drafts),
+                      temperature=_ptr(temperature), W1=_ptr(W1), W2t=_ptr(W2t) if W1 is not None else None,
+                      anchor_tokens=_ptr(anchor), R=R, step=int(step) & 0xFFFFFFFF,
+                      seed=int(seed) & 0xFFFFFFFFFFFFFFFF)
+    return p, (B, k, V)
+
+
+def workspace_bytes(B: int, k: int, V: int, dtype: int = DSPARK_BF16) -> int:
+    p = VerifyProblem(B=B, k=k, V=V, dtype=dtype)
+    n = lib().dspark_workspace_bytes(ctypes.byref(p))
+    if n == 0:
+        raise ValueError("invalid problem sizes")
+    return int(n)
+
+
+def _verify(fname, target, draft, draft_tokens, num_drafts=None, temperature=None, W1=None, W2t=None,
+            anchor=None, seed=0, step=0, diag=False, workspace=None, out=None):
+    p, (B, k, V) = _problem(target, draft, draft_tokens, num_drafts, temperature, W1, W2t, anchor, seed, step)
+    dev = target.device
+    need = lib().dspark_workspace_bytes(ctypes.byref(p))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if out is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        toks = torch.empty(B, k + 1, dtype=torch.int32, device=dev)
+        dg = torch.empty(B, k + 1, 5, dtype=torch.float64, device=dev) if diag else None
+    else:
+        acc, toks, dg = out
+    o = VerifyOutputs(accepted_len=_ptr(acc), out_tokens=_ptr(toks), diag=_ptr(dg))
+    _check(getattr(lib(), fname)(ctypes.byref(p), ctypes.byref(o), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(dev)))
+    return acc, toks, dg
+
+
+def verify_tokenwise(target, draft, draft_tokens, **kw):
+    """Token-by-token verification; returns (accepted_len [B], out_tokens [B, k+1], diag or None)."""
+    return _verify("dspark_verify_tokenwise", target, draft, draft_tokens, **kw)
+
+
+def verify_block(target, draft, draft_tokens, **kw):
+    """Block verification; returns (accepted_len [B], out_tokens [B, k+1], diag or None)."""
+    return _verify("dspark_verify_block", target, draft, draft_tokens, **kw)
+
+
+def markov_bias(W1, W2t, prev_tokens, logits_in=None, out=None):
+    """out[i] = logits_in[i] + W1[prev_tokens[i]] . W2 (fp32 [rows, V])."""
+    dev = W1.device
+    V, R = W1.shape
+    rows = int(prev_tokens.shape[0])
+    _need(W1, "W1", (V, R), _BF16, dev)
+    _need(W2t, "W2t", (V, R), _BF16, dev)
+    _need(prev_tokens, "prev_tokens", (rows,), (torch.int32,), dev)
+    dt = DSPARK_F32
+    if logits_in is not None:
+        dt = DSPARK_F32 if logits_in.dtype == torch.float32 else DSPARK_BF16
+        _need(logits_in, "logits_in", (rows, V), (torch.float32,) + _BF16, dev)
+    if out is None:
+        out = torch.empty(rows, V, dtype=torch.float32, device=dev)
+    _need(out, "out", (rows, V), (torch.float32,), dev)
+    _check(lib().dspark_markov_bias(_ptr(W1), _ptr(W2t), V, R, _ptr(prev_tokens), rows, _ptr(logits_in), dt,
+                                    _ptr(out), _stream(dev)))
+    return out
+
+
+def adaptive_k(hidden, w, bias: float, verify_ms, want_c: bool = True):
+    """Confidence head + adaptive count; returns (n [B] int32, c [B, k], a [B, k])."""
+    dev = hidden.device
+    B, k, H = hidden.shape
+    _need(hidden, "hidden", (B, k, H), _BF16, dev)
+    _need(w, "w", (H,), _BF16, dev)
+    ms = (ctypes.c_float * len(verify_ms))(*[float(x) for x in verify_ms])
+    n = torch.empty(B, dtype=torch.int32, device=dev)
+    c = torch.empty(B, k, dtype=torch.float32, device=dev) if want_c else None
+    a = torch.empty(B, k, dtype=torch.float32, device=dev) if want_c else None
+    _check(lib().dspark_adaptive_k(_ptr(hidden), _ptr(w), float(bias), B, k, H, ctypes.cast(ms, ctypes.c_void_p),
+                                   len(verify_ms), _ptr(n), _ptr(c), _ptr(a), _stream(dev)))
+    return n, c, a

@@ -1,0 +1,188 @@
+// Host side of the C ABI declared in include/dspark_verify.h: argument checks,
+// workspace carve-up and the launches.  No allocation, no synchronisation.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/dspark_verify.h"
+#include "common.hpp"
+
+using namespace dspark;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool rank_ok(int R) { return R == 32 || R == 64 || R == 128 || R == 256; }
+
+// Offsets of every workspace region, in the order of dspark::Workspace.
+struct Layout {
+  size_t off[14];
+  size_t total;
+};
+
+Layout layout(int B, int k, int V) {
+  const size_t NG = (size_t)(V + kGroup - 1) / kGroup;
+  const size_t BT = (size_t)B * (k + 1), BD = (size_t)B * k;
+  const size_t sizes[14] = {
+      BT * NG * sizeof(float2),  // tpart
+      BD * NG * sizeof(float2),  // dpart
+      BD * NG * sizeof(float),   // wgrp
+      BT * sizeof(float),        // tm
+      BT * sizeof(double),       // tl2s
+      BD * sizeof(float),        // dm
+      BD * sizeof(double),       // dl2s
+      BT * sizeof(double),       // logP
+      BD * sizeof(double),       // lpx
+      BD * sizeof(double),       // lqx
+      (size_t)B * 4 * sizeof(int32_t),  // info
+      (size_t)B * sizeof(uint32_t),     // rowmask
+      BD * sizeof(int32_t),             // items
+      sizeof(int32_t),                  // nitems
+  };
+  Layout L;
+  size_t o = 0;
+  for (int i = 0; i < 14; ++i) {
+    L.off[i] = o;
+    o += align_up(sizes[i] > 0 ? sizes[i] : 1);
+  }
+  L.total = o;
+  return L;
+}
+
+bool problem_sizes_ok(const dspark_verify_problem* p) {
+  if (p == nullptr) return false;
+  if (p->B < 1 || p->k < 1 || p->k > DSPARK_MAX_K || p->V < 1) return false;
+  if (p->dtype != DSPARK_F32 && p->dtype != DSPARK_BF16) return false;
+  // row offsets are computed in size_t; the int32 token ids bound V
+  return true;
+}
+
+dspark_status verify_common(const dspark_verify_problem* p, const dspark_verify_outputs* o, void* ws,
+                            size_t ws_bytes, void* stream, int method) {
+  if (!problem_sizes_ok(p) || o == nullptr) return DSPARK_ERR_INVALID_ARG;
+  if (!p->target_logits || !p->draft_logits || !p->draft_tokens || !o->accepted_len || !o->out_tokens)
+    return DSPARK_ERR_INVALID_ARG;
+  if (p->W1 != nullptr) {
+    if (p->W2t == nullptr) return DSPARK_ERR_INVALID_ARG;
+    if (!rank_ok(p->R)) return DSPARK_ERR_UNSUPPORTED;
+    if (!aligned16(p->W1) || !aligned16(p->W2t)) return DSPARK_ERR_UNSUPPORTED;
+  }
+  const Layout L = layout(p->B, p->k, p->V);
+  if (ws == nullptr || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
+    return DSPARK_ERR_WORKSPACE;
+
+  Args a;
+  memset(&a, 0, sizeof(a));
+  a.B = p->B; a.k = p->k; a.V = p->V; a.R = p->W1 ? p->R : 0;
+  a.NG = (p->V + kGroup - 1) / kGroup;
+  a.dtype = p->dtype;
+  const int esz = p->dtype == DSPARK_BF16 ? 2 : 4;
+  a.vec_ok = ((size_t)p->V * esz) % 16 == 0 && aligned16(p->target_logits) && aligned16(p->draft_logits);
+  a.target = p->target_logits;
+  a.draft = p->draft_logits;
+  a.tokens = p->draft_tokens;
+  a.num_drafts = p->num_drafts;
+  a.temperature = p->temperature;
+  a.W1 = p->W1;
+  a.W2t = p->W1 ? p->W2t : nullptr;
+  a.anchor = p->anchor_tokens;
+  a.key0 = (uint32_t)(p->seed & 0xffffffffu);
+  a.key1 = (uint32_t)(p->seed >> 32);
+  a.step = p->step;
+  a.method = method;
+  a.accepted_len = o->accepted_len;
+  a.out_tokens = o->out_tokens;
+  a.diag = o->diag;
+  char* base = reinterpret_cast<char*>(ws);
+  a.ws.tpart = reinterpret_cast<float2*>(base + L.off[0]);
+  a.ws.dpart = reinterpret_cast<float2*>(base + L.off[1]);
+  a.ws.wgrp = reinterpret_cast<float*>(base + L.off[2]);
+  a.ws.tm = reinterpret_cast<float*>(base + L.off[3]);
+  a.ws.tl2s = reinterpret_cast<double*>(base + L.off[4]);
+  a.ws.dm = reinterpret_cast<float*>(base + L.off[5]);
+  a.ws.dl2s = reinterpret_cast<double*>(base + L.off[6]);
+  a.ws.logP = reinterpret_cast<double*>(base + L.off[7]);
+  a.ws.lpx = reinterpret_cast<double*>(base + L.off[8]);
+  a.ws.lqx = reinterpret_cast<double*>(base + L.off[9]);
+  a.ws.info = reinterpret_cast<int32_t*>(base + L.off[10]);
+  a.ws.rowmask = reinterpret_cast<uint32_t*>(base + L.off[11]);
+  a.ws.items = reinterpret_cast<int32_t*>(base + L.off[12]);
+  a.ws.nitems = reinterpret_cast<int32_t*>(base + L.off[13]);
+  if (launch_verify(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return DSPARK_ERR_HIP;
+  return DSPARK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dspark_workspace_bytes(const dspark_verify_problem* p) {
+  if (!problem_sizes_ok(p)) return 0;
+  return layout(p->B, p->k, p->V).total;
+}
+
+dspark_status dspark_verify_tokenwise(const dspark_verify_problem* p, const dspark_verify_outputs* o,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  return verify_common(p, o, ws, ws_bytes, stream, 0);
+}
+
+dspark_status dspark_verify_block(const dspark_verify_problem* p, const dspark_verify_outputs* o,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  return verify_common(p, o, ws, ws_bytes, stream, 1);
+}
+
+dspark_status dspark_markov_bias(const uint16_t* W1, const uint16_t* W2t, int32_t V, int32_t R,
+                                 const int32_t* prev_tokens, int32_t rows, const void* logits_in,
+                                 int32_t dtype, float* out, void* stream) {
+  if (!W1 || !W2t || !prev_tokens || !out || V < 1 || rows < 0) return DSPARK_ERR_INVALID_ARG;
+  if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return DSPARK_ERR_INVALID_ARG;
+  if (!rank_ok(R) || !aligned16(W1) || !aligned16(W2t)) return DSPARK_ERR_UNSUPPORTED;
+  if (rows == 0) return DSPARK_OK;
+  BiasArgs ba;
+  ba.W1 = W1; ba.W2t = W2t; ba.V = V; ba.R = R; ba.rows = rows; ba.dtype = dtype;
+  const int esz = dtype == DSPARK_BF16 ? 2 : 4;
+  ba.vec_ok = ((size_t)V * esz) % 16 == 0 && ((size_t)V * 4) % 16 == 0 && aligned16(out) &&
+              (logits_in == nullptr || aligned16(logits_in));
+  ba.prev = prev_tokens;
+  ba.logits_in = logits_in;
+  ba.out = out;
+  const int NG = (V + kGroup - 1) / kGroup;
+  if (launch_markov_bias(ba, NG, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return DSPARK_ERR_HIP;
+  return DSPARK_OK;
+}
+
+dspark_status dspark_adaptive_k(const uint16_t* hidden, const uint16_t* w, float bias, int32_t B, int32_t k,
+                                int32_t H, const float* verify_ms, int32_t n_ms, int32_t* n_out, float* c_out,
+                                float* a_out, void* stream) {
+  if (!hidden || !w || !verify_ms || !n_out || B < 1 || k < 1 || k > DSPARK_MAX_K || H < 1)
+    return DSPARK_ERR_INVALID_ARG;
+  if (n_ms < k + 2 || n_ms > kMaxMs) return DSPARK_ERR_INVALID_ARG;
+  AdaptArgs aa;
+  memset(&aa, 0, sizeof(aa));
+  aa.hidden = hidden; aa.w = w; aa.bias = bias; aa.B = B; aa.k = k; aa.H = H; aa.n_ms = n_ms;
+  aa.n_out = n_out; aa.c_out = c_out; aa.a_out = a_out;
+  for (int i = 0; i < n_ms; ++i) {
+    if (!(verify_ms[i] > 0.0f)) return DSPARK_ERR_INVALID_ARG;
+    aa.ms[i] = verify_ms[i];
+  }
+  if (launch_adaptive(aa, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return DSPARK_ERR_HIP;
+  return DSPARK_OK;
+}
+
+const char* dspark_status_string(dspark_status s) {
+  switch (s) {
+    case DSPARK_OK: return "ok";
+    case DSPARK_ERR_INVALID_ARG: return "invalid argument";
+    case DSPARK_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DSPARK_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case DSPARK_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

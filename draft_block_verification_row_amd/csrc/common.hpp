@@ -1,0 +1,196 @@
+// Device helpers for the gfx950 verify sampler: Philox4x32-10, logit loads,
+// wave64 cross-lane reductions and the workspace layout shared by the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+constexpr int kGroup = 256;        // vocab ids per race group (and per pass workgroup)
+constexpr int kWaveCols = 64;      // vocab ids per wave inside a group
+constexpr int kWaves = 4;          // waves per pass workgroup
+constexpr int kThreads = kWaves * 64;
+constexpr int kMaxK = 32;
+constexpr int kChunk = 16;         // rows per MFMA chunk
+
+constexpr double kLog2e = 1.4426950408889634074;
+constexpr double kLn2 = 0.69314718055994530942;
+
+enum Purpose : uint32_t { kPurposeDraft = 0, kPurposeAccept = 1, kPurposeRaceGroup = 2, kPurposeRaceItem = 3 };
+enum Dtype : int { kF32 = 0, kBF16 = 1 };
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of
+// (c0,c1,c2,c3) -> (hi(M1 c2)^c1^k0, lo(M1 c2), hi(M0 c0)^c3^k1, lo(M0 c0)),
+// the key advancing by the Weyl constants between rounds.  Only word 0 is used.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+    k0 += 0x9E3779B9u; k1 += 0xBB67AE85u;
+  }
+  return c0;
+}
+
+// Accept uniform u = ((x >> 8) + 1) * 2^-24, in (0, 1], exact in fp32 and fp64.
+__device__ __forceinline__ double accept_uniform(uint32_t k0, uint32_t k1, uint32_t b, uint32_t j, uint32_t step) {
+  const uint32_t x = philox_word0(b, j, kPurposeAccept, step, k0, k1);
+  return (double)((x >> 8) + 1u) * 0x1.0p-24;
+}
+
+// Exponential clock E = -ln(U), U = ((x >> 8) + 1/2) * 2^-24 in (0, 1), fp64.
+__device__ __forceinline__ double race_clock(uint32_t k0, uint32_t k1, uint32_t b, uint32_t idx,
+                                             uint32_t purpose, uint32_t step) {
+  const uint32_t x = philox_word0(b, idx, purpose, step, k0, k1);
+  const double U = ((double)(x >> 8) + 0.5) * 0x1.0p-24;
+  return -log(U);
+}
+
+// ---------------------------------------------------------------------------
+// Loads.  bf16 -> fp32 is a 16-bit shift.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// 16 consecutive logits of one row, columns [c0, c0+16), -inf beyond V.
+// `vec` says the row base is 16-byte aligned and V is a multiple of the vector width.
+template <int DT>
+__device__ __forceinline__ void load16(const void* __restrict__ row, int c0, int V, bool vec, float (&x)[16]) {
+  if (DT == kBF16) {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(row);
+    if (vec && c0 + 16 <= V) {
+      const uint4 a = *reinterpret_cast<const uint4*>(p + c0);
+      const uint4 b = *reinterpret_cast<const uint4*>(p + c0 + 8);
+      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { x[2 * i] = bf16lo(w[i]); x[2 * i + 1] = bf16hi(w[i]); }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = (c0 + i < V) ? bf16_to_f32(p[c0 + i]) : -INFINITY;
+    }
+  } else {
+    const float* p = reinterpret_cast<const float*>(row);
+    if (vec && c0 + 16 <= V) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 a = *reinterpret_cast<const float4*>(p + c0 + 4 * i);
+        x[4 * i] = a.x; x[4 * i + 1] = a.y; x[4 * i + 2] = a.z; x[4 * i + 3] = a.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = (c0 + i < V) ? p[c0 + i] : -INFINITY;
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float load1(const void* __restrict__ row, int c) {
+  if (DT == kBF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[c]);
+  return reinterpret_cast<const float*>(row)[c];
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane reductions inside the 4 lanes {n, n+16, n+32, n+48} of a wave.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float max4lanes(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float sum4lanes(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace (carved on the host, 256-byte aligned regions).
+// ---------------------------------------------------------------------------
+struct Workspace {
+  float2* tpart;      // [B*(k+1)][NG] target row group partials (raw max, sum 2^((l-m)c))
+  float2* dpart;      // [B*k][NG]     draft row group partials on biased logits
+  float* wgrp;        // [B*k][NG]     residual group masses of pass-2 rows
+  float* tm;          // [B*(k+1)]     target row max (raw logits)
+  double* tl2s;       // [B*(k+1)]     log2 of sum 2^((l-m)c)
+  float* dm;          // [B*k]         draft row max (biased logits)
+  double* dl2s;       // [B*k]
+  double* logP;       // [B*(k+1)]     log P_j (clipped prefix)
+  double* lpx;        // [B*k]         log p_j(x_j)
+  double* lqx;        // [B*k]         log q_j(x_j)
+  int32_t* info;      // [B*4]         gamma, stop (token-wise t / block provisional), f, flags
+  uint32_t* rowmask;  // [B]           pass-2 rows of each stream (bit i = slot i)
+  int32_t* items;     // [B*k]         compact pass-2 list of b*k + i
+  int32_t* nitems;    // [1]
+};
+
+struct Args {
+  int B, k, V, R, NG, dtype;
+  int vec_ok;                     // 1 if V is a multiple of the 16-byte vector width
+  const void* target;
+  const void* draft;
+  const int32_t* tokens;
+  const int32_t* num_drafts;
+  const float* temperature;
+  const uint16_t* W1;
+  const uint16_t* W2t;
+  const int32_t* anchor;
+  uint32_t key0, key1, step;
+  int method;                     // 0 token-wise, 1 block
+  int32_t* accepted_len;
+  int32_t* out_tokens;
+  double* diag;
+  Workspace ws;
+};
+
+__device__ __forceinline__ int stream_gamma(const Args& a, int b) {
+  if (a.num_drafts == nullptr) return a.k;
+  const int g = a.num_drafts[b];
+  return g < 0 ? 0 : (g > a.k ? a.k : g);
+}
+
+__device__ __forceinline__ float stream_temp(const Args& a, int b) {
+  return a.temperature == nullptr ? 1.0f : a.temperature[b];
+}
+
+__device__ __forceinline__ int clamp_tok(int x, int V) { return x < 0 ? 0 : (x >= V ? V - 1 : x); }
+
+// Previous token conditioning draft slot j of stream b (-1: no bias).
+__device__ __forceinline__ int draft_prev(const Args& a, int b, int j) {
+  int prev = (j == 0) ? (a.anchor ? a.anchor[b] : -1) : a.tokens[b * a.k + j - 1];
+  return (prev >= 0 && prev < a.V) ? prev : -1;
+}
+
+struct BiasArgs {
+  const uint16_t* W1;
+  const uint16_t* W2t;
+  int V, R, rows, dtype, vec_ok;
+  const int32_t* prev;
+  const void* logits_in;
+  float* out;
+};
+
+constexpr int kMaxMs = 256;
+struct AdaptArgs {
+  const uint16_t* hidden;
+  const uint16_t* w;
+  float bias;
+  int B, k, H, n_ms;
+  int32_t* n_out;
+  float* c_out;
+  float* a_out;
+  float ms[kMaxMs];
+};
+
+// launchers (kernels.hip)
+hipError_t launch_verify(const Args& a, hipStream_t st);
+hipError_t launch_markov_bias(const BiasArgs& ba, int NG, hipStream_t st);
+hipError_t launch_adaptive(const AdaptArgs& aa, hipStream_t st);
+
+}  // namespace dspark

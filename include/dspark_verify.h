@@ -1,0 +1,162 @@
+/*
+ * dspark_verify.h -- C ABI of the MI355X (gfx950) DSpark verify sampler.
+ *
+ * One speculative-decoding verify step for B streams, each carrying a block of
+ * draft tokens: the drafter's logits get the DSpark Markov-head bias, both sides
+ * are softmaxed, and either the token-by-token rule or block verification keeps
+ * a prefix of the drafts and emits one token of the target's own.
+ *
+ * Sources (page titles, with the section each entry point follows):
+ *   [P1] "MTP, DSpark and Block Verification, Explained" (al-engr.com)
+ *   [P2] "MTP Heads and Confidence Heads" (naphjohn.github.io LLM-blog, ep7)
+ *   [P3] "Teaching the Speculator What a Draft Costs" (al-engr.com)
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked "device" must be device memory of the current HIP device;
+ *     "host" pointers are read during the call only.  All tensors are dense,
+ *     row-major, with the shapes given.  bf16 values are raw 16-bit patterns.
+ *   - The caller owns every buffer, including the workspace.  The library never
+ *     allocates, frees or synchronises; all work is enqueued on `stream`
+ *     (a hipStream_t; NULL means the default stream) and completes in order.
+ *   - Host-checkable errors return a status and enqueue nothing.  A failed
+ *     launch returns DSPARK_ERR_HIP.  Device-data preconditions (token ids in
+ *     range, temperatures > 0, num_drafts in [0, k]) are the caller's: the
+ *     kernels clamp indices so that no access leaves its buffer, but outputs for
+ *     invalid data are unspecified.
+ *   - Same inputs, seed and step give bit-identical outputs on every run: no
+ *     reduction uses floating-point atomics.
+ *   - Random numbers are Philox4x32-10 (Salmon et al., SC'11) with key = seed
+ *     and counter = (global stream index, index, purpose, step): purpose 1 gives
+ *     the accept uniforms u_{b,j} = ((x >> 8) + 1) 2^-24, purposes 2 and 3 the
+ *     exponential clocks of the sampler.  Outputs do not depend on how streams
+ *     are batched or sharded.
+ */
+#ifndef DSPARK_VERIFY_H
+#define DSPARK_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSPARK_OK = 0,
+  DSPARK_ERR_INVALID_ARG = 1, /* NULL required pointer, non-positive size, k > 32 ... */
+  DSPARK_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. rank R not in {32,64,128,256}) */
+  DSPARK_ERR_WORKSPACE = 3,   /* workspace NULL, misaligned (256 B) or smaller than required */
+  DSPARK_ERR_HIP = 4          /* a HIP launch or device query failed */
+} dspark_status;
+
+typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
+
+/* Vocabulary group size of the two-level race sampler (ids [256g, 256g+256)). */
+#define DSPARK_RACE_GROUP 256
+/* Largest draft block the verify entry points accept. */
+#define DSPARK_MAX_K 32
+
+/*
+ * One verify problem.  Shapes follow the pages' statement of the step: the
+ * drafter proposes k tokens with their distributions, the target produces its
+ * own distribution at every draft position plus one more, and the sampler keeps
+ * a prefix and emits one target token [P1 §1 "One token per step"; P1 §4].
+ */
+typedef struct {
+  int32_t B;                      /* streams, >= 1                                          */
+  int32_t k;                      /* draft slots per stream, 1..32                           */
+  int32_t V;                      /* vocabulary size, >= 1                                   */
+  int32_t dtype;                  /* dspark_dtype of both logit tensors                      */
+  const void* target_logits;      /* device [B, k+1, V]; row j is the target at slot j given
+                                     x_<j, row gamma_b the bonus position                    */
+  const void* draft_logits;       /* device [B, k, V]: raw drafter logits, before the bias   */
+  const int32_t* draft_tokens;    /* device [B, k]: x_{b,j} in [0, V)                         */
+  const int32_t* num_drafts;      /* device [B]: gamma_b in [0, k] (ragged verify: only rows
+                                     0..gamma_b are read); NULL means gamma_b = k            */
+  const float* temperature;       /* device [B], > 0; NULL means 1.  Target logits and the
+                                     biased draft logits are both divided by T_b             */
+  const uint16_t* W1;             /* device bf16 [V, R]: Markov factor rows, indexed by the
+                                     previous token; NULL switches the bias off              */
+  const uint16_t* W2t;            /* device bf16 [V, R]: W2t[v, r] = W2[r, v], the [R, V]
+                                     factor stored as a linear layer keeps its weight        */
+  const int32_t* anchor_tokens;   /* device [B]: token before slot 0 (the last accepted one);
+                                     < 0 leaves slot 0 unbiased; NULL means all < 0         */
+  int32_t R;                      /* Markov rank: 32, 64, 128 or 256 (ignored if W1 NULL)    */
+  uint32_t step;                  /* Philox counter word: successive calls should differ    */
+  uint64_t seed;                  /* Philox key                                             */
+} dspark_verify_problem;
+
+typedef struct {
+  int32_t* accepted_len;          /* device [B]: drafts kept, s_b in [0, gamma_b]            */
+  int32_t* out_tokens;            /* device [B, k+1]: x_0..x_{s-1}, Y, then -1               */
+  double* diag;                   /* device [B, k+1, 5] or NULL: per slot j, (log p_j(x_j),
+                                     log q_j(x_j), P_j, R_j, h_j); NaN where not computed    */
+} dspark_verify_outputs;
+
+/* Bytes of workspace the two verify entry points need for this problem (host, pure).
+ * Returns 0 if the problem's sizes are invalid. */
+size_t dspark_workspace_bytes(const dspark_verify_problem* problem);
+
+/*
+ * Token-by-token verification (Leviathan et al.) [P1 §4 "Token by token"]:
+ * draft j is kept iff u_{b,j} <= min(1, p_j(x_j) / q_j(x_j)); at the first
+ * rejection t the emitted token is drawn from max(0, p_t - q_t) normalised, and
+ * when every draft survives from the bonus position p_gamma.
+ * q_j includes the Markov bias W1[prev_j] . W2 [P2 §6; P1 §3 "The Markov fix-up"],
+ * prev_0 = anchor, prev_j = x_{j-1}.
+ * workspace: device, >= dspark_workspace_bytes(problem), 256-byte aligned; its
+ * contents need no initialisation and are scratch after the call.
+ */
+dspark_status dspark_verify_tokenwise(const dspark_verify_problem* problem,
+                                      const dspark_verify_outputs* out,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Block verification (Sun et al.) [P1 §4 "Block verification", Figure 3]:
+ * P_0 = 1, P_i = min(1, P_{i-1} r_{i-1}); R_i = sum_v max(0, P_i p_i(v) - q_i(v));
+ * h_i = R_i / (R_i + 1 - P_i) (1 when P_i = 1), h_gamma = P_gamma; the kept length
+ * is tau = the last i with u_{b,i-1} <= h_i (0 if none); the emitted token is drawn
+ * from max(0, P_tau p_tau - q_tau) normalised, or from p_gamma when tau = gamma.
+ * Same arguments and workspace rules as dspark_verify_tokenwise.
+ */
+dspark_status dspark_verify_block(const dspark_verify_problem* problem,
+                                  const dspark_verify_outputs* out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * DSpark Markov-head bias alone [P2 §6 "Why the Markov Head Helps"]:
+ * out[i, v] = logits_in[i, v] + sum_r W1[prev_tokens[i], r] * W2t[v, r]  (fp32).
+ * W1, W2t: device bf16 [V, R], R in {32, 64, 128, 256}.  prev_tokens: device
+ * [rows]; an id outside [0, V) gives a zero bias row.  logits_in: device
+ * [rows, V] of `dtype`, or NULL for zero.  out: device fp32 [rows, V].
+ */
+dspark_status dspark_markov_bias(const uint16_t* W1, const uint16_t* W2t, int32_t V, int32_t R,
+                                 const int32_t* prev_tokens, int32_t rows,
+                                 const void* logits_in, int32_t dtype, float* out, void* stream);
+
+/*
+ * Confidence head and adaptive verification count [P2 §7-9; P3 "The controller,
+ * and the table it reads from"; P1 §6 "The arithmetic you need before tuning k"]:
+ *   c_{b,j} = sigmoid(w . hidden[b, j, :] + bias)          (hidden -> Linear -> sigmoid)
+ *   a_{b,j} = prod_{i<=j} c_{b,i}                           (prefix survival)
+ *   n_b     = argmax_{n in 0..k} (1 + sum_{j<n} a_{b,j}) / verify_ms[n + 1]
+ * with the smallest n on ties; verify_ms is indexed by the token count of one
+ * stream's verify (n drafts + the target's own position).
+ * hidden: device bf16 [B, k, H]; w: device bf16 [H]; verify_ms: HOST float
+ * [n_ms], k + 2 <= n_ms <= 256, copied into the launch; n_out: device int32 [B];
+ * c_out, a_out: device fp32 [B, k] or NULL.  n_out can be passed as num_drafts
+ * of dspark_verify_block for ragged verification without a host round trip.
+ */
+dspark_status dspark_adaptive_k(const uint16_t* hidden, const uint16_t* w, float bias,
+                                int32_t B, int32_t k, int32_t H,
+                                const float* verify_ms, int32_t n_ms,
+                                int32_t* n_out, float* c_out, float* a_out, void* stream);
+
+/* Static description of a status code. */
+const char* dspark_status_string(dspark_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_VERIFY_H */
