@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Throughput of the DSpark verify sampler on one MI355X.
+
+Workload: B=64 streams, k=5 drafts, V=129280, bf16 logits, Markov bias rank 256
+(the headline shape).  One step verifies the batch the way a serving step
+would use this library: the confidence head + adaptive count over the batch's
+hidden states, then token-wise verification and block verification of the same
+draft blocks (so a step verifies 2*B blocks).  Inputs are resident in HBM before
+the timed region; several copies of the whole input set rotate so that no call
+finds its inputs in the 256 MB Infinity Cache.
+
+Prints one JSON line.  ``value`` = verified draft blocks per second.
+``roofline`` is for the dominant launch (row statistics, pass 1), timed with
+HIP events recorded around it by the library's stage hook on the same stream.
+``cpu_baseline`` is the fp64 oracle on the host, on the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "verified draft blocks/s (B x k x V) and achieved HBM GB/s at B=64,k=5,V=129280"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on the call's stream)."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.h.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def ms(self, a, b) -> float:
+        if self.h.hipEventSynchronize(b) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        f = ctypes.c_float()
+        if self.h.hipEventElapsedTime(ctypes.byref(f), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(f.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.h.hipEventDestroy(e)
+
+
+def alg_bytes(B, k, V, R, e, s, gamma) -> float:
+    """Algorithmic bytes of one verify call: every draft-slot row pair once, the bonus row
+    only where it is sampled, W2 once and the gathered W1 rows, plus the small I/O."""
+    rows = float(np.sum(2 * gamma + (s == gamma)))
+    return e * V * rows + 2.0 * R * V + 2.0 * R * float(np.sum(gamma)) + 16.0 * B * k
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=3, help="rotating copies of the input set")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (streams shard with no "
+              "collective; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads
+    import draft_block_verification_row_amd as dv
+
+    dv.lib()  # fails loudly without the built HIP library
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("generating the headline workload (B=64, k=5, V=129280, bf16, Markov rank 256)")
+    wl = workloads.make_zipf("h", 64, 64, 5, confidence=True)
+    B, k, V, R = wl.B, wl.k, wl.V, wl.R
+
+    def up(x):
+        a = np.ascontiguousarray(x)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    base = dict(target=up(wl.target), draft=up(wl.draft), tokens=up(wl.draft_tokens.astype(np.int32)),
+                temp=up(wl.temperature), anchor=up(wl.anchor.astype(np.int32)), W1=up(wl.W1), W2t=up(wl.W2t),
+                hidden=up(wl.hidden), w=up(wl.conf_w))
+    sets = [base] + [{kk: v.clone() for kk, v in base.items()} for _ in range(args.sets - 1)]
+    ws_bytes = dv.workspace_bytes(B, k, V, dv.DSPARK_BF16)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    outs = {m: (torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, k + 1, dtype=torch.int32, device=dev),
+                None) for m in ("tokenwise", "block")}
+    verify = {"tokenwise": dv.verify_tokenwise, "block": dv.verify_block}
+    ms_table = wl.verify_ms
+
+    def call(method, s, step, ev=None):
+        return verify[method](s["target"], s["draft"], s["tokens"], temperature=s["temp"], W1=s["W1"],
+                              W2t=s["W2t"], anchor=s["anchor"], seed=wl.seed, step=step, workspace=ws,
+                              out=outs[method], stage_events=ev)
+
+    def one_step(i, evs=None):
+        s = sets[i % len(sets)]
+        dv.adaptive_k(s["hidden"], s["w"], wl.conf_b, ms_table, want_c=False)
+        call("tokenwise", s, i, None if evs is None else evs[0])
+        call("block", s, i, None if evs is None else evs[1])
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        one_step(args.warmup + i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+
+    # per-launch times: a separate pass with the library's stage events
+    hip = HipEvents()
+    nprof = min(args.steps, 50)
+    stage_ms = {m: np.zeros(dv.STAGES) for m in ("tokenwise", "block")}
+    realized = {}
+    all_ev = []
+    for i in range(nprof):
+        evs = (hip.create(dv.STAGES + 1), hip.create(dv.STAGES + 1))
+        all_ev.append(evs)
+        one_step(i, evs)
+    torch.cuda.synchronize()
+    for evs in all_ev:
+        for m, e in zip(("tokenwise", "block"), evs):
+            stage_ms[m] += np.array([hip.ms(e[j], e[j + 1]) for j in range(dv.STAGES)])
+        hip.destroy(evs[0] + evs[1])
+    for m in stage_ms:
+        stage_ms[m] /= nprof
+    for m in ("tokenwise", "block"):
+        call(m, sets[0], 0)
+        torch.cuda.synchronize()
+        realized[m] = outs[m][0].cpu().numpy()
+
+    gamma = np.full(B, k)
+    e = 2
+    bytes_call = {m: alg_bytes(B, k, V, R, e, realized[m], gamma) for m in realized}
+    # pass 1 reads: every target row 0..k (bonus rows included), every draft row, W2, gathered W1 rows
+    full_pass1 = e * V * B * (2 * k + 1) + 2.0 * R * V + 2.0 * R * B * k
+    t_pass1 = 0.5 * (stage_ms["tokenwise"][0] + stage_ms["block"][0])
+    alg_pass1 = 0.5 * (bytes_call["tokenwise"] + bytes_call["block"]) - 16.0 * B * k
+    achieved = alg_pass1 / (t_pass1 * 1e-3) / 1e9
+    blocks_per_s = 2 * B / (ms_step * 1e-3)
+    step_bytes = bytes_call["tokenwise"] + bytes_call["block"] + 2.0 * B * k * 4096
+    result = {
+        "metric": METRIC,
+        "value": round(blocks_per_s, 1),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "headline: B=64 k=5 V=129280, bf16 logits (Zipf-biased Gaussian target, correlated "
+                        "draft), Markov bias rank 256, T_b in [0.6, 1.0], seed 64",
+            "step": "confidence head + adaptive n, token-wise verify, block verify (2*B blocks per step)",
+            "B": B, "k": k, "V": V, "R": R, "input_sets_rotated": args.sets,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "pass1_kernel (row statistics + fused Markov MFMA)",
+            "kernel_ms": round(t_pass1, 5),
+            "alg_bytes_per_launch": int(alg_pass1),
+            "bytes_read_by_design_per_launch": int(full_pass1),
+            "frac_on_bytes_read": round(full_pass1 / (t_pass1 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        },
+        "stage_ms": {m: [round(x, 5) for x in stage_ms[m]] for m in stage_ms},
+        "stages": ["pass1 row statistics", "scan", "pass2 residual masses", "finalize/sampler"],
+        "blocks_per_s_by_verifier": {m: round(B / (float(np.sum(stage_ms[m])) * 1e-3), 1) for m in stage_ms},
+        "logits_per_s": round(2 * B * k * V / (ms_step * 1e-3), 1),
+        "step_alg_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "accepted_mean": {m: round(float(np.mean(realized[m])), 4) for m in realized},
+    }
+
+    if not args.no_cpu_baseline:
+        from oracle import dspark as odsp   # cpu_baseline leg only
+        try:
+            from threadpoolctl import threadpool_info
+            blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        except Exception:
+            blas_threads = 1
+        log("timing the fp64 oracle on the host (the same batch, both verifiers + adaptive head)")
+        c0 = time.perf_counter()
+        odsp.adaptive_k(wl.hidden, wl.conf_w, wl.conf_b, wl.verify_ms)
+        for m in ("tokenwise", "block"):
+            odsp.verify(wl.target, wl.draft, wl.dtype, wl.draft_tokens, wl.temperature, wl.anchor, wl.W1, wl.W2t,
+                        seed=wl.seed, step=0, method=m)
+        cpu_s = time.perf_counter() - c0
+        result["cpu_baseline"] = {
+            "value": round(2 * B / cpu_s, 3),
+            "unit": "blocks/s",
+            "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"one full step of the same batch (adaptive head + token-wise + block verify of {B} "
+                      f"streams) in fp64 numpy, {cpu_s:.1f} s; elementwise work single-threaded, "
+                      f"BLAS products on {blas_threads} threads",
+        }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

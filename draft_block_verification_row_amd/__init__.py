@@ -23,6 +23,7 @@ DSPARK_F32 = 0
 DSPARK_BF16 = 1
 RACE_GROUP = 256
 MAX_K = 32
+STAGES = 4   # launches per verify call
 
 
 class VerifyProblem(ctypes.Structure):
@@ -37,7 +38,8 @@ class VerifyProblem(ctypes.Structure):
 
 
 class VerifyOutputs(ctypes.Structure):
-    _fields_ = [("accepted_len", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p), ("diag", ctypes.c_void_p)]
+    _fields_ = [("accepted_len", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p), ("diag", ctypes.c_void_p),
+                ("stage_events", ctypes.c_void_p)]
 
 
 _lib = None
@@ -147,7 +149,7 @@ def workspace_bytes(B: int, k: int, V: int, dtype: int = DSPARK_BF16) -> int:
 
 
 def _verify(fname, target, draft, draft_tokens, num_drafts=None, temperature=None, W1=None, W2t=None,
-            anchor=None, seed=0, step=0, diag=False, workspace=None, out=None):
+            anchor=None, seed=0, step=0, diag=False, workspace=None, out=None, stage_events=None):
     p, (B, k, V) = _problem(target, draft, draft_tokens, num_drafts, temperature, W1, W2t, anchor, seed, step)
     dev = target.device
     need = lib().dspark_workspace_bytes(ctypes.byref(p))
@@ -159,7 +161,11 @@ def _verify(fname, target, draft, draft_tokens, num_drafts=None, temperature=Non
         dg = torch.empty(B, k + 1, 5, dtype=torch.float64, device=dev) if diag else None
     else:
         acc, toks, dg = out
-    o = VerifyOutputs(accepted_len=_ptr(acc), out_tokens=_ptr(toks), diag=_ptr(dg))
+    ev = None
+    if stage_events is not None:   # DSPARK_STAGES + 1 raw hipEvent_t handles
+        ev = (ctypes.c_void_p * len(stage_events))(*stage_events)
+    o = VerifyOutputs(accepted_len=_ptr(acc), out_tokens=_ptr(toks), diag=_ptr(dg),
+                      stage_events=ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None)
     _check(getattr(lib(), fname)(ctypes.byref(p), ctypes.byref(o), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(dev)))
     return acc, toks, dg

@@ -113,7 +113,8 @@ dspark_status verify_common(const dspark_verify_problem* p, const dspark_verify_
   a.ws.rowmask = reinterpret_cast<uint32_t*>(base + L.off[11]);
   a.ws.items = reinterpret_cast<int32_t*>(base + L.off[12]);
   a.ws.nitems = reinterpret_cast<int32_t*>(base + L.off[13]);
-  if (launch_verify(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return DSPARK_ERR_HIP;
+  if (launch_verify(a, reinterpret_cast<hipStream_t>(stream), o->stage_events) != hipSuccess)
+    return DSPARK_ERR_HIP;
   return DSPARK_OK;
 }
 

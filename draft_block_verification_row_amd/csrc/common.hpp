@@ -189,7 +189,7 @@ struct AdaptArgs {
 };
 
 // launchers (kernels.hip)
-hipError_t launch_verify(const Args& a, hipStream_t st);
+hipError_t launch_verify(const Args& a, hipStream_t st, void* const* events);
 hipError_t launch_markov_bias(const BiasArgs& ba, int NG, hipStream_t st);
 hipError_t launch_adaptive(const AdaptArgs& aa, hipStream_t st);
 

@@ -632,27 +632,35 @@ __global__ __launch_bounds__(kThreads) void adaptive_kernel(AdaptArgs aa) {
 // launch wrappers (host side of this translation unit)
 // ---------------------------------------------------------------------------
 template <int DT, int KS, bool MARKOV>
-static hipError_t launch_passes(const Args& a, hipStream_t st) {
+static hipError_t launch_passes(const Args& a, hipStream_t st, void* const* ev) {
+  auto mark = [&](int i) {
+    if (ev != nullptr && ev[i] != nullptr) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[i]), st);
+  };
+  mark(0);
   hipLaunchKernelGGL((pass1_kernel<DT, KS, MARKOV>), dim3(a.NG), dim3(kThreads), 0, st, a);
+  mark(1);
   hipLaunchKernelGGL((scan_kernel<DT>), dim3(a.B), dim3(kThreads), 0, st, a);
+  mark(2);
   hipLaunchKernelGGL((pass2_kernel<DT, KS, MARKOV>), dim3(a.NG), dim3(kThreads), 0, st, a);
+  mark(3);
   hipLaunchKernelGGL((finalize_kernel<DT>), dim3(a.B), dim3(kThreads), 0, st, a);
+  mark(4);
   return hipGetLastError();
 }
 
 template <int DT>
-static hipError_t launch_dt(const Args& a, hipStream_t st) {
-  if (a.W1 == nullptr) return launch_passes<DT, 1, false>(a, st);
+static hipError_t launch_dt(const Args& a, hipStream_t st, void* const* ev) {
+  if (a.W1 == nullptr) return launch_passes<DT, 1, false>(a, st, ev);
   switch (a.R) {
-    case 32: return launch_passes<DT, 1, true>(a, st);
-    case 64: return launch_passes<DT, 2, true>(a, st);
-    case 128: return launch_passes<DT, 4, true>(a, st);
-    default: return launch_passes<DT, 8, true>(a, st);
+    case 32: return launch_passes<DT, 1, true>(a, st, ev);
+    case 64: return launch_passes<DT, 2, true>(a, st, ev);
+    case 128: return launch_passes<DT, 4, true>(a, st, ev);
+    default: return launch_passes<DT, 8, true>(a, st, ev);
   }
 }
 
-hipError_t launch_verify(const Args& a, hipStream_t st) {
-  return a.dtype == kBF16 ? launch_dt<kBF16>(a, st) : launch_dt<kF32>(a, st);
+hipError_t launch_verify(const Args& a, hipStream_t st, void* const* ev) {
+  return a.dtype == kBF16 ? launch_dt<kBF16>(a, st, ev) : launch_dt<kF32>(a, st, ev);
 }
 
 template <int DT>

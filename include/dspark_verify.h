@@ -91,7 +91,14 @@ typedef struct {
   int32_t* out_tokens;            /* device [B, k+1]: x_0..x_{s-1}, Y, then -1               */
   double* diag;                   /* device [B, k+1, 5] or NULL: per slot j, (log p_j(x_j),
                                      log q_j(x_j), P_j, R_j, h_j); NaN where not computed    */
+  void* const* stage_events;      /* NULL, or DSPARK_STAGES + 1 hipEvent_t the call records on
+                                     `stream` before its first launch and after each launch
+                                     (row statistics, scan, residual masses, sampler): a
+                                     timing hook, nothing is allocated                      */
 } dspark_verify_outputs;
+
+/* Launches per verify call (see stage_events). */
+#define DSPARK_STAGES 4
 
 /* Bytes of workspace the two verify entry points need for this problem (host, pure).
  * Returns 0 if the problem's sizes are invalid. */

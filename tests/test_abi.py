@@ -60,6 +60,7 @@ int main(void) {
   P(dspark_verify_problem, W1) P(dspark_verify_problem, W2t) P(dspark_verify_problem, anchor_tokens)
   P(dspark_verify_problem, R) P(dspark_verify_problem, step) P(dspark_verify_problem, seed)
   P(dspark_verify_outputs, accepted_len) P(dspark_verify_outputs, out_tokens) P(dspark_verify_outputs, diag)
+  P(dspark_verify_outputs, stage_events)
   return 0;
 }
 '''
