@@ -23,7 +23,7 @@ DSPARK_F32 = 0
 DSPARK_BF16 = 1
 RACE_GROUP = 256
 MAX_K = 32
-STAGES = 4   # launches per verify call
+STAGES = 5   # launches per verify call
 
 
 class VerifyProblem(ctypes.Structure):

@@ -21,17 +21,18 @@ bool rank_ok(int R) { return R == 32 || R == 64 || R == 128 || R == 256; }
 
 // Offsets of every workspace region, in the order of dspark::Workspace.
 struct Layout {
-  size_t off[14];
+  size_t off[15];
   size_t total;
 };
 
 Layout layout(int B, int k, int V) {
   const size_t NG = (size_t)(V + kGroup - 1) / kGroup;
   const size_t BT = (size_t)B * (k + 1), BD = (size_t)B * k;
-  const size_t sizes[14] = {
-      BT * NG * sizeof(float2),  // tpart
-      BD * NG * sizeof(float2),  // dpart
-      BD * NG * sizeof(float),   // wgrp
+  const size_t tiles = (BD + kChunk - 1) / kChunk;
+  const size_t sizes[15] = {
+      BT * NG * sizeof(float2),           // tpart
+      BD * NG * sizeof(float2),           // dpart
+      BD * NG * sizeof(float),            // wgrp
       BT * sizeof(float),        // tm
       BT * sizeof(double),       // tl2s
       BD * sizeof(float),        // dm
@@ -41,12 +42,13 @@ Layout layout(int B, int k, int V) {
       BD * sizeof(double),       // lqx
       (size_t)B * 4 * sizeof(int32_t),  // info
       (size_t)B * sizeof(uint32_t),     // rowmask
-      BD * sizeof(int32_t),             // items
+      BD * sizeof(Item),                // items
       sizeof(int32_t),                  // nitems
+      tiles * 8 * 64 * sizeof(uint4),   // btile (sized for the largest rank, R = 256)
   };
   Layout L;
   size_t o = 0;
-  for (int i = 0; i < 14; ++i) {
+  for (int i = 0; i < 15; ++i) {
     L.off[i] = o;
     o += align_up(sizes[i] > 0 ? sizes[i] : 1);
   }
@@ -72,6 +74,7 @@ dspark_status verify_common(const dspark_verify_problem* p, const dspark_verify_
     if (!rank_ok(p->R)) return DSPARK_ERR_UNSUPPORTED;
     if (!aligned16(p->W1) || !aligned16(p->W2t)) return DSPARK_ERR_UNSUPPORTED;
   }
+  if (verify_lds_bytes(p->B) > kMaxPassLds) return DSPARK_ERR_UNSUPPORTED;
   const Layout L = layout(p->B, p->k, p->V);
   if (ws == nullptr || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
     return DSPARK_ERR_WORKSPACE;
@@ -111,8 +114,9 @@ dspark_status verify_common(const dspark_verify_problem* p, const dspark_verify_
   a.ws.lqx = reinterpret_cast<double*>(base + L.off[9]);
   a.ws.info = reinterpret_cast<int32_t*>(base + L.off[10]);
   a.ws.rowmask = reinterpret_cast<uint32_t*>(base + L.off[11]);
-  a.ws.items = reinterpret_cast<int32_t*>(base + L.off[12]);
+  a.ws.items = reinterpret_cast<Item*>(base + L.off[12]);
   a.ws.nitems = reinterpret_cast<int32_t*>(base + L.off[13]);
+  a.ws.btile = reinterpret_cast<uint4*>(base + L.off[14]);
   if (launch_verify(a, reinterpret_cast<hipStream_t>(stream), o->stage_events) != hipSuccess)
     return DSPARK_ERR_HIP;
   return DSPARK_OK;
@@ -167,6 +171,7 @@ dspark_status dspark_adaptive_k(const uint16_t* hidden, const uint16_t* w, float
   memset(&aa, 0, sizeof(aa));
   aa.hidden = hidden; aa.w = w; aa.bias = bias; aa.B = B; aa.k = k; aa.H = H; aa.n_ms = n_ms;
   aa.n_out = n_out; aa.c_out = c_out; aa.a_out = a_out;
+  aa.vec_ok = (H % 8) == 0 && aligned16(hidden) && aligned16(w);
   for (int i = 0; i < n_ms; ++i) {
     if (!(verify_ms[i] > 0.0f)) return DSPARK_ERR_INVALID_ARG;
     aa.ms[i] = verify_ms[i];

@@ -110,13 +110,22 @@ __device__ __forceinline__ float sum4lanes(float v) {
   return v;
 }
 
+// One row of the residual pass, prepared by the scan: the target/draft rows, the
+// Markov previous token, the row maxima, the temperature constant (hi + lo) and the
+// exponent constants of P p and q in log2 units (hi + lo).
+struct Item {
+  int32_t dr, tr, prev, pad;
+  float Mt, Md, chi, clo;
+  float kph, kpl, kqh, kql;
+};
+
 // ---------------------------------------------------------------------------
 // Workspace (carved on the host, 256-byte aligned regions).
 // ---------------------------------------------------------------------------
 struct Workspace {
-  float2* tpart;      // [B*(k+1)][NG] target row group partials (raw max, sum 2^((l-m)c))
-  float2* dpart;      // [B*k][NG]     draft row group partials on biased logits
-  float* wgrp;        // [B*k][NG]     residual group masses of pass-2 rows
+  float2* tpart;      // [NG][B*(k+1)]   target row group partials (raw max, sum 2^((l-m)c))
+  float2* dpart;      // [NG][B*k]       draft row group partials on biased logits
+  float* wgrp;        // [NG][B*k]       residual group masses of pass-2 rows
   float* tm;          // [B*(k+1)]     target row max (raw logits)
   double* tl2s;       // [B*(k+1)]     log2 of sum 2^((l-m)c)
   float* dm;          // [B*k]         draft row max (biased logits)
@@ -126,8 +135,9 @@ struct Workspace {
   double* lqx;        // [B*k]         log q_j(x_j)
   int32_t* info;      // [B*4]         gamma, stop (token-wise t / block provisional), f, flags
   uint32_t* rowmask;  // [B]           pass-2 rows of each stream (bit i = slot i)
-  int32_t* items;     // [B*k]         compact pass-2 list of b*k + i
+  Item* items;        // [B*k]         compact pass-2 list
   int32_t* nitems;    // [1]
+  uint4* btile;       // [ceil(B*k/16)][R/32][64] W1 tiles in MFMA lane order (pass 1, then pass 2)
 };
 
 struct Args {
@@ -181,12 +191,17 @@ struct AdaptArgs {
   const uint16_t* hidden;
   const uint16_t* w;
   float bias;
-  int B, k, H, n_ms;
+  int B, k, H, n_ms, vec_ok;
   int32_t* n_out;
   float* c_out;
   float* a_out;
   float ms[kMaxMs];
 };
+
+// Dynamic LDS of pass 1 (the per-stream table, 12 bytes a stream); calls needing
+// more than kMaxPassLds (B > 4096) are rejected as unsupported.
+size_t verify_lds_bytes(int B);
+constexpr size_t kMaxPassLds = 48 * 1024;
 
 // launchers (kernels.hip)
 hipError_t launch_verify(const Args& a, hipStream_t st, void* const* events);

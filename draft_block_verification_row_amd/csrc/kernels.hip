@@ -3,23 +3,32 @@
 // Sources (page titles): [P1] "MTP, DSpark and Block Verification, Explained";
 // [P2] "MTP Heads and Confidence Heads"; [P3] "Teaching the Speculator What a Draft Costs".
 //
-// A call is four launches on one stream:
-//   pass1     one workgroup per 256-id vocabulary group g; every target row
-//             (slots 0..gamma_b) and every draft row (slots 0..gamma_b-1) gets a
-//             partial (max, sum 2^((l - max) log2e / T)) over the group.  Draft rows
-//             get the Markov bias W1[prev] . W2 from MFMA tiles held in registers:
-//             the wave keeps its 64 columns of W2 as the A operand for the whole
-//             launch and streams draft rows through the B operand [P2 §6; P1 §3].
+// A call is five launches on one stream:
+//   pack      the B operand of the Markov product [P2 §6; P1 §3 "The Markov fix-up"]:
+//             W1[prev] of every draft row, 16 rows per tile, stored in MFMA lane
+//             order so that a wave reads one k-step of a tile as one contiguous
+//             1 KB load (gathering W1 rows per wave is the slow part otherwise).
+//   pass1     one workgroup per 256-id vocabulary group g.  Target rows (slots
+//             0..gamma_b): a 16-lane row reduces the group's 256 ids to a partial
+//             (max, sum 2^((l - max) log2e / T)).  Draft rows (slots 0..gamma_b-1):
+//             each wave keeps its 64 columns of W2 as MFMA A operands, streams the
+//             packed W1 tiles through the B operand and adds the bias; the wave
+//             partials meet in LDS once every 16 chunks (the only barriers).
 //   scan      one workgroup per stream: row normalisers from the partials (fp64),
 //             log p_j(x_j), log q_j(x_j) (gathered bias in fp64), the token-wise stop
 //             and the clipped prefix P_i [P1 §4], and the rows whose residual mass
 //             is needed.  Block verification needs R_i only where u_{i-1} <= P_i
-//             (h_i <= P_i always), plus the row the sampler may land on.
-//   pass2     like pass1 over the listed rows only: per group, the residual mass
-//             sum max(0, P_i p_i - q_i) (Markov bias recomputed on MFMA).
+//             (h_i <= P_i always), plus the row the sampler may land on.  The scan
+//             also packs the W1 tiles of those rows.
+//   pass2     like the draft half of pass1 over the listed rows only: per group,
+//             the residual mass sum max(0, P_i p_i - q_i) (Markov bias recomputed).
 //   finalize  one workgroup per stream: R_i, h_i, tau (top-down), then the
 //             two-level exponential race over group masses and within the winning
 //             group (weights recomputed in fp64), and the outputs.
+//
+// Partials are group-major ([group or segment][row]): a stream's rows are adjacent,
+// so the per-stream scan and finalize read short contiguous runs.  Full windows take
+// unconditional 16-byte loads (VEC); only the last, ragged window masks columns.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -30,8 +39,6 @@ namespace dspark {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kSuper = 256;   // rows per LDS flush (one per thread)
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
@@ -52,18 +59,27 @@ __device__ __forceinline__ void temp_split(float T, float& chi, float& clo) {
 // A row m = n of subtile s, i.e. vocabulary id cb + 16(n>>2) + 4s + (n&3), k-range
 // 8q + 32kk.  With that permutation the 16x16 output puts columns cb + 16q + [0,16)
 // of draft row n into lane (n, q), in order (acc[s][i] -> column cb + 16q + 4s + i).
-template <int KS>
+// VEC: each 16-column window starts at min(start, V - 16) (the kernels mask the
+// columns a clamped window repeats); otherwise columns past V are clamped to V - 1
+// and masked after the product.
+template <int KS, bool VEC = false>
 __device__ __forceinline__ void load_w2_slab(const Args& a, int cb, int n, int q, bf16x8 (&A)[4][KS]) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    int vr = cb + 16 * (n >> 2) + 4 * s + (n & 3);
-    vr = vr < a.V ? vr : a.V - 1;   // columns past V are masked after the product
+    int vr;
+    if (VEC) {
+      vr = min(cb + 16 * (n >> 2), a.V - 16) + 4 * s + (n & 3);
+    } else {
+      vr = cb + 16 * (n >> 2) + 4 * s + (n & 3);
+      vr = vr < a.V ? vr : a.V - 1;
+    }
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) A[s][kk] = load_bf16x8(a.W2t + (size_t)vr * a.R + kk * 32 + 8 * q);
   }
 }
 
-// Bias of draft row n (previous token `prev`, -1 = none) at this lane's 16 columns.
+// Bias of draft row n (previous token `prev`, -1 = none) at this lane's 16 columns,
+// B operand straight from global memory.
 template <int KS>
 __device__ __forceinline__ void markov_tile(const Args& a, const bf16x8 (&A)[4][KS], int prev, int q, float (&bias)[16]) {
   bf16x8 Bop[KS];
@@ -83,13 +99,104 @@ __device__ __forceinline__ void markov_tile(const Args& a, const bf16x8 (&A)[4][
     for (int i = 0; i < 4; ++i) bias[4 * s + i] = acc[s][i];
 }
 
-// Partial (max, sum 2^((x - max) c)) of 16 values of one row, reduced over the 4
-// lanes holding the wave's 64 columns of that row.
+// ---------------------------------------------------------------------------
+// Cross-lane reductions.  DPP within a 16-lane row: quad_perm [1,0,3,2],
+// quad_perm [2,3,0,1], row_half_mirror, row_mirror; every lane ends with the
+// row's result, and every lane computes it in the same order.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dppf<0xB1>(v));
+  v = fmaxf(v, dppf<0x4E>(v));
+  v = fmaxf(v, dppf<0x141>(v));
+  v = fmaxf(v, dppf<0x140>(v));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dppf<0xB1>(v);
+  v += dppf<0x4E>(v);
+  v += dppf<0x141>(v);
+  v += dppf<0x140>(v);
+  return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// 16 logits kept packed until use: bf16 as 8 words, fp32 as 16 floats.
+template <int DT> struct Raw16;
+template <> struct Raw16<kBF16> { uint32_t w[8]; };
+template <> struct Raw16<kF32> { float f[16]; };
+
+// VEC: columns [c0, c0+16) are inside the row and 16-byte aligned (the caller clamps
+// the window): plain vector loads.  Otherwise each element is checked against V and
+// -inf fills the rest.
+template <int DT, bool VEC>
+__device__ __forceinline__ void raw_load(Raw16<DT>& r, const char* __restrict__ row, int c0, int V) {
+  if (DT == kBF16) {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(row);
+    auto& w = reinterpret_cast<Raw16<kBF16>&>(r).w;
+    if (VEC) {
+      const uint4 a = *reinterpret_cast<const uint4*>(p + c0);
+      const uint4 b = *reinterpret_cast<const uint4*>(p + c0 + 8);
+      w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t lo = (c0 + 2 * i < V) ? p[c0 + 2 * i] : 0xFF80u;      // bf16 -inf
+        const uint32_t hi = (c0 + 2 * i + 1 < V) ? p[c0 + 2 * i + 1] : 0xFF80u;
+        w[i] = lo | (hi << 16);
+      }
+    }
+  } else {
+    const float* p = reinterpret_cast<const float*>(row);
+    auto& f = reinterpret_cast<Raw16<kF32>&>(r).f;
+    if (VEC) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 a = *reinterpret_cast<const float4*>(p + c0 + 4 * i);
+        f[4 * i] = a.x; f[4 * i + 1] = a.y; f[4 * i + 2] = a.z; f[4 * i + 3] = a.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) f[i] = (c0 + i < V) ? p[c0 + i] : -INFINITY;
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void raw_to_f32(const Raw16<DT>& r, float (&x)[16]) {
+  if (DT == kBF16) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t w = reinterpret_cast<const Raw16<kBF16>&>(r).w[i];
+      x[2 * i] = bf16lo(w);
+      x[2 * i + 1] = bf16hi(w);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = reinterpret_cast<const Raw16<kF32>&>(r).f[i];
+  }
+}
+
+// Columns a clamped window repeats (the first `shift` of 16) do not count.
+__device__ __forceinline__ void mask_shift(float (&x)[16], int shift) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = i < shift ? -INFINITY : x[i];
+}
+
+// Partial (max, sum 2^((x - max) c)) of 16 values; RED selects the lanes that share
+// the row: 0 = the 4 lanes {n, n+16, n+32, n+48} (MFMA layout), 1 = a 16-lane DPP row.
+template <int RED>
 __device__ __forceinline__ float2 row_partial(const float (&x)[16], float chi, float clo) {
   float m = x[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) m = fmaxf(m, x[i]);
-  m = max4lanes(m);
+  m = RED == 0 ? max4lanes(m) : row16_max(m);
   float s = 0.f;
   if (m != -INFINITY) {
 #pragma unroll
@@ -98,11 +205,95 @@ __device__ __forceinline__ float2 row_partial(const float (&x)[16], float chi, f
       s += __builtin_amdgcn_exp2f(fmaf(t, chi, t * clo));
     }
   }
-  s = sum4lanes(s);
+  s = RED == 0 ? sum4lanes(s) : row16_sum(s);
   return make_float2(m, s);
 }
 
-// Combine the 4 wave partials of one row into the group partial.
+// ---------------------------------------------------------------------------
+// pack: W1 tiles in MFMA lane order.  Tile c, k-step kk, lane l holds
+// W1[prev(16c + l%16)][32kk + 8(l/16) .. +8] (zero for a row without bias or an
+// inactive row).  One wave per tile; the first also clears the pass-2 row count.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void pack_kernel(Args a) {
+  const int c = blockIdx.x, l = threadIdx.x, n = l & 15, q = l >> 4;
+  if (c == 0 && l == 0) *a.ws.nitems = 0;
+  if (a.W1 == nullptr) return;
+  const int dr = c * kChunk + n;
+  int prev = -1;
+  if (dr < a.B * a.k) {
+    const int b = dr / a.k, j = dr - b * a.k;
+    if (j < stream_gamma(a, b)) prev = draft_prev(a, b, j);
+  }
+  const int ks = a.R / 32;   // <= 8
+  uint4 v[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+    v[kk] = (kk < ks && prev >= 0) ? *reinterpret_cast<const uint4*>(a.W1 + (size_t)prev * a.R + kk * 32 + 8 * q)
+                                   : make_uint4(0, 0, 0, 0);
+  uint4* dst = a.ws.btile + (size_t)c * ks * 64 + l;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+    if (kk < ks) dst[kk * 64] = v[kk];
+}
+
+// One k-step slice of a packed tile per lane: the B operand of 16 rows.
+template <int KS>
+__device__ __forceinline__ void load_btile(const Args& a, int c, int l, bf16x8 (&B)[KS]) {
+  const uint4* t = a.ws.btile + (size_t)c * KS * 64 + l;
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) B[kk] = __builtin_bit_cast(bf16x8, t[kk * 64]);
+}
+
+// Bias of the lane's row at its 16 columns: A = this wave's W2 slab, B = a packed tile.
+template <int KS>
+__device__ __forceinline__ void markov_mma(const bf16x8 (&A)[4][KS], const bf16x8 (&B)[KS], float (&bias)[16]) {
+  f32x4 acc[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[s][kk], B[kk], acc[s], 0, 0, 0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bias[4 * s + i] = acc[s][i];
+}
+
+// Per-stream constants of a pass in LDS: (chi, clo) of 1/T and gamma_b.
+__host__ __device__ __forceinline__ size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+__host__ __device__ __forceinline__ size_t stream_table_bytes(int B) {
+  return align16((size_t)B * sizeof(float2)) + align16((size_t)B * sizeof(int));
+}
+
+struct StreamTable {
+  const float2* tc;
+  const int* gam;
+};
+
+__device__ __forceinline__ StreamTable build_stream_table(const Args& a, char* smem) {
+  float2* tc = reinterpret_cast<float2*>(smem);
+  int* gam = reinterpret_cast<int*>(smem + align16((size_t)a.B * sizeof(float2)));
+  for (int b = threadIdx.x; b < a.B; b += kThreads) {
+    float chi, clo;
+    temp_split(stream_temp(a, b), chi, clo);
+    tc[b] = make_float2(chi, clo);
+    gam[b] = stream_gamma(a, b);
+  }
+  __syncthreads();
+  return StreamTable{tc, gam};
+}
+
+// ---------------------------------------------------------------------------
+// pass1: row statistics.  Workgroup g owns vocabulary ids [256g, 256g + 256).
+// ---------------------------------------------------------------------------
+// Draft rows, 16 per chunk: the logits of the next PD chunks and the next W1 tile
+// are in flight while the current chunk goes through the MFMA and the reduction.
+// The 4 wave partials of a row (64 ids each) meet in LDS; every 16 chunks one
+// barrier pair turns them into group partials.
+constexpr int kFlush = 16;   // chunks per LDS flush (256 rows, one per thread)
+
 __device__ __forceinline__ float2 combine_waves(const float2 (&p)[kWaves], float chi, float clo) {
   float M = p[0].x;
 #pragma unroll
@@ -119,202 +310,286 @@ __device__ __forceinline__ float2 combine_waves(const float2 (&p)[kWaves], float
   return make_float2(M, S);
 }
 
-// ---------------------------------------------------------------------------
-// pass1: row statistics, per 256-id group.
-// ---------------------------------------------------------------------------
-template <int DT, int KS, bool MARKOV>
-__global__ __launch_bounds__(kThreads) void pass1_kernel(Args a) {
-  __shared__ float2 part[kSuper][kWaves];
-  const int g = blockIdx.x;
+template <int DT, int KS, bool MARKOV, bool VEC>
+__device__ __forceinline__ void pass1_draft(const Args& a, const StreamTable& st, int g,
+                                            float2 (*part)[kWaves]) {
+  constexpr int PD = 2;   // logits prefetch distance (chunks)
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, q = l >> 4;
   const int cb = g * kGroup + w * kWaveCols;
-  const int c0 = cb + 16 * q;
-  const bool vec = a.vec_ok != 0;
-  if (g == 0 && tid == 0) *a.ws.nitems = 0;   // pass-2 list is rebuilt by scan
-
-  // draft rows (b, j), j < gamma_b
+  const int cw = cb + 16 * q;                                // this lane's 16-column window
+  const int c0 = VEC ? min(cw, a.V - 16) : cw;               // where it is loaded from
+  const int shift = VEC ? (cw >= a.V ? 16 : cw - c0) : 0;    // columns of the window owned elsewhere
+  const bool rag = VEC && cb + kWaveCols > a.V;              // wave-uniform
   const int ND = a.B * a.k;
-  if (ND > 0) {
-    bf16x8 A[4][KS];
-    if (MARKOV) load_w2_slab<KS>(a, cb, n, q, A);
-    for (int r0 = 0; r0 < ND; r0 += kSuper) {
-      for (int ch = r0; ch < r0 + kSuper && ch < ND; ch += kChunk) {
-        const int dr = ch + n;
-        const int b = dr / a.k, j = dr - b * a.k;
-        const bool active = dr < ND && j < stream_gamma(a, b < a.B ? b : 0);
-        float x[16];
-        float bias[16];
-        if (MARKOV) markov_tile<KS>(a, A, active ? draft_prev(a, b, j) : -1, q, bias);
-        float chi = 0.f, clo = 0.f;
-        if (active) {
-          const char* row = reinterpret_cast<const char*>(a.draft) + (size_t)dr * a.V * (DT == kBF16 ? 2 : 4);
-          load16<DT>(row, c0, a.V, vec, x);
-          temp_split(stream_temp(a, b), chi, clo);
-          if (MARKOV) {
+  const int nch = (ND + kChunk - 1) / kChunk;
+  const size_t rb = (size_t)a.V * (DT == kBF16 ? 2 : 4);
+  const char* base = reinterpret_cast<const char*>(a.draft);
+  auto row_of_dr = [&](int dr, int& b) {   // false if draft row dr is past the batch or inactive
+    b = dr / a.k;
+    return dr < ND && dr - b * a.k < st.gam[b < a.B ? b : a.B - 1];
+  };
+  auto row_of = [&](int c, int& b) { return row_of_dr(c * kChunk + n, b); };
+  auto load_x = [&](int c, Raw16<DT>& x) {
+    int b;
+    if (c < nch && row_of(c, b)) raw_load<DT, VEC>(x, base + (size_t)(c * kChunk + n) * rb, c0, a.V);
+  };
+
+  bf16x8 A[4][KS];
+  bf16x8 Bc[KS];
+  if (MARKOV) {
+    load_w2_slab<KS, VEC>(a, cb, n, q, A);
+    load_btile<KS>(a, 0, l, Bc);
+  }
+  Raw16<DT> xb[PD];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] += bias[i];
-          }
-        } else {
+  for (int i = 0; i < PD; ++i) load_x(i, xb[i]);
+  for (int cbase = 0; cbase < nch; cbase += PD) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) x[i] = -INFINITY;
-        }
-        const float2 pw = row_partial(x, chi, clo);
-        if (q == 0) part[ch - r0 + n][w] = pw;
+    for (int i = 0; i < PD; ++i) {
+      const int c = cbase + i;
+      if (c >= nch) break;
+      float bias[16];
+      if (MARKOV) {
+        markov_mma<KS>(A, Bc, bias);
+        if (c + 1 < nch) load_btile<KS>(a, c + 1, l, Bc);
       }
-      __syncthreads();
-      const int dr = r0 + tid;
-      if (dr < ND) {
-        const int b = dr / a.k, j = dr - b * a.k;
-        if (j < stream_gamma(a, b)) {
-          float chi, clo;
-          temp_split(stream_temp(a, b), chi, clo);
+      float x[16];
+      raw_to_f32<DT>(xb[i], x);
+      load_x(c + PD, xb[i]);
+      int b;
+      const bool act = row_of(c, b);
+      if (MARKOV) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] += bias[e];
+      }
+      if (rag) mask_shift(x, shift);
+      const float2 tc = act ? st.tc[b] : make_float2(0.f, 0.f);
+      const float2 pw = row_partial<0>(x, tc.x, tc.y);
+      if (q == 0) part[(c % kFlush) * kChunk + n][w] = pw;
+      if (c % kFlush == kFlush - 1 || c == nch - 1) {   // uniform: every wave runs the same chunks
+        __syncthreads();
+        const int dr = (c - c % kFlush) * kChunk + tid;
+        int bb;
+        if (tid < (c % kFlush + 1) * kChunk && row_of_dr(dr, bb)) {
           float2 p[kWaves];
 #pragma unroll
           for (int ww = 0; ww < kWaves; ++ww) p[ww] = part[tid][ww];
-          a.ws.dpart[(size_t)dr * a.NG + g] = combine_waves(p, chi, clo);
+          a.ws.dpart[(size_t)g * ND + dr] = combine_waves(p, st.tc[bb].x, st.tc[bb].y);
         }
+        __syncthreads();
       }
-      __syncthreads();
     }
   }
+}
 
-  // target rows (b, j), j <= gamma_b
-  const int NT = a.B * (a.k + 1);
-  for (int r0 = 0; r0 < NT; r0 += kSuper) {
-    for (int ch = r0; ch < r0 + kSuper && ch < NT; ch += kChunk) {
-      const int tr = ch + n;
-      const int b = tr / (a.k + 1), j = tr - b * (a.k + 1);
-      const bool active = tr < NT && j <= stream_gamma(a, b < a.B ? b : 0);
+// Target rows: a 16-lane DPP row covers the group's 256 ids of one row; the
+// workgroup takes 16 rows per step, U steps per batch, and loads the next batch
+// while reducing the current one.
+template <int DT, bool VEC>
+__device__ __forceinline__ void pass1_target(const Args& a, const StreamTable& st, int g) {
+  constexpr int U = DT == kBF16 ? 4 : 2;
+  constexpr int RS = kThreads / 16;   // rows per step
+  const int tid = threadIdx.x, rq = tid >> 4, l16 = tid & 15;
+  const int cw = g * kGroup + 16 * l16;
+  const int c0 = VEC ? min(cw, a.V - 16) : cw;
+  const int shift = VEC ? (cw >= a.V ? 16 : cw - c0) : 0;
+  const bool rag = VEC && (g + 1) * kGroup > a.V;
+  const int k1 = a.k + 1;
+  const int NT = a.B * k1;
+  const size_t rb = (size_t)a.V * (DT == kBF16 ? 2 : 4);
+  const char* base = reinterpret_cast<const char*>(a.target);
+  auto row_ok = [&](int tr, int& b) {
+    b = tr / k1;
+    return tr < NT && tr - b * k1 <= st.gam[b < a.B ? b : a.B - 1];
+  };
+  auto load_batch = [&](int r0, Raw16<DT>(&raw)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int tr = r0 + RS * u + rq;
+      int b;
+      if (row_ok(tr, b)) raw_load<DT, VEC>(raw[u], base + (size_t)tr * rb, c0, a.V);
+    }
+  };
+  auto consume = [&](int r0, const Raw16<DT>(&raw)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int tr = r0 + RS * u + rq;
+      int b;
+      const bool act = row_ok(tr, b);
       float x[16];
-      float chi = 0.f, clo = 0.f;
-      if (active) {
-        const char* row = reinterpret_cast<const char*>(a.target) + (size_t)tr * a.V * (DT == kBF16 ? 2 : 4);
-        load16<DT>(row, c0, a.V, vec, x);
-        temp_split(stream_temp(a, b), chi, clo);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = -INFINITY;
-      }
-      const float2 pw = row_partial(x, chi, clo);
-      if (q == 0) part[ch - r0 + n][w] = pw;
+      raw_to_f32<DT>(raw[u], x);
+      if (rag) mask_shift(x, shift);
+      const float2 tc = act ? st.tc[b] : make_float2(0.f, 0.f);
+      const float2 pw = row_partial<1>(x, tc.x, tc.y);
+      if (l16 == 0 && act) a.ws.tpart[(size_t)g * NT + tr] = pw;
     }
-    __syncthreads();
-    const int tr = r0 + tid;
-    if (tr < NT) {
-      const int b = tr / (a.k + 1), j = tr - b * (a.k + 1);
-      if (j <= stream_gamma(a, b)) {
-        float chi, clo;
-        temp_split(stream_temp(a, b), chi, clo);
-        float2 p[kWaves];
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) p[ww] = part[tid][ww];
-        a.ws.tpart[(size_t)tr * a.NG + g] = combine_waves(p, chi, clo);
-      }
-    }
-    __syncthreads();
+  };
+  Raw16<DT> ra[U], rbuf[U];
+  load_batch(0, ra);
+  for (int r0 = 0; r0 < NT; r0 += 2 * RS * U) {
+    load_batch(r0 + RS * U, rbuf);
+    consume(r0, ra);
+    if (r0 + RS * U >= NT) break;
+    load_batch(r0 + 2 * RS * U, ra);
+    consume(r0 + RS * U, rbuf);
+  }
+}
+
+// VEC (rows 16-byte aligned, V >= 16) is a whole-kernel choice made on the host.
+template <int DT, int KS, bool MARKOV, bool VEC>
+__global__ __launch_bounds__(kThreads, 2) void pass1_kernel(Args a) {
+  extern __shared__ char smem[];
+  __shared__ float2 part[kFlush * kChunk][kWaves];
+  const StreamTable st = build_stream_table(a, smem);
+  const int g = blockIdx.x;
+  // alternate the phase order so that MFMA-heavy and streaming phases overlap across the chip
+  if (g & 1) {
+    pass1_target<DT, VEC>(a, st, g);
+    pass1_draft<DT, KS, MARKOV, VEC>(a, st, g, part);
+  } else {
+    pass1_draft<DT, KS, MARKOV, VEC>(a, st, g, part);
+    pass1_target<DT, VEC>(a, st, g);
   }
 }
 
 // ---------------------------------------------------------------------------
 // scan: one workgroup per stream.
 // ---------------------------------------------------------------------------
-// Row normaliser from the group partials: M = max m_g, log2 S = log2 sum s_g 2^((m_g - M) c).
-__device__ void row_norm(const float2* __restrict__ parts, int NG, double c, int l, float& M_out, double& l2s_out) {
+// Row normaliser from its group partials (group-major, `nrows` rows per group):
+// M = max m_g, log2 S = log2 sum s_g 2^((m_g - M) c).  One wave per row; each lane
+// loads 8 partials at a time, and the wave-uniform running max rescales the sums.
+__device__ __forceinline__ void row_norm(const float2* __restrict__ part, int row, int nrows, int ng, double c, int l,
+                                         float& M_out, double& l2s_out) {
   float M = -INFINITY;
-  for (int gi = l; gi < NG; gi += 64) M = fmaxf(M, parts[gi].x);
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   double S = 0.0;
-  for (int gi = l; gi < NG; gi += 64) {
-    const float2 p = parts[gi];
-    if (p.x != -INFINITY) S += (double)p.y * exp2(((double)p.x - (double)M) * c);
+  for (int g0 = 0; g0 < ng; g0 += 512) {
+    float2 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int g = g0 + l + 64 * i;
+      v[i] = g < ng ? part[(size_t)g * nrows + row] : make_float2(-INFINITY, 0.f);
+    }
+    float m = v[0].x;
+#pragma unroll
+    for (int i = 1; i < 8; ++i) m = fmaxf(m, v[i].x);
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (m > M) {
+      if (M != -INFINITY) S *= exp2(((double)M - (double)m) * c);
+      M = m;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (v[i].x != -INFINITY) S += (double)v[i].y * exp2(((double)v[i].x - (double)M) * c);
   }
-  for (int off = 32; off >= 1; off >>= 1) S += __shfl_xor(S, off);
+  S = wave_sum(S);
   M_out = M;
   l2s_out = log2(S);
 }
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
-  __shared__ double s_lpx[kMaxK], s_lqx[kMaxK];
+  __shared__ float s_M[2 * kMaxK + 1];
+  __shared__ double s_l2s[2 * kMaxK + 1];
+  __shared__ double s_lt[kMaxK], s_ld[kMaxK], s_u[kMaxK], s_lr[kMaxK], s_lp[kMaxK + 1];
+  __shared__ int s_base;
+  __shared__ uint32_t s_mask;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int gamma = stream_gamma(a, b);
   const double T = (double)stream_temp(a, b);
   const double c = kLog2e / T;
   const int k1 = a.k + 1;
-
-  // normalisers: rows handled one per wave
-  for (int r = w; r < 2 * gamma + 1; r += kWaves) {
-    float M; double l2s;
-    if (r <= gamma) {
-      const int tr = b * k1 + r;
-      row_norm(a.ws.tpart + (size_t)tr * a.NG, a.NG, c, l, M, l2s);
-      if (l == 0) { a.ws.tm[tr] = M; a.ws.tl2s[tr] = l2s; }
-    } else {
-      const int dr = b * a.k + (r - gamma - 1);
-      row_norm(a.ws.dpart + (size_t)dr * a.NG, a.NG, c, l, M, l2s);
-      if (l == 0) { a.ws.dm[dr] = M; a.ws.dl2s[dr] = l2s; }
-    }
-  }
-  __syncthreads();
-
-  // gathered log-probabilities of the drafts, one wave per slot
+  const int NT = a.B * k1, ND = a.B * a.k;
   const size_t esz = DT == kBF16 ? 2 : 4;
-  for (int j = w; j < gamma; j += kWaves) {
-    const int x = clamp_tok(a.tokens[b * a.k + j], a.V);
+  const int nrows = 2 * gamma + 1;
+
+  if (tid < gamma) s_u[tid] = accept_uniform(a.key0, a.key1, (uint32_t)b, (uint32_t)tid, a.step);
+
+  // gathered logits at the drafts, 16 lanes per slot; the bias dot product in fp64
+  for (int j0 = 0; j0 < gamma; j0 += kThreads / 16) {
+    const int j = j0 + (tid >> 4), l16 = tid & 15;
     double bias = 0.0;
-    if (a.W1 != nullptr) {
-      const int prev = draft_prev(a, b, j);
-      if (prev >= 0) {
-        for (int r = l; r < a.R; r += 64)
-          bias += (double)bf16_to_f32(a.W1[(size_t)prev * a.R + r]) * (double)bf16_to_f32(a.W2t[(size_t)x * a.R + r]);
-      }
-      for (int off = 32; off >= 1; off >>= 1) bias += __shfl_xor(bias, off);
-    }
-    if (l == 0) {
+    double lt = 0.0, ld = 0.0;
+    if (j < gamma) {
+      const int x = clamp_tok(a.tokens[b * a.k + j], a.V);
       const int tr = b * k1 + j, dr = b * a.k + j;
-      const double lt = load1<DT>(reinterpret_cast<const char*>(a.target) + (size_t)tr * a.V * esz, x);
-      const double ld = (double)load1<DT>(reinterpret_cast<const char*>(a.draft) + (size_t)dr * a.V * esz, x) + bias;
-      const double lpx = (lt - (double)a.ws.tm[tr]) / T - a.ws.tl2s[tr] * kLn2;
-      const double lqx = (ld - (double)a.ws.dm[dr]) / T - a.ws.dl2s[dr] * kLn2;
-      s_lpx[j] = lpx; s_lqx[j] = lqx;
-      a.ws.lpx[dr] = lpx; a.ws.lqx[dr] = lqx;
+      if (l16 == 0) {
+        lt = load1<DT>(reinterpret_cast<const char*>(a.target) + (size_t)tr * a.V * esz, x);
+        ld = load1<DT>(reinterpret_cast<const char*>(a.draft) + (size_t)dr * a.V * esz, x);
+      }
+      const int prev = a.W1 != nullptr ? draft_prev(a, b, j) : -1;
+      if (prev >= 0) {
+        for (int r = 16 * l16; r < a.R; r += 256) {
+          const uint4* p1 = reinterpret_cast<const uint4*>(a.W1 + (size_t)prev * a.R + r);
+          const uint4* p2 = reinterpret_cast<const uint4*>(a.W2t + (size_t)x * a.R + r);
+          const uint4 u0 = p1[0], u1 = p1[1], v0 = p2[0], v1 = p2[1];
+          const uint32_t wa[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+          const uint32_t wb[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            bias += (double)bf16lo(wa[i]) * (double)bf16lo(wb[i]) + (double)bf16hi(wa[i]) * (double)bf16hi(wb[i]);
+        }
+      }
+    }
+    for (int off = 8; off >= 1; off >>= 1) bias += __shfl_xor(bias, off);
+    if (j < gamma && l16 == 0) {
+      s_lt[j] = lt;
+      s_ld[j] = ld + bias;
+    }
+  }
+
+  // row normalisers, one wave per row
+  for (int r = w; r < nrows; r += kWaves) {
+    const bool is_t = r <= gamma;
+    const int row = is_t ? b * k1 + r : b * a.k + (r - gamma - 1);
+    float M;
+    double l2s;
+    row_norm(is_t ? a.ws.tpart : a.ws.dpart, row, is_t ? NT : ND, a.NG, c, l, M, l2s);
+    if (l == 0) {
+      s_M[r] = M;
+      s_l2s[r] = l2s;
+      if (is_t) { a.ws.tm[row] = M; a.ws.tl2s[row] = l2s; }
+      else { a.ws.dm[row] = M; a.ws.dl2s[row] = l2s; }
     }
   }
   __syncthreads();
 
+  // per slot, in parallel: log p_j(x_j), log q_j(x_j), log r_j
+  if (tid < gamma) {
+    const int j = tid;
+    const double lpx = (s_lt[j] - (double)s_M[j]) / T - s_l2s[j] * kLn2;
+    const double lqx = (s_ld[j] - (double)s_M[gamma + 1 + j]) / T - s_l2s[gamma + 1 + j] * kLn2;
+    a.ws.lpx[b * a.k + j] = lpx;
+    a.ws.lqx[b * a.k + j] = lqx;
+    s_lr[j] = lpx - lqx;
+  }
+  __syncthreads();
   if (tid == 0) {
     // token-wise stop t: first j with u_j > min(1, r_j)
     int t = gamma;
     for (int j = 0; j < gamma; ++j) {
-      const double lr = s_lpx[j] - s_lqx[j];
-      const double thr = lr >= 0.0 ? 1.0 : exp(lr);
-      const double u = accept_uniform(a.key0, a.key1, (uint32_t)b, (uint32_t)j, a.step);
-      if (!(u <= thr)) { t = j; break; }
+      const double thr = s_lr[j] >= 0.0 ? 1.0 : exp(s_lr[j]);
+      if (!(s_u[j] <= thr)) { t = j; break; }
     }
     // clipped prefix log P_i
-    double lp[kMaxK + 1];
-    lp[0] = 0.0;
+    s_lp[0] = 0.0;
     for (int i = 1; i <= gamma; ++i) {
-      const double v = lp[i - 1] + (s_lpx[i - 1] - s_lqx[i - 1]);
-      lp[i] = v < 0.0 ? v : 0.0;
+      const double v = s_lp[i - 1] + s_lr[i - 1];
+      s_lp[i] = v < 0.0 ? v : 0.0;
     }
-    for (int i = 0; i <= gamma; ++i) a.ws.logP[b * k1 + i] = lp[i];
     uint32_t mask = 0;
     int stop = 0, f = 0;
     if (a.method == 0) {
       stop = t;
       if (t < gamma) mask = 1u << t;
     } else {
-      if (gamma == 0 || accept_uniform(a.key0, a.key1, (uint32_t)b, (uint32_t)(gamma - 1), a.step) <= exp(lp[gamma])) {
+      if (gamma == 0 || s_u[gamma - 1] <= exp(s_lp[gamma])) {
         stop = gamma;   // top test passed (or no drafts): tau = gamma
       } else {
-        for (int i = gamma - 1; i >= 0; --i) if (lp[i] == 0.0) { f = i; break; }
+        for (int i = gamma - 1; i >= 0; --i) if (s_lp[i] == 0.0) { f = i; break; }
         mask = 1u << f;  // tau >= f; row f may be sampled
-        for (int i = f + 1; i < gamma; ++i) {
-          const double u = accept_uniform(a.key0, a.key1, (uint32_t)b, (uint32_t)(i - 1), a.step);
-          if (u <= exp(lp[i])) mask |= 1u << i;   // h_i <= P_i: only these can pass
-        }
+        for (int i = f + 1; i < gamma; ++i)
+          if (s_u[i - 1] <= exp(s_lp[i])) mask |= 1u << i;   // h_i <= P_i: only these can pass
         stop = -1;
       }
     }
@@ -323,76 +598,124 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
     a.ws.info[4 * b + 2] = f;
     a.ws.info[4 * b + 3] = t;
     a.ws.rowmask[b] = mask;
-    for (int i = 0; i < gamma; ++i)
-      if (mask & (1u << i)) {
-        const int slot = atomicAdd(a.ws.nitems, 1);
-        a.ws.items[slot] = b * a.k + i;
+    s_mask = mask;
+    s_base = mask ? atomicAdd(a.ws.nitems, __popc(mask)) : 0;
+  }
+  __syncthreads();
+  if (tid <= gamma) a.ws.logP[b * k1 + tid] = s_lp[tid];
+  const uint32_t mask = s_mask;
+  if (tid < gamma && ((mask >> tid) & 1u)) {
+    const int i = tid;
+    Item it;
+    it.dr = b * a.k + i;
+    it.tr = b * k1 + i;
+    it.prev = a.W1 != nullptr ? draft_prev(a, b, i) : -1;
+    it.pad = 0;
+    it.Mt = s_M[i];
+    it.Md = s_M[gamma + 1 + i];
+    temp_split((float)T, it.chi, it.clo);
+    const double kp = (a.method == 1 ? s_lp[i] * kLog2e : 0.0) - s_l2s[i];
+    const double kq = -s_l2s[gamma + 1 + i];
+    it.kph = (float)kp;
+    it.kpl = (float)(kp - (double)it.kph);
+    it.kqh = (float)kq;
+    it.kql = (float)(kq - (double)it.kqh);
+    a.ws.items[s_base + __popc(mask & ((1u << i) - 1u))] = it;
+  }
+  // W1 tiles of the listed rows for pass 2 (pass 1, the only other reader, is done)
+  if (a.W1 != nullptr && mask != 0u) {
+    const int ks = a.R / 32;
+    int it = s_base;
+    for (int i = 0; i < gamma; ++i) {
+      if (!((mask >> i) & 1u)) continue;
+      if (tid < 4 * ks) {
+        const int kk = tid >> 2, q = tid & 3;
+        const int prev = draft_prev(a, b, i);
+        a.ws.btile[((size_t)(it >> 4) * ks + kk) * 64 + (it & 15) + 16 * q] =
+            prev >= 0 ? *reinterpret_cast<const uint4*>(a.W1 + (size_t)prev * a.R + kk * 32 + 8 * q)
+                      : make_uint4(0, 0, 0, 0);
       }
+      ++it;
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // pass2: residual group masses sum max(0, P_i p_i - q_i) of the listed rows.
+// The scan prepared one Item per listed row (row indices and exponent constants)
+// and its packed W1 tile.  Waves reduce 64 ids each; the 4 wave sums of a row meet
+// in LDS and are flushed every 256 rows.
 // ---------------------------------------------------------------------------
-template <int DT, int KS, bool MARKOV>
-__global__ __launch_bounds__(kThreads) void pass2_kernel(Args a) {
-  __shared__ float part[kSuper][kWaves];
-  const int g = blockIdx.x;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, q = l >> 4;
-  const int cb = g * kGroup + w * kWaveCols;
-  const int c0 = cb + 16 * q;
-  const bool vec = a.vec_ok != 0;
+template <int DT, int KS, bool MARKOV, bool VEC>
+__global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
+  __shared__ float part[kFlush * kChunk][kWaves];
   const int NI = *a.ws.nitems;
   if (NI == 0) return;
-  const int k1 = a.k + 1;
-  const size_t esz = DT == kBF16 ? 2 : 4;
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, q = l >> 4;
+  const int cb = (g * kWaves + w) * kWaveCols;
+  const int cw = cb + 16 * q;
+  const int c0 = VEC ? min(cw, a.V - 16) : cw;
+  const int shift = VEC ? (cw >= a.V ? 16 : cw - c0) : 0;
+  const bool rag = VEC && cb + kWaveCols > a.V;
+  const size_t rb = (size_t)a.V * (DT == kBF16 ? 2 : 4);
+  const int nch = (NI + kChunk - 1) / kChunk;
+  const int ND = a.B * a.k;
 
   bf16x8 A[4][KS];
-  if (MARKOV) load_w2_slab<KS>(a, cb, n, q, A);
-  for (int r0 = 0; r0 < NI; r0 += kSuper) {
-    for (int ch = r0; ch < r0 + kSuper && ch < NI; ch += kChunk) {
-      const int it = ch + n;
-      const bool active = it < NI;
-      const int dr = active ? a.ws.items[it] : 0;
-      const int b = dr / a.k, i = dr - b * a.k;
-      float bias[16];
-      if (MARKOV) markov_tile<KS>(a, A, active ? draft_prev(a, b, i) : -1, q, bias);
-      float s = 0.f;
-      if (active) {
-        const int tr = b * k1 + i;
-        float xt[16], xd[16];
-        load16<DT>(reinterpret_cast<const char*>(a.target) + (size_t)tr * a.V * esz, c0, a.V, vec, xt);
-        load16<DT>(reinterpret_cast<const char*>(a.draft) + (size_t)dr * a.V * esz, c0, a.V, vec, xd);
-        float chi, clo;
-        temp_split(stream_temp(a, b), chi, clo);
-        const float Mt = a.ws.tm[tr], Md = a.ws.dm[dr];
-        // exponent constants in log2 units, split hi + lo
-        const double kp = (a.method == 1 ? a.ws.logP[tr] * kLog2e : 0.0) - a.ws.tl2s[tr];
-        const double kq = -a.ws.dl2s[dr];
-        const float kph = (float)kp, kpl = (float)(kp - (double)kph);
-        const float kqh = (float)kq, kql = (float)(kq - (double)kqh);
+  bf16x8 Bc[KS];
+  if (MARKOV) {
+    load_w2_slab<KS, VEC>(a, cb, n, q, A);
+    load_btile<KS>(a, 0, l, Bc);
+  }
+  auto item_at = [&](int c) {
+    const int it = c * kChunk + n;
+    return it < NI ? it : NI - 1;
+  };
+  auto fetch = [&](int c, Raw16<DT>& t, Raw16<DT>& d) {
+    if (c < nch) {
+      const int2 h = *reinterpret_cast<const int2*>(&a.ws.items[item_at(c)].dr);   // (dr, tr)
+      raw_load<DT, VEC>(t, reinterpret_cast<const char*>(a.target) + (size_t)h.y * rb, c0, a.V);
+      raw_load<DT, VEC>(d, reinterpret_cast<const char*>(a.draft) + (size_t)h.x * rb, c0, a.V);
+    }
+  };
+  Raw16<DT> tb, db;
+  fetch(0, tb, db);
+  for (int c = 0; c < nch; ++c) {
+    float bias[16];
+    if (MARKOV) {
+      markov_mma<KS>(A, Bc, bias);
+      if (c + 1 < nch) load_btile<KS>(a, c + 1, l, Bc);
+    }
+    const float4* kc = reinterpret_cast<const float4*>(&a.ws.items[item_at(c)].Mt);
+    const float4 k0 = kc[0], k1 = kc[1];   // (Mt, Md, chi, clo), (kph, kpl, kqh, kql)
+    float xt[16], xd[16];
+    raw_to_f32<DT>(tb, xt);
+    raw_to_f32<DT>(db, xd);
+    fetch(c + 1, tb, db);
+    if (rag) mask_shift(xt, shift);
+    float s = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float tp = xt[e] - Mt;
-          const float d = MARKOV ? xd[e] + bias[e] : xd[e];
-          const float tq = d - Md;
-          const float ep = fmaf(tp, chi, kph) + fmaf(tp, clo, kpl);
-          const float eq = fmaf(tq, chi, kqh) + fmaf(tq, clo, kql);
-          const float pv = __builtin_amdgcn_exp2f(ep), qv = __builtin_amdgcn_exp2f(eq);
-          const float wv = pv - qv;
-          s += (c0 + e < a.V && wv > 0.f) ? wv : 0.f;
-        }
+    for (int e = 0; e < 16; ++e) {
+      const float tp = xt[e] - k0.x;
+      const float d = MARKOV ? xd[e] + bias[e] : xd[e];
+      const float tq = d - k0.y;
+      const float ep = fmaf(tp, k0.z, k1.x) + fmaf(tp, k0.w, k1.y);
+      const float eq = fmaf(tq, k0.z, k1.z) + fmaf(tq, k0.w, k1.w);
+      const float wv = __builtin_amdgcn_exp2f(ep) - __builtin_amdgcn_exp2f(eq);
+      s += ((VEC || c0 + e < a.V) && wv > 0.f) ? wv : 0.f;
+    }
+    s = sum4lanes(s);
+    if (q == 0) part[(c % kFlush) * kChunk + n][w] = s;
+    if (c % kFlush == kFlush - 1 || c == nch - 1) {
+      __syncthreads();
+      const int it = (c - c % kFlush) * kChunk + tid;
+      if (tid < (c % kFlush + 1) * kChunk && it < NI) {
+        const int dr = a.ws.items[it].dr;
+        a.ws.wgrp[(size_t)g * ND + dr] = (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]);
       }
-      s = sum4lanes(s);
-      if (q == 0) part[ch - r0 + n][w] = s;
+      __syncthreads();
     }
-    __syncthreads();
-    const int it = r0 + tid;
-    if (it < NI) {
-      const int dr = a.ws.items[it];
-      a.ws.wgrp[(size_t)dr * a.NG + g] = (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]);
-    }
-    __syncthreads();
   }
 }
 
@@ -401,7 +724,7 @@ __global__ __launch_bounds__(kThreads) void pass2_kernel(Args a) {
 // ---------------------------------------------------------------------------
 __device__ double block_sum(double v, double* red) {
   const int tid = threadIdx.x;
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  v = wave_sum(v);
   if ((tid & 63) == 0) red[tid >> 6] = v;
   __syncthreads();
   const double r = (red[0] + red[1]) + (red[2] + red[3]);
@@ -425,109 +748,133 @@ __device__ void block_argmax(double& score, int& idx, double* rs, int* ri) {
   __syncthreads();
 }
 
-template <int DT>
+// Markov bias at one vocabulary id in fp64: sum_r W1[prev, r] W2t[v, r] (R = 32 KS).
+template <int KS>
+__device__ __forceinline__ double bias_at(const Args& a, int prev, int v) {
+  const uint4* p1 = reinterpret_cast<const uint4*>(a.W1 + (size_t)prev * (32 * KS));
+  const uint4* p2 = reinterpret_cast<const uint4*>(a.W2t + (size_t)v * (32 * KS));
+  uint4 u[4 * KS], x[4 * KS];
+#pragma unroll
+  for (int i = 0; i < 4 * KS; ++i) { u[i] = p1[i]; x[i] = p2[i]; }
+  double acc = 0.0;
+#pragma unroll
+  for (int i = 0; i < 4 * KS; ++i) {
+    const uint32_t wa[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
+    const uint32_t wb[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc += (double)bf16lo(wa[e]) * (double)bf16lo(wb[e]) + (double)bf16hi(wa[e]) * (double)bf16hi(wb[e]);
+  }
+  return acc;
+}
+
+template <int DT, int KS>
 __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
   __shared__ double red[kWaves];
   __shared__ double rs[kWaves];
   __shared__ int ri[kWaves];
   __shared__ double s_R[kMaxK], s_h[kMaxK + 1];
   const int b = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int k1 = a.k + 1;
-  const int gamma = a.ws.info[4 * b + 0];
-  int stop = a.ws.info[4 * b + 1];
-  const int f = a.ws.info[4 * b + 2];
+  const int NG = a.NG;
+  const int NT = a.B * k1, ND = a.B * a.k;
+  const int4 info = *reinterpret_cast<const int4*>(a.ws.info + 4 * b);
+  const int gamma = info.x, f = info.z;
+  int stop = info.y;
   const uint32_t mask = a.ws.rowmask[b];
   const double T = (double)stream_temp(a, b);
   const double c = kLog2e / T;
   const size_t esz = DT == kBF16 ? 2 : 4;
 
+  // group clocks do not depend on the data: computed while the loads below are in flight
+  double Eg[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int gi = tid + kThreads * t;
+    Eg[t] = gi < NG ? race_clock(a.key0, a.key1, (uint32_t)b, (uint32_t)gi, kPurposeRaceGroup, a.step) : 1.0;
+  }
   if (tid <= kMaxK) s_h[tid] = NAN;
   if (tid < kMaxK) s_R[tid] = NAN;
   __syncthreads();
-  // residual masses R_i of the candidate rows above f
+
+  // residual masses R_i of the candidate rows above f, one wave per row
   if (a.method == 1 && stop < 0) {
+    int ci = 0;
     for (int i = f + 1; i < gamma; ++i) {
-      if (!(mask & (1u << i))) continue;
-      const float* wr = a.ws.wgrp + (size_t)(b * a.k + i) * a.NG;
-      double v = 0.0;
-      for (int gi = tid; gi < a.NG; gi += kThreads) v += (double)wr[gi];
-      const double R = block_sum(v, red);
-      if (tid == 0) {
-        const double lp = a.ws.logP[b * k1 + i];
-        s_R[i] = R;
-        s_h[i] = R / (R - expm1(lp));
+      if (!((mask >> i) & 1u)) continue;
+      if ((ci & (kWaves - 1)) == w) {
+        const int dr = b * a.k + i;
+        double v = 0.0;
+        for (int gi = l; gi < NG; gi += 64) v += (double)a.ws.wgrp[(size_t)gi * ND + dr];
+        v = wave_sum(v);
+        if (l == 0) {
+          s_R[i] = v;
+          s_h[i] = v / (v - expm1(a.ws.logP[b * k1 + i]));
+        }
       }
+      ++ci;
     }
     __syncthreads();
     // tau: the highest i whose test passes; rows outside the mask cannot pass (u > P_i >= h_i)
     stop = f;
     for (int i = gamma - 1; i > f; --i) {
-      if (!(mask & (1u << i))) continue;
-      const double u = accept_uniform(a.key0, a.key1, (uint32_t)b, (uint32_t)(i - 1), a.step);
-      if (u <= s_h[i]) { stop = i; break; }
+      if (!((mask >> i) & 1u)) continue;
+      if (accept_uniform(a.key0, a.key1, (uint32_t)b, (uint32_t)(i - 1), a.step) <= s_h[i]) { stop = i; break; }
     }
   }
   const int s = stop;
+  const int tr = b * k1 + s;
+  const int dr = b * a.k + (s < gamma ? s : 0);
 
-  // weights of the sampled row: bonus / fallback use the target's own group partials
+  // group masses of the sampled row: the residual (pass 2) or, for the bonus row
+  // and an all-zero residual, the target's own partials
   bool use_p = (s == gamma);
-  const float* wr = a.ws.wgrp + (size_t)(b * a.k + (s < gamma ? s : 0)) * a.NG;
   if (!use_p) {
     double v = 0.0;
-    for (int gi = tid; gi < a.NG; gi += kThreads) v += (double)wr[gi];
-    const double tot = block_sum(v, red);
-    if (!(tot > 0.0)) use_p = true;   // all-zero residual: draw from p_s
+    for (int gi = tid; gi < NG; gi += kThreads) v += (double)a.ws.wgrp[(size_t)gi * ND + dr];
+    if (!(block_sum(v, red) > 0.0)) use_p = true;
   }
-  const int tr = b * k1 + s;
-  const float2* tp = a.ws.tpart + (size_t)tr * a.NG;
   const double Mt = (double)a.ws.tm[tr];
-
-  // group race
   double best = -1.0;
   int gbest = 0x7fffffff;
-  for (int gi = tid; gi < a.NG; gi += kThreads) {
+  for (int gi = tid, t = 0; gi < NG; gi += kThreads, ++t) {
     double W;
     if (use_p) {
-      const float2 p = tp[gi];
+      const float2 p = a.ws.tpart[(size_t)gi * NT + tr];
       W = p.x == -INFINITY ? 0.0 : (double)p.y * exp2(((double)p.x - Mt) * c);
     } else {
-      W = (double)wr[gi];
+      W = (double)a.ws.wgrp[(size_t)gi * ND + dr];
     }
     if (W > 0.0) {
-      const double sc = W / race_clock(a.key0, a.key1, (uint32_t)b, (uint32_t)gi, kPurposeRaceGroup, a.step);
+      const double E = t < 2 ? Eg[t < 2 ? t : 0]
+                             : race_clock(a.key0, a.key1, (uint32_t)b, (uint32_t)gi, kPurposeRaceGroup, a.step);
+      const double sc = W / E;
       if (sc > best) { best = sc; gbest = gi; }
     }
   }
   block_argmax(best, gbest, rs, ri);
-  const int gsel = gbest < a.NG ? gbest : 0;
+  const int gsel = gbest < NG ? gbest : 0;
 
-  // race inside the group, weights recomputed in fp64
+  // race inside the winning group, weights recomputed in fp64
   const int v = gsel * kGroup + tid;
   double sc = -1.0;
   if (v < a.V) {
+    const double E = race_clock(a.key0, a.key1, (uint32_t)b, (uint32_t)v, kPurposeRaceItem, a.step);
     const double lt = load1<DT>(reinterpret_cast<const char*>(a.target) + (size_t)tr * a.V * esz, v);
     double wv;
     if (use_p) {
       wv = exp2((lt - Mt) * c);
     } else {
-      const int dr = b * a.k + s;
       double d = load1<DT>(reinterpret_cast<const char*>(a.draft) + (size_t)dr * a.V * esz, v);
-      if (a.W1 != nullptr) {
-        const int prev = draft_prev(a, b, s);
-        if (prev >= 0) {
-          double bias = 0.0;
-          for (int r = 0; r < a.R; ++r)
-            bias += (double)bf16_to_f32(a.W1[(size_t)prev * a.R + r]) * (double)bf16_to_f32(a.W2t[(size_t)v * a.R + r]);
-          d += bias;
-        }
-      }
-      const double lpP = (a.method == 1 ? a.ws.logP[tr] * kLog2e : 0.0);
+      const int prev = a.W1 != nullptr ? draft_prev(a, b, s) : -1;
+      if (prev >= 0) d += bias_at<KS>(a, prev, v);
+      const double lpP = a.method == 1 ? a.ws.logP[tr] * kLog2e : 0.0;
       const double pv = exp2((lt - Mt) * c - a.ws.tl2s[tr] + lpP);
       const double qv = exp2((d - (double)a.ws.dm[dr]) * c - a.ws.dl2s[dr]);
       wv = pv - qv;
     }
-    if (wv > 0.0) sc = wv / race_clock(a.key0, a.key1, (uint32_t)b, (uint32_t)v, kPurposeRaceItem, a.step);
+    if (wv > 0.0) sc = wv / E;
   }
   int vbest = sc >= 0.0 ? v : 0x7fffffff;
   block_argmax(sc, vbest, rs, ri);
@@ -600,68 +947,121 @@ __global__ __launch_bounds__(kThreads) void markov_bias_kernel(BiasArgs ba) {
 }
 
 // ---------------------------------------------------------------------------
-// Confidence head + adaptive count.  One wave per stream.
+// Confidence head + adaptive count.  One workgroup per stream: each thread owns
+// 16 hidden features of every slot, so all of a stream's loads are in flight at once.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void adaptive_kernel(AdaptArgs aa) {
+  __shared__ double red[kWaves][kMaxK];
+  __shared__ double s_c[kMaxK];
+  const int b = blockIdx.x;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int b = blockIdx.x * kWaves + w;
-  if (b >= aa.B) return;
-  double surv = 1.0, expected = 1.0;
-  double best = 1.0 / (double)aa.ms[1];
-  int nbest = 0;
-  for (int j = 0; j < aa.k; ++j) {
-    const uint16_t* h = aa.hidden + ((size_t)b * aa.k + j) * aa.H;
-    double z = 0.0;
-    for (int e = l; e < aa.H; e += 64) z += (double)bf16_to_f32(h[e]) * (double)bf16_to_f32(aa.w[e]);
-    for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
-    z += (double)aa.bias;
-    const double cj = 1.0 / (1.0 + exp(-z));
-    surv *= cj;
-    expected += surv;                         // 1 + sum_{i<=j} a_i = E(n = j + 1)
-    const double ratio = expected / (double)aa.ms[j + 2];
-    if (ratio > best) { best = ratio; nbest = j + 1; }
-    if (l == 0) {
-      if (aa.c_out) aa.c_out[b * aa.k + j] = (float)cj;
-      if (aa.a_out) aa.a_out[b * aa.k + j] = (float)surv;
+  double z[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) z[j] = 0.0;
+  for (int c0 = 16 * tid; c0 < aa.H; c0 += 16 * kThreads) {
+    float wv[16];
+    if (aa.vec_ok && c0 + 16 <= aa.H) {
+      const uint4 u0 = *reinterpret_cast<const uint4*>(aa.w + c0), u1 = *reinterpret_cast<const uint4*>(aa.w + c0 + 8);
+      const uint32_t ww[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { wv[2 * i] = bf16lo(ww[i]); wv[2 * i + 1] = bf16hi(ww[i]); }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) wv[i] = (c0 + i < aa.H) ? bf16_to_f32(aa.w[c0 + i]) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j >= aa.k) break;
+      const uint16_t* h = aa.hidden + ((size_t)b * aa.k + j) * aa.H;
+      float hv[16];
+      if (aa.vec_ok && c0 + 16 <= aa.H) {
+        const uint4 u0 = *reinterpret_cast<const uint4*>(h + c0), u1 = *reinterpret_cast<const uint4*>(h + c0 + 8);
+        const uint32_t hh[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { hv[2 * i] = bf16lo(hh[i]); hv[2 * i + 1] = bf16hi(hh[i]); }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) hv[i] = (c0 + i < aa.H) ? bf16_to_f32(h[c0 + i]) : 0.f;
+      }
+      double acc = 0.0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc += (double)hv[i] * (double)wv[i];
+      z[j] += acc;
     }
   }
-  if (l == 0) aa.n_out[b] = nbest;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j >= aa.k) break;
+    const double v = wave_sum(z[j]);
+    if (l == 0) red[w][j] = v;
+  }
+  __syncthreads();
+  if (tid < aa.k) {
+    const double zz = ((red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid])) + (double)aa.bias;
+    const double cj = 1.0 / (1.0 + exp(-zz));
+    s_c[tid] = cj;
+    if (aa.c_out) aa.c_out[b * aa.k + tid] = (float)cj;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double surv = 1.0, expected = 1.0;
+    double best = 1.0 / (double)aa.ms[1];
+    int nbest = 0;
+    for (int j = 0; j < aa.k; ++j) {
+      surv *= s_c[j];
+      expected += surv;                      // 1 + sum_{i<=j} a_i = E(n = j + 1)
+      if (aa.a_out) aa.a_out[b * aa.k + j] = (float)surv;
+      const double ratio = expected / (double)aa.ms[j + 2];
+      if (ratio > best) { best = ratio; nbest = j + 1; }
+    }
+    aa.n_out[b] = nbest;
+  }
 }
 
 // ---------------------------------------------------------------------------
 // launch wrappers (host side of this translation unit)
 // ---------------------------------------------------------------------------
-template <int DT, int KS, bool MARKOV>
+template <int DT, int KS, bool MARKOV, bool VEC>
 static hipError_t launch_passes(const Args& a, hipStream_t st, void* const* ev) {
   auto mark = [&](int i) {
     if (ev != nullptr && ev[i] != nullptr) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[i]), st);
   };
+  const int nchd = (a.B * a.k + kChunk - 1) / kChunk;
   mark(0);
-  hipLaunchKernelGGL((pass1_kernel<DT, KS, MARKOV>), dim3(a.NG), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL(pack_kernel, dim3(nchd), dim3(64), 0, st, a);
   mark(1);
-  hipLaunchKernelGGL((scan_kernel<DT>), dim3(a.B), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((pass1_kernel<DT, KS, MARKOV, VEC>), dim3(a.NG), dim3(kThreads), stream_table_bytes(a.B), st, a);
   mark(2);
-  hipLaunchKernelGGL((pass2_kernel<DT, KS, MARKOV>), dim3(a.NG), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((scan_kernel<DT>), dim3(a.B), dim3(kThreads), 0, st, a);
   mark(3);
-  hipLaunchKernelGGL((finalize_kernel<DT>), dim3(a.B), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((pass2_kernel<DT, KS, MARKOV, VEC>), dim3(a.NG), dim3(kThreads), 0, st, a);
   mark(4);
+  hipLaunchKernelGGL((finalize_kernel<DT, KS>), dim3(a.B), dim3(kThreads), 0, st, a);
+  mark(5);
   return hipGetLastError();
+}
+
+template <int DT, bool VEC>
+static hipError_t launch_vec(const Args& a, hipStream_t st, void* const* ev) {
+  if (a.W1 == nullptr) return launch_passes<DT, 1, false, VEC>(a, st, ev);
+  switch (a.R) {
+    case 32: return launch_passes<DT, 1, true, VEC>(a, st, ev);
+    case 64: return launch_passes<DT, 2, true, VEC>(a, st, ev);
+    case 128: return launch_passes<DT, 4, true, VEC>(a, st, ev);
+    default: return launch_passes<DT, 8, true, VEC>(a, st, ev);
+  }
 }
 
 template <int DT>
 static hipError_t launch_dt(const Args& a, hipStream_t st, void* const* ev) {
-  if (a.W1 == nullptr) return launch_passes<DT, 1, false>(a, st, ev);
-  switch (a.R) {
-    case 32: return launch_passes<DT, 1, true>(a, st, ev);
-    case 64: return launch_passes<DT, 2, true>(a, st, ev);
-    case 128: return launch_passes<DT, 4, true>(a, st, ev);
-    default: return launch_passes<DT, 8, true>(a, st, ev);
-  }
+  return (a.vec_ok && a.V >= 16) ? launch_vec<DT, true>(a, st, ev) : launch_vec<DT, false>(a, st, ev);
 }
 
 hipError_t launch_verify(const Args& a, hipStream_t st, void* const* ev) {
   return a.dtype == kBF16 ? launch_dt<kBF16>(a, st, ev) : launch_dt<kF32>(a, st, ev);
 }
+
+size_t verify_lds_bytes(int B) { return stream_table_bytes(B); }
 
 template <int DT>
 static hipError_t launch_bias_dt(const BiasArgs& ba, int NG, hipStream_t st) {
@@ -679,7 +1079,7 @@ hipError_t launch_markov_bias(const BiasArgs& ba, int NG, hipStream_t st) {
 }
 
 hipError_t launch_adaptive(const AdaptArgs& aa, hipStream_t st) {
-  hipLaunchKernelGGL(adaptive_kernel, dim3((aa.B + kWaves - 1) / kWaves), dim3(kThreads), 0, st, aa);
+  hipLaunchKernelGGL(adaptive_kernel, dim3(aa.B), dim3(kThreads), 0, st, aa);
   return hipGetLastError();
 }
 

@@ -44,7 +44,8 @@ extern "C" {
 typedef enum {
   DSPARK_OK = 0,
   DSPARK_ERR_INVALID_ARG = 1, /* NULL required pointer, non-positive size, k > 32 ... */
-  DSPARK_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. rank R not in {32,64,128,256}) */
+  DSPARK_ERR_UNSUPPORTED = 2, /* valid but not implemented: rank R not in {32,64,128,256},
+                                 W1/W2t not 16-byte aligned, or B > 4096 */
   DSPARK_ERR_WORKSPACE = 3,   /* workspace NULL, misaligned (256 B) or smaller than required */
   DSPARK_ERR_HIP = 4          /* a HIP launch or device query failed */
 } dspark_status;
@@ -93,12 +94,12 @@ typedef struct {
                                      log q_j(x_j), P_j, R_j, h_j); NaN where not computed    */
   void* const* stage_events;      /* NULL, or DSPARK_STAGES + 1 hipEvent_t the call records on
                                      `stream` before its first launch and after each launch
-                                     (row statistics, scan, residual masses, sampler): a
-                                     timing hook, nothing is allocated                      */
+                                     (W1 tile packing, row statistics, scan, residual masses,
+                                     sampler): a timing hook, nothing is allocated          */
 } dspark_verify_outputs;
 
 /* Launches per verify call (see stage_events). */
-#define DSPARK_STAGES 4
+#define DSPARK_STAGES 5
 
 /* Bytes of workspace the two verify entry points need for this problem (host, pure).
  * Returns 0 if the problem's sizes are invalid. */
