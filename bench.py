@@ -80,6 +80,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=3, help="rotating copies of the input set")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (a known-size "
+                         "reference for hardware byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -214,6 +217,15 @@ def main() -> int:
         "step_alg_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "accepted_mean": {m: round(float(np.mean(realized[m])), 4) for m in realized},
     }
+
+    if args.copy_mib > 0:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_reference_bytes"] = 2 * (args.copy_mib << 20)
+        del src, dst
 
     if not args.no_cpu_baseline:
         from oracle import dspark as odsp   # cpu_baseline leg only

@@ -329,9 +329,13 @@ __device__ __forceinline__ void pass1_draft(const Args& a, const StreamTable& st
     return dr < ND && dr - b * a.k < st.gam[b < a.B ? b : a.B - 1];
   };
   auto row_of = [&](int c, int& b) { return row_of_dr(c * kChunk + n, b); };
+  // Loads are unconditional (no branch around them, so the wait counters stay exact):
+  // an inactive row reads its stream's first draft row, a chunk past the end the last row.
   auto load_x = [&](int c, Raw16<DT>& x) {
     int b;
-    if (c < nch && row_of(c, b)) raw_load<DT, VEC>(x, base + (size_t)(c * kChunk + n) * rb, c0, a.V);
+    const int dr = min(c * kChunk + n, ND - 1);
+    const int src = row_of_dr(dr, b) ? dr : b * a.k;
+    raw_load<DT, VEC>(x, base + (size_t)src * rb, c0, a.V);
   };
 
   bf16x8 A[4][KS];
@@ -340,46 +344,50 @@ __device__ __forceinline__ void pass1_draft(const Args& a, const StreamTable& st
     load_w2_slab<KS, VEC>(a, cb, n, q, A);
     load_btile<KS>(a, 0, l, Bc);
   }
-  Raw16<DT> xb[PD];
-#pragma unroll
-  for (int i = 0; i < PD; ++i) load_x(i, xb[i]);
-  for (int cbase = 0; cbase < nch; cbase += PD) {
-#pragma unroll
-    for (int i = 0; i < PD; ++i) {
-      const int c = cbase + i;
-      if (c >= nch) break;
-      float bias[16];
-      if (MARKOV) {
-        markov_mma<KS>(A, Bc, bias);
-        if (c + 1 < nch) load_btile<KS>(a, c + 1, l, Bc);
-      }
-      float x[16];
-      raw_to_f32<DT>(xb[i], x);
-      load_x(c + PD, xb[i]);
-      int b;
-      const bool act = row_of(c, b);
-      if (MARKOV) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] += bias[e];
-      }
-      if (rag) mask_shift(x, shift);
-      const float2 tc = act ? st.tc[b] : make_float2(0.f, 0.f);
-      const float2 pw = row_partial<0>(x, tc.x, tc.y);
-      if (q == 0) part[(c % kFlush) * kChunk + n][w] = pw;
-      if (c % kFlush == kFlush - 1 || c == nch - 1) {   // uniform: every wave runs the same chunks
-        __syncthreads();
-        const int dr = (c - c % kFlush) * kChunk + tid;
-        int bb;
-        if (tid < (c % kFlush + 1) * kChunk && row_of_dr(dr, bb)) {
-          float2 p[kWaves];
-#pragma unroll
-          for (int ww = 0; ww < kWaves; ++ww) p[ww] = part[tid][ww];
-          a.ws.dpart[(size_t)g * ND + dr] = combine_waves(p, st.tc[bb].x, st.tc[bb].y);
-        }
-        __syncthreads();
-      }
+  // one chunk: MFMA on the current tile, next tile in flight, reduce the logits in
+  // `xb`, then refill `xb` with the chunk PD ahead
+  auto chunk = [&](int c, Raw16<DT>& xb) {
+    float bias[16];
+    if (MARKOV) {
+      markov_mma<KS>(A, Bc, bias);
+      load_btile<KS>(a, min(c + 1, nch - 1), l, Bc);
     }
+    float x[16];
+    raw_to_f32<DT>(xb, x);
+    load_x(c + PD, xb);
+    int b;
+    const bool act = row_of(c, b);
+    if (MARKOV) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[e] += bias[e];
+    }
+    if (rag) mask_shift(x, shift);
+    const float2 tc = act ? st.tc[b] : make_float2(0.f, 0.f);
+    const float2 pw = row_partial<0>(x, tc.x, tc.y);
+    if (q == 0) part[(c % kFlush) * kChunk + n][w] = pw;
+    if (c % kFlush == kFlush - 1 || c == nch - 1) {   // uniform: every wave runs the same chunks
+      __syncthreads();
+      const int dr = (c - c % kFlush) * kChunk + tid;
+      int bb;
+      if (tid < (c % kFlush + 1) * kChunk && row_of_dr(dr, bb)) {
+        float2 p[kWaves];
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) p[ww] = part[tid][ww];
+        a.ws.dpart[(size_t)g * ND + dr] = combine_waves(p, st.tc[bb].x, st.tc[bb].y);
+      }
+      __syncthreads();
+    }
+  };
+  static_assert(PD == 2, "the chunk loop below is written for two logits buffers");
+  Raw16<DT> x0, x1;
+  load_x(0, x0);
+  load_x(1, x1);
+  int c = 0;
+  for (; c + 2 <= nch; c += 2) {
+    chunk(c, x0);
+    chunk(c + 1, x1);
   }
+  if (c < nch) chunk(c, x0);
 }
 
 // Target rows: a 16-lane DPP row covers the group's 256 ids of one row; the
@@ -402,12 +410,13 @@ __device__ __forceinline__ void pass1_target(const Args& a, const StreamTable& s
     b = tr / k1;
     return tr < NT && tr - b * k1 <= st.gam[b < a.B ? b : a.B - 1];
   };
-  auto load_batch = [&](int r0, Raw16<DT>(&raw)[U]) {
+  auto load_batch = [&](int r0, Raw16<DT>(&raw)[U]) {   // unconditional, as in the draft phase
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int tr = r0 + RS * u + rq;
+      const int tr = min(r0 + RS * u + rq, NT - 1);
       int b;
-      if (row_ok(tr, b)) raw_load<DT, VEC>(raw[u], base + (size_t)tr * rb, c0, a.V);
+      const int src = row_ok(tr, b) ? tr : b * k1;
+      raw_load<DT, VEC>(raw[u], base + (size_t)src * rb, c0, a.V);
     }
   };
   auto consume = [&](int r0, const Raw16<DT>(&raw)[U]) {
@@ -672,12 +681,10 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
     const int it = c * kChunk + n;
     return it < NI ? it : NI - 1;
   };
-  auto fetch = [&](int c, Raw16<DT>& t, Raw16<DT>& d) {
-    if (c < nch) {
-      const int2 h = *reinterpret_cast<const int2*>(&a.ws.items[item_at(c)].dr);   // (dr, tr)
-      raw_load<DT, VEC>(t, reinterpret_cast<const char*>(a.target) + (size_t)h.y * rb, c0, a.V);
-      raw_load<DT, VEC>(d, reinterpret_cast<const char*>(a.draft) + (size_t)h.x * rb, c0, a.V);
-    }
+  auto fetch = [&](int c, Raw16<DT>& t, Raw16<DT>& d) {   // unconditional: past the end re-reads the last item
+    const int2 h = *reinterpret_cast<const int2*>(&a.ws.items[item_at(min(c, nch - 1))].dr);   // (dr, tr)
+    raw_load<DT, VEC>(t, reinterpret_cast<const char*>(a.target) + (size_t)h.y * rb, c0, a.V);
+    raw_load<DT, VEC>(d, reinterpret_cast<const char*>(a.draft) + (size_t)h.x * rb, c0, a.V);
   };
   Raw16<DT> tb, db;
   fetch(0, tb, db);
@@ -685,7 +692,7 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
     float bias[16];
     if (MARKOV) {
       markov_mma<KS>(A, Bc, bias);
-      if (c + 1 < nch) load_btile<KS>(a, c + 1, l, Bc);
+      load_btile<KS>(a, min(c + 1, nch - 1), l, Bc);
     }
     const float4* kc = reinterpret_cast<const float4*>(&a.ws.items[item_at(c)].Mt);
     const float4 k0 = kc[0], k1 = kc[1];   // (Mt, Md, chi, clo), (kph, kpl, kqh, kql)
