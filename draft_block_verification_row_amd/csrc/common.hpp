@@ -198,10 +198,10 @@ struct AdaptArgs {
   float ms[kMaxMs];
 };
 
-// Dynamic LDS of pass 1 (the per-stream table, 12 bytes a stream); calls needing
+// Dynamic LDS of pass 1 (the per-stream table, 8 bytes a stream); calls needing
 // more than kMaxPassLds (B > 4096) are rejected as unsupported.
 size_t verify_lds_bytes(int B);
-constexpr size_t kMaxPassLds = 48 * 1024;
+constexpr size_t kMaxPassLds = 32 * 1024;
 
 // launchers (kernels.hip)
 hipError_t launch_verify(const Args& a, hipStream_t st, void* const* events);

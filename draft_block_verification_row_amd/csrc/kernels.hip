@@ -191,23 +191,31 @@ __device__ __forceinline__ void mask_shift(float (&x)[16], int shift) {
 
 // Partial (max, sum 2^((x - max) c)) of 16 values; RED selects the lanes that share
 // the row: 0 = the 4 lanes {n, n+16, n+32, n+48} (MFMA layout), 1 = a 16-lane DPP row.
+// With m c = mh + ml exactly (mh = fl(m c), ml = fma(m, c, -mh)), each term is
+// 2^(fma(x, c, -mh)) and the common factor 2^-ml is applied once: three operations
+// per value.  c is log2(e)/T rounded to fp32; its rounding moves a term by a relative
+// (x - m) c 2^-24, so the terms that carry the sum are exact to fp32 rounding.
 template <int RED>
-__device__ __forceinline__ float2 row_partial(const float (&x)[16], float chi, float clo) {
+__device__ __forceinline__ float2 row_partial(const float (&x)[16], float c) {
   float m = x[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) m = fmaxf(m, x[i]);
   m = RED == 0 ? max4lanes(m) : row16_max(m);
   float s = 0.f;
   if (m != -INFINITY) {
+    const float mh = m * c;
+    const float ml = fmaf(m, c, -mh);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float t = x[i] - m;
-      s += __builtin_amdgcn_exp2f(fmaf(t, chi, t * clo));
-    }
+    for (int i = 0; i < 16; ++i) s += __builtin_amdgcn_exp2f(fmaf(x[i], c, -mh));
+    s *= __builtin_amdgcn_exp2f(-ml);
   }
   s = RED == 0 ? sum4lanes(s) : row16_sum(s);
   return make_float2(m, s);
 }
+
+// floor(i / d) for 0 <= i < 2^22 and 1 <= d <= 64, from hd = 0.5f / d: (2i + 1) / (2d)
+// lies at least 1/(2d) from an integer and the two fp32 roundings move it by less.
+__device__ __forceinline__ int div_small(int i, float hd) { return (int)((float)(2 * i + 1) * hd); }
 
 // ---------------------------------------------------------------------------
 // pack: W1 tiles in MFMA lane order.  Tile c, k-step kk, lane l holds
@@ -260,25 +268,23 @@ __device__ __forceinline__ void markov_mma(const bf16x8 (&A)[4][KS], const bf16x
     for (int i = 0; i < 4; ++i) bias[4 * s + i] = acc[s][i];
 }
 
-// Per-stream constants of a pass in LDS: (chi, clo) of 1/T and gamma_b.
+// Per-stream constants of a pass in LDS: c = log2(e)/T (fp32) and gamma_b.
 __host__ __device__ __forceinline__ size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
 __host__ __device__ __forceinline__ size_t stream_table_bytes(int B) {
-  return align16((size_t)B * sizeof(float2)) + align16((size_t)B * sizeof(int));
+  return align16((size_t)B * sizeof(float)) + align16((size_t)B * sizeof(int));
 }
 
 struct StreamTable {
-  const float2* tc;
+  const float* tc;
   const int* gam;
 };
 
 __device__ __forceinline__ StreamTable build_stream_table(const Args& a, char* smem) {
-  float2* tc = reinterpret_cast<float2*>(smem);
-  int* gam = reinterpret_cast<int*>(smem + align16((size_t)a.B * sizeof(float2)));
+  float* tc = reinterpret_cast<float*>(smem);
+  int* gam = reinterpret_cast<int*>(smem + align16((size_t)a.B * sizeof(float)));
   for (int b = threadIdx.x; b < a.B; b += kThreads) {
-    float chi, clo;
-    temp_split(stream_temp(a, b), chi, clo);
-    tc[b] = make_float2(chi, clo);
+    tc[b] = (float)(kLog2e / (double)stream_temp(a, b));
     gam[b] = stream_gamma(a, b);
   }
   __syncthreads();
@@ -294,18 +300,15 @@ __device__ __forceinline__ StreamTable build_stream_table(const Args& a, char* s
 // barrier pair turns them into group partials.
 constexpr int kFlush = 16;   // chunks per LDS flush (256 rows, one per thread)
 
-__device__ __forceinline__ float2 combine_waves(const float2 (&p)[kWaves], float chi, float clo) {
+__device__ __forceinline__ float2 combine_waves(const float2 (&p)[kWaves], float c) {
   float M = p[0].x;
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) M = fmaxf(M, p[w].x);
   float S = 0.f;
   if (M != -INFINITY) {
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      if (p[w].x == -INFINITY) continue;
-      const float t = p[w].x - M;
-      S += p[w].y * __builtin_amdgcn_exp2f(fmaf(t, chi, t * clo));
-    }
+    for (int w = 0; w < kWaves; ++w)
+      if (p[w].x != -INFINITY) S += p[w].y * __builtin_amdgcn_exp2f((p[w].x - M) * c);
   }
   return make_float2(M, S);
 }
@@ -324,8 +327,9 @@ __device__ __forceinline__ void pass1_draft(const Args& a, const StreamTable& st
   const int nch = (ND + kChunk - 1) / kChunk;
   const size_t rb = (size_t)a.V * (DT == kBF16 ? 2 : 4);
   const char* base = reinterpret_cast<const char*>(a.draft);
+  const float hk = 0.5f / (float)a.k;
   auto row_of_dr = [&](int dr, int& b) {   // false if draft row dr is past the batch or inactive
-    b = dr / a.k;
+    b = div_small(dr, hk);
     return dr < ND && dr - b * a.k < st.gam[b < a.B ? b : a.B - 1];
   };
   auto row_of = [&](int c, int& b) { return row_of_dr(c * kChunk + n, b); };
@@ -362,8 +366,7 @@ __device__ __forceinline__ void pass1_draft(const Args& a, const StreamTable& st
       for (int e = 0; e < 16; ++e) x[e] += bias[e];
     }
     if (rag) mask_shift(x, shift);
-    const float2 tc = act ? st.tc[b] : make_float2(0.f, 0.f);
-    const float2 pw = row_partial<0>(x, tc.x, tc.y);
+    const float2 pw = row_partial<0>(x, act ? st.tc[b] : 0.f);
     if (q == 0) part[(c % kFlush) * kChunk + n][w] = pw;
     if (c % kFlush == kFlush - 1 || c == nch - 1) {   // uniform: every wave runs the same chunks
       __syncthreads();
@@ -373,7 +376,7 @@ __device__ __forceinline__ void pass1_draft(const Args& a, const StreamTable& st
         float2 p[kWaves];
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) p[ww] = part[tid][ww];
-        a.ws.dpart[(size_t)g * ND + dr] = combine_waves(p, st.tc[bb].x, st.tc[bb].y);
+        a.ws.dpart[(size_t)g * ND + dr] = combine_waves(p, st.tc[bb]);
       }
       __syncthreads();
     }
@@ -406,8 +409,9 @@ __device__ __forceinline__ void pass1_target(const Args& a, const StreamTable& s
   const int NT = a.B * k1;
   const size_t rb = (size_t)a.V * (DT == kBF16 ? 2 : 4);
   const char* base = reinterpret_cast<const char*>(a.target);
+  const float hk1 = 0.5f / (float)k1;
   auto row_ok = [&](int tr, int& b) {
-    b = tr / k1;
+    b = div_small(tr, hk1);
     return tr < NT && tr - b * k1 <= st.gam[b < a.B ? b : a.B - 1];
   };
   auto load_batch = [&](int r0, Raw16<DT>(&raw)[U]) {   // unconditional, as in the draft phase
@@ -428,8 +432,7 @@ __device__ __forceinline__ void pass1_target(const Args& a, const StreamTable& s
       float x[16];
       raw_to_f32<DT>(raw[u], x);
       if (rag) mask_shift(x, shift);
-      const float2 tc = act ? st.tc[b] : make_float2(0.f, 0.f);
-      const float2 pw = row_partial<1>(x, tc.x, tc.y);
+      const float2 pw = row_partial<1>(x, act ? st.tc[b] : 0.f);
       if (l16 == 0 && act) a.ws.tpart[(size_t)g * NT + tr] = pw;
     }
   };
