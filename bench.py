@@ -29,6 +29,23 @@ METRIC = "verified draft blocks/s (B x k x V) and achieved HBM GB/s at B=64,k=5,
 HBM_PEAK_GBS = 8000.0
 STAGE_NAMES = ["pack W1 tiles", "pass1 row statistics", "scan", "pass2 residual masses", "finalize/sampler"]
 
+# HBM traffic of one pass-1 launch at this workload, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE; profiles/pass1_headline_b64_k5_v129280_hbm_bytes.md):
+# FETCH_SIZE scaled by 2.0 (a 256 MiB device copy reads as 128 MiB), WRITE_SIZE by 1.0.
+# Valid only for the kernel sources it was measured on (hash below); otherwise null.
+PASS1_TRAFFIC = {"src_sha256_16": "f1ecdcc461efd12d", "fetch_bytes": 122052.9 * 1024 * 2.0,
+                 "write_bytes": 2807.7 * 1024 * 1.0}
+
+
+def kernel_src_hash() -> str:
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "common.hpp"):
+        with open(os.path.join(here, "draft_block_verification_row_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -86,8 +103,8 @@ def main() -> int:
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (streams shard with no "
-              "collective; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the verify path has no multi-GPU launcher (streams shard "
+              "across GPUs with no collective). Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import torch
@@ -205,7 +222,8 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": (round(PASS1_TRAFFIC["fetch_bytes"] + PASS1_TRAFFIC["write_bytes"])
+                        if kernel_src_hash() == PASS1_TRAFFIC["src_sha256_16"] else None),
             "kernel": "pass1_kernel (row statistics + fused Markov MFMA)",
             "kernel_ms": round(t_pass1, 5),
             "alg_bytes_per_launch": int(alg_pass1),

@@ -97,17 +97,22 @@ __device__ __forceinline__ float load1(const void* __restrict__ row, int c) {
 }
 
 // ---------------------------------------------------------------------------
-// Cross-lane reductions inside the 4 lanes {n, n+16, n+32, n+48} of a wave.
+// Cross-lane reductions inside the 4 lanes {n, n+16, n+32, n+48} of a wave, on
+// the gfx950 row swaps (VALU, no LDS round trip).  permlane16_swap(v, v) returns
+// rows (0,0,2,2) and (1,1,3,3) of v, permlane32_swap(v, v) halves (lo,lo) and
+// (hi,hi); combining the two results gives every lane the same value.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float max4lanes(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float sum4lanes(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // One row of the residual pass, prepared by the scan: the target/draft rows, the

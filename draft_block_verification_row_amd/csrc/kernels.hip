@@ -252,12 +252,13 @@ __device__ __forceinline__ void load_btile(const Args& a, int c, int l, bf16x8 (
   for (int kk = 0; kk < KS; ++kk) B[kk] = __builtin_bit_cast(bf16x8, t[kk * 64]);
 }
 
-// Bias of the lane's row at its 16 columns: A = this wave's W2 slab, B = a packed tile.
+// x + bias at the lane's row and 16 columns: A = this wave's W2 slab, B = a packed
+// tile; the accumulator starts from x (the logits), so the add is free.
 template <int KS>
-__device__ __forceinline__ void markov_mma(const bf16x8 (&A)[4][KS], const bf16x8 (&B)[KS], float (&bias)[16]) {
+__device__ __forceinline__ void markov_mma(const bf16x8 (&A)[4][KS], const bf16x8 (&B)[KS], float (&x)[16]) {
   f32x4 acc[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < 4; ++s) acc[s] = f32x4{x[4 * s], x[4 * s + 1], x[4 * s + 2], x[4 * s + 3]};
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
@@ -265,7 +266,7 @@ __device__ __forceinline__ void markov_mma(const bf16x8 (&A)[4][KS], const bf16x
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bias[4 * s + i] = acc[s][i];
+    for (int i = 0; i < 4; ++i) x[4 * s + i] = acc[s][i];
 }
 
 // Per-stream constants of a pass in LDS: c = log2(e)/T (fp32) and gamma_b.
@@ -351,20 +352,15 @@ __device__ __forceinline__ void pass1_draft(const Args& a, const StreamTable& st
   // one chunk: MFMA on the current tile, next tile in flight, reduce the logits in
   // `xb`, then refill `xb` with the chunk PD ahead
   auto chunk = [&](int c, Raw16<DT>& xb) {
-    float bias[16];
-    if (MARKOV) {
-      markov_mma<KS>(A, Bc, bias);
-      load_btile<KS>(a, min(c + 1, nch - 1), l, Bc);
-    }
     float x[16];
     raw_to_f32<DT>(xb, x);
     load_x(c + PD, xb);
+    if (MARKOV) {
+      markov_mma<KS>(A, Bc, x);   // x += bias
+      load_btile<KS>(a, min(c + 1, nch - 1), l, Bc);
+    }
     int b;
     const bool act = row_of(c, b);
-    if (MARKOV) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) x[e] += bias[e];
-    }
     if (rag) mask_shift(x, shift);
     const float2 pw = row_partial<0>(x, act ? st.tc[b] : 0.f);
     if (q == 0) part[(c % kFlush) * kChunk + n][w] = pw;
@@ -381,16 +377,17 @@ __device__ __forceinline__ void pass1_draft(const Args& a, const StreamTable& st
       __syncthreads();
     }
   };
-  static_assert(PD == 2, "the chunk loop below is written for two logits buffers");
-  Raw16<DT> x0, x1;
-  load_x(0, x0);
-  load_x(1, x1);
+  Raw16<DT> xb[PD];   // ring of logits buffers, indexed at compile time
+#pragma unroll
+  for (int i = 0; i < PD; ++i) load_x(i, xb[i]);
   int c = 0;
-  for (; c + 2 <= nch; c += 2) {
-    chunk(c, x0);
-    chunk(c + 1, x1);
+  for (; c + PD <= nch; c += PD) {
+#pragma unroll
+    for (int i = 0; i < PD; ++i) chunk(c + i, xb[i]);
   }
-  if (c < nch) chunk(c, x0);
+#pragma unroll
+  for (int i = 0; i < PD; ++i)
+    if (c + i < nch) chunk(c + i, xb[i]);
 }
 
 // Target rows: a 16-lane DPP row covers the group's 256 ids of one row; the
@@ -692,8 +689,11 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
   Raw16<DT> tb, db;
   fetch(0, tb, db);
   for (int c = 0; c < nch; ++c) {
-    float bias[16];
+    float bias[16];   // the bias alone (not folded into the draft logits: the residual
+                      // compares P p with q and keeps their rounding apart)
     if (MARKOV) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) bias[e] = 0.f;
       markov_mma<KS>(A, Bc, bias);
       load_btile<KS>(a, min(c + 1, nch - 1), l, Bc);
     }
@@ -838,24 +838,34 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
   const int dr = b * a.k + (s < gamma ? s : 0);
 
   // group masses of the sampled row: the residual (pass 2) or, for the bonus row
-  // and an all-zero residual, the target's own partials
-  bool use_p = (s == gamma);
-  if (!use_p) {
-    double v = 0.0;
-    for (int gi = tid; gi < NG; gi += kThreads) v += (double)a.ws.wgrp[(size_t)gi * ND + dr];
-    if (!(block_sum(v, red) > 0.0)) use_p = true;
-  }
+  // and an all-zero residual, the target's own partials.  A thread's first two
+  // groups load both kinds at once; groups past 512 (V > 131072) are re-read.
   const double Mt = (double)a.ws.tm[tr];
+  const bool resid = s < gamma;
+  auto target_mass = [&](float2 p) {
+    return p.x == -INFINITY ? 0.0 : (double)p.y * exp2(((double)p.x - Mt) * c);
+  };
+  float Wr[2];
+  float2 Tp[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {   // unconditional loads (clamped group), masked after
+    const int gi = tid + kThreads * t;
+    const int gc = gi < NG ? gi : NG - 1;
+    Wr[t] = a.ws.wgrp[(size_t)gc * ND + dr];
+    Tp[t] = a.ws.tpart[(size_t)gc * NT + tr];
+    if (gi >= NG || !resid) Wr[t] = 0.f;
+    if (gi >= NG) Tp[t] = make_float2(-INFINITY, 0.f);
+  }
+  double rsum = (double)Wr[0] + (double)Wr[1];
+  if (resid)
+    for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) rsum += (double)a.ws.wgrp[(size_t)gi * ND + dr];
+  const bool use_p = !resid || !(block_sum(rsum, red) > 0.0);
   double best = -1.0;
   int gbest = 0x7fffffff;
   for (int gi = tid, t = 0; gi < NG; gi += kThreads, ++t) {
     double W;
-    if (use_p) {
-      const float2 p = a.ws.tpart[(size_t)gi * NT + tr];
-      W = p.x == -INFINITY ? 0.0 : (double)p.y * exp2(((double)p.x - Mt) * c);
-    } else {
-      W = (double)a.ws.wgrp[(size_t)gi * ND + dr];
-    }
+    if (t < 2) W = use_p ? target_mass(Tp[t < 2 ? t : 0]) : (double)Wr[t < 2 ? t : 0];
+    else W = use_p ? target_mass(a.ws.tpart[(size_t)gi * NT + tr]) : (double)a.ws.wgrp[(size_t)gi * ND + dr];
     if (W > 0.0) {
       const double E = t < 2 ? Eg[t < 2 ? t : 0]
                              : race_clock(a.key0, a.key1, (uint32_t)b, (uint32_t)gi, kPurposeRaceGroup, a.step);
@@ -957,60 +967,37 @@ __global__ __launch_bounds__(kThreads) void markov_bias_kernel(BiasArgs ba) {
 }
 
 // ---------------------------------------------------------------------------
-// Confidence head + adaptive count.  One workgroup per stream: each thread owns
-// 16 hidden features of every slot, so all of a stream's loads are in flight at once.
+// Confidence head + adaptive count.  One workgroup per stream, one wave per slot:
+// the wave's lanes take 8 consecutive hidden features each, 512 per step, and the
+// dot product accumulates in fp64.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void adaptive_kernel(AdaptArgs aa) {
-  __shared__ double red[kWaves][kMaxK];
   __shared__ double s_c[kMaxK];
   const int b = blockIdx.x;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  double z[kMaxK];
+  for (int j = w; j < aa.k; j += kWaves) {
+    const uint16_t* h = aa.hidden + ((size_t)b * aa.k + j) * aa.H;
+    double acc = 0.0;
+    if (aa.vec_ok) {   // H % 8 == 0 and 16-byte aligned rows
+#pragma unroll 4
+      for (int c0 = 8 * l; c0 < aa.H; c0 += 512) {
+        const uint4 hv = *reinterpret_cast<const uint4*>(h + c0);
+        const uint4 wv = *reinterpret_cast<const uint4*>(aa.w + c0);
+        const uint32_t hh[4] = {hv.x, hv.y, hv.z, hv.w};
+        const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) z[j] = 0.0;
-  for (int c0 = 16 * tid; c0 < aa.H; c0 += 16 * kThreads) {
-    float wv[16];
-    if (aa.vec_ok && c0 + 16 <= aa.H) {
-      const uint4 u0 = *reinterpret_cast<const uint4*>(aa.w + c0), u1 = *reinterpret_cast<const uint4*>(aa.w + c0 + 8);
-      const uint32_t ww[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) { wv[2 * i] = bf16lo(ww[i]); wv[2 * i + 1] = bf16hi(ww[i]); }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) wv[i] = (c0 + i < aa.H) ? bf16_to_f32(aa.w[c0 + i]) : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j >= aa.k) break;
-      const uint16_t* h = aa.hidden + ((size_t)b * aa.k + j) * aa.H;
-      float hv[16];
-      if (aa.vec_ok && c0 + 16 <= aa.H) {
-        const uint4 u0 = *reinterpret_cast<const uint4*>(h + c0), u1 = *reinterpret_cast<const uint4*>(h + c0 + 8);
-        const uint32_t hh[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) { hv[2 * i] = bf16lo(hh[i]); hv[2 * i + 1] = bf16hi(hh[i]); }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) hv[i] = (c0 + i < aa.H) ? bf16_to_f32(h[c0 + i]) : 0.f;
+        for (int i = 0; i < 4; ++i)
+          acc += (double)bf16lo(hh[i]) * (double)bf16lo(ww[i]) + (double)bf16hi(hh[i]) * (double)bf16hi(ww[i]);
       }
-      double acc = 0.0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc += (double)hv[i] * (double)wv[i];
-      z[j] += acc;
+    } else {
+      for (int c = l; c < aa.H; c += 64) acc += (double)bf16_to_f32(h[c]) * (double)bf16_to_f32(aa.w[c]);
     }
-  }
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (j >= aa.k) break;
-    const double v = wave_sum(z[j]);
-    if (l == 0) red[w][j] = v;
-  }
-  __syncthreads();
-  if (tid < aa.k) {
-    const double zz = ((red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid])) + (double)aa.bias;
-    const double cj = 1.0 / (1.0 + exp(-zz));
-    s_c[tid] = cj;
-    if (aa.c_out) aa.c_out[b * aa.k + tid] = (float)cj;
+    acc = wave_sum(acc);
+    if (l == 0) {
+      const double cj = 1.0 / (1.0 + exp(-(acc + (double)aa.bias)));
+      s_c[j] = cj;
+      if (aa.c_out) aa.c_out[b * aa.k + j] = (float)cj;
+    }
   }
   __syncthreads();
   if (tid == 0) {
