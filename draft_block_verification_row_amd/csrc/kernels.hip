@@ -314,10 +314,50 @@ __device__ __forceinline__ float2 combine_waves(const float2 (&p)[kWaves], float
   return make_float2(M, S);
 }
 
+// W1 tiles reach the B operand through LDS: the workgroup copies kStage tiles at a
+// time from `btile` (thread t moves 16-byte units t, t + 256, ...), two blocks in
+// LDS, the next block's loads in flight while the current one is used.  A wave then
+// reads a k-step of a tile with one conflict-free ds_read_b128 per lane.
+constexpr int kStage = 4;   // tiles (chunks) per staged block
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // a native vector: stays in registers
+
+template <int KS>
+struct TileStage {
+  static constexpr int kUnits = kStage * KS * 64;   // 16-byte units per block
+  static constexpr int kPer = kUnits / kThreads;    // units per thread (= KS)
+  u32x4 v[kPer];
+};
+
+template <int KS>
+__device__ __forceinline__ void tile_stage_load(const Args& a, int blk, int nch, TileStage<KS>& t) {
+  const u32x4* src = reinterpret_cast<const u32x4*>(a.ws.btile);
+#pragma unroll
+  for (int i = 0; i < TileStage<KS>::kPer; ++i) {
+    const int u = threadIdx.x + kThreads * i;
+    const int tile = min(blk * kStage + u / (KS * 64), nch - 1);
+    t.v[i] = src[(size_t)tile * KS * 64 + u % (KS * 64)];
+  }
+}
+
+template <int KS>
+__device__ __forceinline__ void tile_stage_store(const TileStage<KS>& t, uint4* dst) {
+  u32x4* d = reinterpret_cast<u32x4*>(dst);
+#pragma unroll
+  for (int i = 0; i < TileStage<KS>::kPer; ++i) d[threadIdx.x + kThreads * i] = t.v[i];
+}
+
+// Draft rows, 16 per chunk, in blocks of kStage chunks: the logits of the next PD
+// chunks are in flight while the current chunk goes through the MFMA (B operand from
+// LDS) and the reduction.  The 4 wave partials of a row (64 ids each) meet in LDS and
+// every 16 chunks one barrier pair turns them into group partials.  Chunks past the
+// batch (at most kStage - 1) run with clamped loads and write nothing.
 template <int DT, int KS, bool MARKOV, bool VEC>
 __device__ __forceinline__ void pass1_draft(const Args& a, const StreamTable& st, int g,
-                                            float2 (*part)[kWaves]) {
+                                            float2 (*part)[kWaves], uint4* bst) {
   constexpr int PD = 2;   // logits prefetch distance (chunks)
+  static_assert(kStage % PD == 0 && kFlush % kStage == 0, "block, ring and flush sizes must nest");
+  static_assert(TileStage<KS>::kUnits % kThreads == 0, "a staged block must split evenly");
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, q = l >> 4;
   const int cb = g * kGroup + w * kWaveCols;
   const int cw = cb + 16 * q;                                // this lane's 16-column window
@@ -326,6 +366,7 @@ __device__ __forceinline__ void pass1_draft(const Args& a, const StreamTable& st
   const bool rag = VEC && cb + kWaveCols > a.V;              // wave-uniform
   const int ND = a.B * a.k;
   const int nch = (ND + kChunk - 1) / kChunk;
+  const int nblk = (nch + kStage - 1) / kStage;
   const size_t rb = (size_t)a.V * (DT == kBF16 ? 2 : 4);
   const char* base = reinterpret_cast<const char*>(a.draft);
   const float hk = 0.5f / (float)a.k;
@@ -344,20 +385,22 @@ __device__ __forceinline__ void pass1_draft(const Args& a, const StreamTable& st
   };
 
   bf16x8 A[4][KS];
-  bf16x8 Bc[KS];
+  TileStage<KS> stage;
   if (MARKOV) {
     load_w2_slab<KS, VEC>(a, cb, n, q, A);
-    load_btile<KS>(a, 0, l, Bc);
+    tile_stage_load<KS>(a, 0, nch, stage);
+    tile_stage_store<KS>(stage, bst);
+    tile_stage_load<KS>(a, 1, nch, stage);
   }
-  // one chunk: MFMA on the current tile, next tile in flight, reduce the logits in
-  // `xb`, then refill `xb` with the chunk PD ahead
-  auto chunk = [&](int c, Raw16<DT>& xb) {
+  auto chunk = [&](int c, const uint4* tiles, Raw16<DT>& xb) {
     float x[16];
     raw_to_f32<DT>(xb, x);
     load_x(c + PD, xb);
     if (MARKOV) {
-      markov_mma<KS>(A, Bc, x);   // x += bias
-      load_btile<KS>(a, min(c + 1, nch - 1), l, Bc);
+      bf16x8 Bop[KS];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) Bop[kk] = __builtin_bit_cast(bf16x8, tiles[kk * 64 + l]);
+      markov_mma<KS>(A, Bop, x);   // x += bias
     }
     int b;
     const bool act = row_of(c, b);
@@ -380,14 +423,17 @@ __device__ __forceinline__ void pass1_draft(const Args& a, const StreamTable& st
   Raw16<DT> xb[PD];   // ring of logits buffers, indexed at compile time
 #pragma unroll
   for (int i = 0; i < PD; ++i) load_x(i, xb[i]);
-  int c = 0;
-  for (; c + PD <= nch; c += PD) {
+  __syncthreads();   // block 0 of the tiles is in LDS
+  for (int j = 0; j < nblk; ++j) {
+    const uint4* tiles = bst + (j & 1) * TileStage<KS>::kUnits;
 #pragma unroll
-    for (int i = 0; i < PD; ++i) chunk(c + i, xb[i]);
+    for (int cc = 0; cc < kStage; ++cc) chunk(j * kStage + cc, tiles + cc * KS * 64, xb[cc % PD]);
+    if (MARKOV) {
+      tile_stage_store<KS>(stage, bst + ((j + 1) & 1) * TileStage<KS>::kUnits);
+      tile_stage_load<KS>(a, j + 2, nch, stage);
+    }
+    __syncthreads();   // block j + 1 is in LDS; nobody reads block j any more
   }
-#pragma unroll
-  for (int i = 0; i < PD; ++i)
-    if (c + i < nch) chunk(c + i, xb[i]);
 }
 
 // Target rows: a 16-lane DPP row covers the group's 256 ids of one row; the
@@ -449,14 +495,15 @@ template <int DT, int KS, bool MARKOV, bool VEC>
 __global__ __launch_bounds__(kThreads, 2) void pass1_kernel(Args a) {
   extern __shared__ char smem[];
   __shared__ float2 part[kFlush * kChunk][kWaves];
+  __shared__ uint4 bst[MARKOV ? 2 * TileStage<KS>::kUnits : 1];   // 64 KB at R = 256
   const StreamTable st = build_stream_table(a, smem);
   const int g = blockIdx.x;
   // alternate the phase order so that MFMA-heavy and streaming phases overlap across the chip
   if (g & 1) {
     pass1_target<DT, VEC>(a, st, g);
-    pass1_draft<DT, KS, MARKOV, VEC>(a, st, g, part);
+    pass1_draft<DT, KS, MARKOV, VEC>(a, st, g, part, bst);
   } else {
-    pass1_draft<DT, KS, MARKOV, VEC>(a, st, g, part);
+    pass1_draft<DT, KS, MARKOV, VEC>(a, st, g, part, bst);
     pass1_target<DT, VEC>(a, st, g);
   }
 }
