@@ -705,8 +705,6 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
 template <int DT, int KS, bool MARKOV, bool VEC>
 __global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
   __shared__ float part[kFlush * kChunk][kWaves];
-  const int NI = *a.ws.nitems;
-  if (NI == 0) return;
   const int g = blockIdx.x;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, q = l >> 4;
   const int cb = (g * kWaves + w) * kWaveCols;
@@ -715,27 +713,34 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
   const int shift = VEC ? (cw >= a.V ? 16 : cw - c0) : 0;
   const bool rag = VEC && cb + kWaveCols > a.V;
   const size_t rb = (size_t)a.V * (DT == kBF16 ? 2 : 4);
-  const int nch = (NI + kChunk - 1) / kChunk;
   const int ND = a.B * a.k;
 
+  // the W2 slab does not depend on the list: its loads go out before the count is read
   bf16x8 A[4][KS];
+  if (MARKOV) load_w2_slab<KS, VEC>(a, cb, n, q, A);
+  const int NI = *a.ws.nitems;
+  if (NI == 0) return;
+  const int nch = (NI + kChunk - 1) / kChunk;
   bf16x8 Bc[KS];
-  if (MARKOV) {
-    load_w2_slab<KS, VEC>(a, cb, n, q, A);
-    load_btile<KS>(a, 0, l, Bc);
-  }
+  if (MARKOV) load_btile<KS>(a, 0, l, Bc);
+  // Item of this lane's row in chunk c (clamped: chunks past the list re-read the last item)
   auto item_at = [&](int c) {
-    const int it = c * kChunk + n;
+    const int it = min(c, nch - 1) * kChunk + n;
     return it < NI ? it : NI - 1;
   };
-  auto fetch = [&](int c, Raw16<DT>& t, Raw16<DT>& d) {   // unconditional: past the end re-reads the last item
-    const int2 h = *reinterpret_cast<const int2*>(&a.ws.items[item_at(min(c, nch - 1))].dr);   // (dr, tr)
+  auto rows_of = [&](int c) { return *reinterpret_cast<const int2*>(&a.ws.items[item_at(c)].dr); };   // (dr, tr)
+  auto fetch = [&](int2 h, Raw16<DT>& t, Raw16<DT>& d) {
     raw_load<DT, VEC>(t, reinterpret_cast<const char*>(a.target) + (size_t)h.y * rb, c0, a.V);
     raw_load<DT, VEC>(d, reinterpret_cast<const char*>(a.draft) + (size_t)h.x * rb, c0, a.V);
   };
+  // pipeline: row indices two chunks ahead, logits one chunk ahead
   Raw16<DT> tb, db;
-  fetch(0, tb, db);
+  fetch(rows_of(0), tb, db);
+  int2 hn = rows_of(1);
   for (int c = 0; c < nch; ++c) {
+    const int2 hnn = rows_of(c + 2);
+    const float4* kc = reinterpret_cast<const float4*>(&a.ws.items[item_at(c)].Mt);
+    const float4 k0 = kc[0], k1 = kc[1];   // (Mt, Md, chi, clo), (kph, kpl, kqh, kql)
     float bias[16];   // the bias alone (not folded into the draft logits: the residual
                       // compares P p with q and keeps their rounding apart)
     if (MARKOV) {
@@ -744,12 +749,11 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
       markov_mma<KS>(A, Bc, bias);
       load_btile<KS>(a, min(c + 1, nch - 1), l, Bc);
     }
-    const float4* kc = reinterpret_cast<const float4*>(&a.ws.items[item_at(c)].Mt);
-    const float4 k0 = kc[0], k1 = kc[1];   // (Mt, Md, chi, clo), (kph, kpl, kqh, kql)
     float xt[16], xd[16];
     raw_to_f32<DT>(tb, xt);
     raw_to_f32<DT>(db, xd);
-    fetch(c + 1, tb, db);
+    fetch(hn, tb, db);
+    hn = hnn;
     if (rag) mask_shift(xt, shift);
     float s = 0.f;
 #pragma unroll
