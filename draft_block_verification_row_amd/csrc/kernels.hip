@@ -285,7 +285,9 @@ __device__ __forceinline__ StreamTable build_stream_table(const Args& a, char* s
   float* tc = reinterpret_cast<float*>(smem);
   int* gam = reinterpret_cast<int*>(smem + align16((size_t)a.B * sizeof(float)));
   for (int b = threadIdx.x; b < a.B; b += kThreads) {
-    tc[b] = (float)(kLog2e / (double)stream_temp(a, b));
+    const float T = stream_temp(a, b);
+    // T = 0 (greedy) only needs the row maxima: any finite positive c keeps the sums finite
+    tc[b] = T > 0.f ? (float)(kLog2e / (double)T) : 1e-30f;
     gam[b] = stream_gamma(a, b);
   }
   __syncthreads();
@@ -542,6 +544,56 @@ __device__ __forceinline__ void row_norm(const float2* __restrict__ part, int ro
   l2s_out = log2(S);
 }
 
+// Temperature 0 [P1 §4 "Greedy is a different code path"]: a draft is kept iff it is
+// the target's argmax at its slot (first id among equal maxima); the first mismatch
+// stops the block and the target's argmax there is emitted (the bonus position's when
+// every draft is kept).  The argmax of a target row comes from its group maxima (raw
+// logits, exact): the first group that reaches the row maximum, then the first id of
+// that group holding it.  No residual pass and no sampler are involved.
+template <int DT>
+__device__ __forceinline__ void greedy_scan(const Args& a, int b, int gamma) {
+  __shared__ int s_am[kMaxK + 1];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int k1 = a.k + 1, NT = a.B * k1, NG = a.NG;
+  const size_t rb = (size_t)a.V * (DT == kBF16 ? 2 : 4);
+  for (int r = w; r <= gamma; r += kWaves) {   // one wave per target row
+    const int row = b * k1 + r;
+    float M = -INFINITY;
+    for (int g = l; g < NG; g += 64) M = fmaxf(M, a.ws.tpart[(size_t)g * NT + row].x);
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    int gs = 0x7fffffff;
+    for (int g = l; g < NG; g += 64)
+      if (a.ws.tpart[(size_t)g * NT + row].x == M) gs = min(gs, g);
+    for (int off = 32; off >= 1; off >>= 1) gs = min(gs, __shfl_xor(gs, off));
+    gs = gs < NG ? gs : 0;
+    int vs = 0x7fffffff;
+    const char* rowp = reinterpret_cast<const char*>(a.target) + (size_t)row * rb;
+#pragma unroll
+    for (int i = 0; i < kGroup / 64; ++i) {
+      const int v = gs * kGroup + (kGroup / 64) * l + i;
+      if (v < a.V && load1<DT>(rowp, v) == M) vs = min(vs, v);
+    }
+    for (int off = 32; off >= 1; off >>= 1) vs = min(vs, __shfl_xor(vs, off));
+    if (l == 0) s_am[r] = vs < a.V ? vs : gs * kGroup;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int t = gamma;
+    for (int j = 0; j < gamma; ++j)
+      if (s_am[j] != a.tokens[b * a.k + j]) { t = j; break; }
+    a.ws.info[4 * b + 0] = gamma;
+    a.ws.info[4 * b + 1] = t;      // the stop: no residual mass is needed
+    a.ws.info[4 * b + 2] = 0;
+    a.ws.info[4 * b + 3] = s_am[t];   // the emitted token
+    a.ws.rowmask[b] = 0u;
+  }
+  if (tid <= gamma) a.ws.logP[b * k1 + tid] = NAN;
+  if (tid < gamma) {
+    a.ws.lpx[b * a.k + tid] = NAN;
+    a.ws.lqx[b * a.k + tid] = NAN;
+  }
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
   __shared__ float s_M[2 * kMaxK + 1];
@@ -552,7 +604,12 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int gamma = stream_gamma(a, b);
-  const double T = (double)stream_temp(a, b);
+  const float Tf = stream_temp(a, b);
+  if (Tf == 0.f) {   // the whole workgroup takes the greedy branch
+    greedy_scan<DT>(a, b, gamma);
+    return;
+  }
+  const double T = (double)Tf;
   const double c = kLog2e / T;
   const int k1 = a.k + 1;
   const int NT = a.B * k1, ND = a.B * a.k;
@@ -844,7 +901,20 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
   const int gamma = info.x, f = info.z;
   int stop = info.y;
   const uint32_t mask = a.ws.rowmask[b];
-  const double T = (double)stream_temp(a, b);
+  const float Tf = stream_temp(a, b);
+  if (Tf == 0.f) {   // greedy: the scan decided the stop and the token
+    if (tid <= a.k) {
+      const int s = stop;
+      a.out_tokens[b * k1 + tid] = tid < s ? a.tokens[b * a.k + tid] : (tid == s ? info.w : -1);
+      if (a.diag != nullptr) {
+        double* dg = a.diag + ((size_t)b * k1 + tid) * 5;
+        for (int e = 0; e < 5; ++e) dg[e] = NAN;
+      }
+    }
+    if (tid == 0) a.accepted_len[b] = stop;
+    return;
+  }
+  const double T = (double)Tf;
   const double c = kLog2e / T;
   const size_t esz = DT == kBF16 ? 2 : 4;
 

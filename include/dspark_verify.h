@@ -20,7 +20,7 @@
  *     (a hipStream_t; NULL means the default stream) and completes in order.
  *   - Host-checkable errors return a status and enqueue nothing.  A failed
  *     launch returns DSPARK_ERR_HIP.  Device-data preconditions (token ids in
- *     range, temperatures > 0, num_drafts in [0, k]) are the caller's: the
+ *     range, temperatures >= 0, num_drafts in [0, k]) are the caller's: the
  *     kernels clamp indices so that no access leaves its buffer, but outputs for
  *     invalid data are unspecified.
  *   - Same inputs, seed and step give bit-identical outputs on every run: no
@@ -74,8 +74,10 @@ typedef struct {
   const int32_t* draft_tokens;    /* device [B, k]: x_{b,j} in [0, V)                         */
   const int32_t* num_drafts;      /* device [B]: gamma_b in [0, k] (ragged verify: only rows
                                      0..gamma_b are read); NULL means gamma_b = k            */
-  const float* temperature;       /* device [B], > 0; NULL means 1.  Target logits and the
-                                     biased draft logits are both divided by T_b             */
+  const float* temperature;       /* device [B], >= 0; NULL means 1.  T_b > 0: target logits
+                                     and the biased draft logits are both divided by T_b.
+                                     T_b = 0: the greedy branch (both entry points), see
+                                     dspark_verify_tokenwise                                  */
   const uint16_t* W1;             /* device bf16 [V, R]: Markov factor rows, indexed by the
                                      previous token; NULL switches the bias off              */
   const uint16_t* W2t;            /* device bf16 [V, R]: W2t[v, r] = W2[r, v], the [R, V]
@@ -106,6 +108,12 @@ typedef struct {
 size_t dspark_workspace_bytes(const dspark_verify_problem* problem);
 
 /*
+ * Streams with temperature 0 take the greedy branch in both verify entry points
+ * [P1 §4 "Greedy is a different code path"]: draft j is kept iff it equals the
+ * argmax of target row j (the first id among equal maxima); the emitted token is the
+ * argmax at the first mismatch, or at the bonus position when every draft is kept.
+ * Their diag entries are NaN (no probabilities are formed).
+ *
  * Token-by-token verification (Leviathan et al.) [P1 §4 "Token by token"]:
  * draft j is kept iff u_{b,j} <= min(1, p_j(x_j) / q_j(x_j)); at the first
  * rejection t the emitted token is drawn from max(0, p_t - q_t) normalised, and

@@ -252,13 +252,32 @@ def verify_stream(tl: np.ndarray, dl: np.ndarray, x: np.ndarray, gamma: int, T: 
                 degenerate=degenerate, logr=logr, u=u)
 
 
+def greedy_stream(tl: np.ndarray, x: np.ndarray, gamma: int) -> dict:
+    """Temperature 0 [P1 §4 "Greedy is a different code path"]: a draft is kept iff it
+    equals the target's argmax at its slot; the first mismatch stops the block and the
+    emitted token is the target's argmax there (the bonus position's argmax when every
+    draft is kept).  READING: ties go to the lowest vocabulary id.  The decisions are
+    exact comparisons, so no margin applies; log-probabilities and the block quantities
+    are undefined at T = 0 (NaN in diag).
+    """
+    am = [int(np.argmax(tl[j])) for j in range(gamma + 1)]   # np.argmax: first of equal maxima
+    s = gamma
+    for j in range(gamma):
+        if am[j] != int(x[j]):
+            s = j
+            break
+    return dict(s=s, Y=am[s], diag=np.full((gamma + 1, 5), np.nan), margin_accept=np.inf,
+                margin_sample=np.inf, degenerate=False)
+
+
 def verify(target, draft, dtype: str, draft_tokens, temperature=None, anchor=None,
            W1=None, W2t=None, num_drafts=None, seed: int = 0, step: int = 0,
            method: str = "block", group: int = RACE_GROUP_SIZE) -> dict:
     """Both verifiers over B streams.
 
     target [B, k+1, V], draft [B, k, V] (fp32 or bf16 bits), draft_tokens [B, k],
-    temperature [B] (None = 1), anchor [B] (None = -1), num_drafts [B]
+    temperature [B] (None = 1; a stream with T = 0 takes the greedy branch whatever
+    the method, as the pages' sampler does), anchor [B] (None = -1), num_drafts [B]
     (None = k; READING: ragged gamma_b reads rows 0..gamma_b only).
     Returns accepted_len [B], out_tokens [B, k+1] (x_0..x_{s-1}, Y, then -1),
     diag [B, k+1, 5] = (log p(x_j), log q(x_j), P_j, R_j, h_j), and margins.
@@ -283,8 +302,11 @@ def verify(target, draft, dtype: str, draft_tokens, temperature=None, anchor=Non
         gamma = int(g_all[b])
         tl = widen(target[b, : gamma + 1], dtype)
         dl = widen(np.asarray(draft)[b, :gamma], dtype) if gamma > 0 else np.zeros((0, V))
-        r = verify_stream(tl, dl, x_all[b], gamma, float(T_all[b]), int(a_all[b]), W1, W2t,
-                          seed, b, step, method, group)
+        if T_all[b] == 0.0:
+            r = greedy_stream(tl, x_all[b], gamma)
+        else:
+            r = verify_stream(tl, dl, x_all[b], gamma, float(T_all[b]), int(a_all[b]), W1, W2t,
+                              seed, b, step, method, group)
         s = r["s"]
         acc[b] = s
         out[b, :s] = x_all[b, :s]

@@ -91,6 +91,10 @@ def compare(g, o, wl, method, tally: Tally, label=""):
         if g.get("diag") is None:
             continue
         dg, do = g["diag"][b], o["diag"][b]
+        if float(wl.temperature[b]) == 0.0:   # greedy branch: no probabilities on either side
+            if not (np.all(np.isnan(dg[: gamma + 1])) and np.all(np.isnan(do[: gamma + 1]))):
+                tally.unexplained.append((label, b, "greedy diag not NaN"))
+            continue
         for j in range(gamma):
             e1 = abs(dg[j, 0] - do[j, 0])
             e2 = abs(dg[j, 1] - do[j, 1])

@@ -320,3 +320,64 @@ def test_accept_uniform_threshold_ends():
     assert np.all(u <= 1.0) and np.all(u > 0.0)
     assert dspark.tokenwise_stop(np.zeros(3), u[:3])[0] == 3
     assert dspark.tokenwise_stop(np.full(3, -np.inf), u[:3])[0] == 0
+
+
+# ----------------------------------------------------------------------------
+# greedy branch, temperature 0 [P1 §4 "Greedy is a different code path"]
+# ----------------------------------------------------------------------------
+def _separated_rows(rng, rows, V, gap=4.0):
+    """Gaussian logits whose largest entry leads the second by at least `gap`."""
+    x = rng.standard_normal((rows, V))
+    top = np.argmax(x, axis=-1)
+    x[np.arange(rows), top] = np.max(np.delete(x, 0, axis=-1), axis=-1).clip(min=x.max()) + gap
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3, 4])
+def test_greedy_is_the_low_temperature_limit(seed):
+    """As T -> 0, p_j and q_j become one-hot at their argmax; with greedy drafts
+    (x_j = argmax q_j) both sampled verifiers then keep exactly the drafts that equal
+    the target argmax and emit the target argmax at the stop.  The T = 0 branch must
+    give the same lengths and tokens as both verifiers at T = 1e-3."""
+    rng = np.random.default_rng(100 + seed)
+    B, k, V = 6, 4, 40
+    target = np.stack([_separated_rows(rng, k + 1, V) for _ in range(B)])
+    draft = np.stack([_separated_rows(rng, k, V) for _ in range(B)])
+    # let some drafts agree with the target so that blocks are partly kept
+    for b in range(B):
+        for j in range(k):
+            if rng.random() < 0.6:
+                draft[b, j] = target[b, j]
+    x = np.argmax(draft, axis=-1).astype(np.int32)
+    g = dspark.verify(target, draft, "f32", x, temperature=np.zeros(B, np.float32), seed=seed, method="block")
+    for method in ("tokenwise", "block"):
+        r = dspark.verify(target, draft, "f32", x, temperature=np.full(B, 1e-3, np.float32), seed=seed,
+                          method=method)
+        assert np.array_equal(g["accepted_len"], r["accepted_len"]), method
+        assert np.array_equal(g["out_tokens"], r["out_tokens"]), method
+    assert 0 < int(np.sum(g["accepted_len"])) < B * k   # both kept and rejected drafts occur
+
+
+def test_greedy_ties_go_to_the_lowest_id():
+    V, k = 12, 2
+    target = np.zeros((1, k + 1, V), np.float32)
+    target[0, 0, [5, 9]] = 3.0        # two equal maxima: id 5 is the argmax
+    target[0, 1, 2] = 1.0
+    target[0, 2, [7, 8]] = 2.0
+    draft = np.zeros((1, k, V), np.float32)
+    zero = np.zeros(1, np.float32)
+    r = dspark.verify(target, draft, "f32", np.array([[9, 2]], np.int32), temperature=zero, method="tokenwise")
+    assert r["accepted_len"][0] == 0 and r["out_tokens"][0].tolist() == [5, -1, -1]
+    r = dspark.verify(target, draft, "f32", np.array([[5, 2]], np.int32), temperature=zero, method="block")
+    assert r["accepted_len"][0] == 2 and r["out_tokens"][0].tolist() == [5, 2, 7]
+
+
+def test_greedy_ignores_seed_step_and_method():
+    wl = workloads.make_zipf("g", 11, 6, 4, V=300, dtype="bf16", greedy_every=1)
+    outs = [dspark.verify(wl.target, wl.draft, wl.dtype, wl.draft_tokens, wl.temperature, wl.anchor, wl.W1,
+                          wl.W2t, seed=sd, step=st, method=m)
+            for sd, st, m in ((1, 0, "block"), (2, 5, "tokenwise"), (3, 9, "block"))]
+    for o in outs[1:]:
+        assert np.array_equal(o["accepted_len"], outs[0]["accepted_len"])
+        assert np.array_equal(o["out_tokens"], outs[0]["out_tokens"])
+    assert np.all(np.isnan(outs[0]["diag"]))

@@ -135,11 +135,14 @@ def make_tiny(seed: int = 1, B: int = 4, k: int = 3, V: int = 16, rho: float = 0
 def make_zipf(name: str, seed: int, B: int, k: int, V: int = V_FULL, dtype: str = "bf16",
               rho=(0.3, 0.95), temp=(0.6, 1.0), markov: bool = True, R: int = RANK,
               sigma: float = 3.0, zipf_s: float = 1.1, rho_per_slot=None,
-              confidence: bool = False, H: int = HIDDEN) -> Workload:
+              confidence: bool = False, H: int = HIDDEN, greedy_every: int = 0) -> Workload:
     """Zipf-biased Gaussian target logits with a correlated draft (c2..c5 recipes).
 
     ``rho`` / ``temp`` are a fixed value or a (lo, hi) range drawn per stream;
-    ``rho_per_slot`` (length k) overrides rho slot by slot.
+    ``rho_per_slot`` (length k) overrides rho slot by slot.  ``greedy_every`` = m > 0
+    sets T = 0 on every m-th stream (mixed batches); such a stream's drafts copy the
+    position of the target row's largest logit with probability 3/4 and of the draft
+    row's otherwise, so that greedy blocks are partly kept.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     target = np.empty((B, k + 1, V), dtype=np.uint16 if dtype == "bf16" else np.float32)
@@ -161,7 +164,17 @@ def make_zipf(name: str, seed: int, B: int, k: int, V: int = V_FULL, dtype: str 
         target[b] = _store(t, dtype)
         draft[b] = _store(d, dtype)
     stored_draft = bf16_bits_to_f32(draft) if dtype == "bf16" else draft
-    toks = _gumbel_drafts(rng, stored_draft, temperature)
+    greedy = np.zeros(B, dtype=bool)
+    if greedy_every > 0:
+        greedy[::greedy_every] = True
+        temperature[greedy] = 0.0
+    toks = _gumbel_drafts(rng, stored_draft, np.where(greedy, 1.0, temperature).astype(np.float32))
+    if greedy.any():
+        stored_target = bf16_bits_to_f32(target) if dtype == "bf16" else target
+        for b in np.nonzero(greedy)[0]:
+            for j in range(k):
+                src = stored_target[b, j] if rng.random() < 0.75 else stored_draft[b, j]
+                toks[b, j] = int(np.argmax(src))
     anchor = rng.integers(0, V, size=B, dtype=np.int64).astype(np.int32)
     W1 = W2t = None
     if markov:
