@@ -169,7 +169,8 @@ def _race(scores_w: np.ndarray, clocks: np.ndarray):
     return best, float(1.0 - second / s[best])
 
 
-def race_sample(w: np.ndarray, seed: int, b: int, step: int, group: int = RACE_GROUP_SIZE):
+def race_sample(w: np.ndarray, seed: int, b: int, step: int, group: int = RACE_GROUP_SIZE,
+                purposes=(philox.PURPOSE_RACE_GROUP, philox.PURPOSE_RACE_ITEM)):
     """Draw Y with P(Y = v) = w_v / sum(w) by a two-level exponential race.
 
     READING (the pages only say "sample from the normalized residual"): the
@@ -183,10 +184,10 @@ def race_sample(w: np.ndarray, seed: int, b: int, step: int, group: int = RACE_G
     V = w.shape[0]
     ng = (V + group - 1) // group
     W = np.array([np.sum(w[g * group: min(V, (g + 1) * group)]) for g in range(ng)])
-    Eg = philox.race_clocks(seed, b, np.arange(ng), philox.PURPOSE_RACE_GROUP, step)
+    Eg = philox.race_clocks(seed, b, np.arange(ng), purposes[0], step)
     g, mg = _race(W, Eg)
     lo, hi = g * group, min(V, (g + 1) * group)
-    Ev = philox.race_clocks(seed, b, np.arange(lo, hi), philox.PURPOSE_RACE_ITEM, step)
+    Ev = philox.race_clocks(seed, b, np.arange(lo, hi), purposes[1], step)
     v, mv = _race(w[lo:hi], Ev)
     return lo + v, min(mg, mv)
 
@@ -317,6 +318,61 @@ def verify(target, draft, dtype: str, draft_tokens, temperature=None, anchor=Non
         degen[b] = r["degenerate"]
     return dict(accepted_len=acc, out_tokens=out, diag=diag, margin_accept=m_acc,
                 margin_sample=m_smp, degenerate=degen)
+
+
+# ----------------------------------------------------------------------------
+# the drafter's Markov walk  [P2 §6 "Why the Markov Head Helps"; P1 §3 "The Markov
+# fix-up" and Figure 2]
+# ----------------------------------------------------------------------------
+def draft_purposes(j: int):
+    """READING: the walk's race clocks for slot j use Philox purpose words 16 + 2j
+    (groups) and 17 + 2j (ids), apart from the verifier's (1, 2, 3)."""
+    return 16 + 2 * j, 17 + 2 * j
+
+
+def draft_walk(draft, dtype: str, temperature=None, anchor=None, W1=None, W2t=None, num_drafts=None,
+               seed: int = 0, step: int = 0, group: int = RACE_GROUP_SIZE) -> dict:
+    """Draw the drafts slot by slot from the drafter with its Markov head:
+    x_j ~ softmax((d_j + W1[x_{j-1}] . W2) / T), x_{-1} = the anchor token.
+
+    The drafter's logits d_j [B, k, V] come from its parallel pass; the Markov head
+    is what makes slot j depend on the token drawn at slot j-1.  T = 0 takes the
+    largest biased logit (first id on ties).  Draws use the two-level race with the
+    slot's own clocks (``draft_purposes``).  Returns tokens [B, k] (-1 past
+    gamma_b), log q_j(x_j) [B, k] and the smallest decision margin per stream:
+    the race margin, or for T = 0 (x_1 - x_2) / (|x_1| + 1) over the two largest
+    biased logits.
+    """
+    draft = np.asarray(draft)
+    B, k, V = draft.shape
+    T_all = np.ones(B) if temperature is None else np.asarray(temperature, dtype=np.float32).astype(np.float64)
+    a_all = np.full(B, -1) if anchor is None else np.asarray(anchor, dtype=np.int64)
+    g_all = np.full(B, k) if num_drafts is None else np.asarray(num_drafts, dtype=np.int64)
+    if W1 is not None:
+        W1 = widen(W1, "bf16")
+        W2t = widen(W2t, "bf16")
+    toks = np.full((B, k), -1, dtype=np.int32)
+    logq = np.full((B, k), np.nan)
+    margin = np.full(B, np.inf)
+    for b in range(B):
+        prev = int(a_all[b])
+        for j in range(int(g_all[b])):
+            d = widen(draft[b, j], dtype)
+            if W1 is not None:
+                d = d + markov_bias(W1, W2t, prev)[0]
+            T = float(T_all[b])
+            if T == 0.0:
+                order = np.argsort(-d, kind="stable")
+                x = int(np.argmax(d))
+                m = (d[order[0]] - d[order[1]]) / (abs(d[order[0]]) + 1.0) if V > 1 else np.inf
+            else:
+                ls = log_softmax(d / T)
+                x, m = race_sample(np.exp(ls), seed, b, step, group, draft_purposes(j))
+                logq[b, j] = ls[x]
+            toks[b, j] = x
+            margin[b] = min(margin[b], m)
+            prev = x
+    return dict(tokens=toks, logq=logq, margin=margin)
 
 
 # ----------------------------------------------------------------------------
