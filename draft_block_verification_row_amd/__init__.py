@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.argtypes = [ctypes.POINTER(VerifyProblem), ctypes.POINTER(VerifyOutputs), vp, sz, vp]
             f.restype = i32
+        L.dspark_draft_sample.argtypes = [ctypes.POINTER(VerifyProblem), vp, vp, vp, sz, vp]
+        L.dspark_draft_sample.restype = i32
         L.dspark_markov_bias.argtypes = [vp, vp, i32, i32, vp, i32, vp, i32, vp, vp]
         L.dspark_markov_bias.restype = i32
         L.dspark_adaptive_k.argtypes = [vp, vp, ctypes.c_float, i32, i32, i32, vp, i32, vp, vp, vp, vp]
@@ -179,6 +181,51 @@ def verify_tokenwise(target, draft, draft_tokens, **kw):
 def verify_block(target, draft, draft_tokens, **kw):
     """Block verification; returns (accepted_len [B], out_tokens [B, k+1], diag or None)."""
     return _verify("dspark_verify_block", target, draft, draft_tokens, **kw)
+
+
+def draft_sample(draft, num_drafts=None, temperature=None, W1=None, W2t=None, anchor=None, seed=0, step=0,
+                 logq=False, workspace=None, out=None):
+    """The drafter's Markov walk: x_j ~ softmax((d_j + W1[x_{j-1}] W2)/T) slot by slot.
+
+    draft [B, k, V]; returns (tokens [B, k] int32 with -1 past gamma_b, log q_j(x_j) [B, k] fp64 or None).
+    """
+    if draft.dim() != 3:
+        raise ValueError("draft_logits must be [B, k, V]")
+    B, k, V = draft.shape
+    dev = draft.device
+    if draft.dtype == torch.float32:
+        dt, dts = DSPARK_F32, (torch.float32,)
+    elif draft.dtype in _BF16:
+        dt, dts = DSPARK_BF16, _BF16
+    else:
+        raise ValueError("logits must be float32 or bf16")
+    _need(draft, "draft_logits", (B, k, V), dts, dev)
+    if num_drafts is not None:
+        _need(num_drafts, "num_drafts", (B,), (torch.int32,), dev)
+    if temperature is not None:
+        _need(temperature, "temperature", (B,), (torch.float32,), dev)
+    R = 0
+    if W1 is not None:
+        if W2t is None:
+            raise ValueError("W2t is required with W1")
+        R = int(W1.shape[1])
+        _need(W1, "W1", (V, R), _BF16, dev)
+        _need(W2t, "W2t", (V, R), _BF16, dev)
+    if anchor is not None:
+        _need(anchor, "anchor_tokens", (B,), (torch.int32,), dev)
+    p = VerifyProblem(B=B, k=k, V=V, dtype=dt, target_logits=None, draft_logits=_ptr(draft), draft_tokens=None,
+                      num_drafts=_ptr(num_drafts), temperature=_ptr(temperature), W1=_ptr(W1),
+                      W2t=_ptr(W2t) if W1 is not None else None, anchor_tokens=_ptr(anchor), R=R,
+                      step=int(step) & 0xFFFFFFFF, seed=int(seed) & 0xFFFFFFFFFFFFFFFF)
+    need = lib().dspark_workspace_bytes(ctypes.byref(p))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    toks = torch.empty(B, k, dtype=torch.int32, device=dev) if out is None else out
+    _need(toks, "tokens_out", (B, k), (torch.int32,), dev)
+    lq = torch.empty(B, k, dtype=torch.float64, device=dev) if logq else None
+    _check(lib().dspark_draft_sample(ctypes.byref(p), _ptr(toks), _ptr(lq), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(dev)))
+    return toks, lq
 
 
 def markov_bias(W1, W2t, prev_tokens, logits_in=None, out=None):

@@ -122,9 +122,50 @@ dspark_status verify_common(const dspark_verify_problem* p, const dspark_verify_
   return DSPARK_OK;
 }
 
+// The drafter walk: the verify problem's shapes, draft logits, temperatures, Markov
+// factors, anchors, num_drafts, seed and step; no target logits or draft tokens.
+dspark_status walk_common(const dspark_verify_problem* p, int32_t* tokens_out, double* logq_out, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (!problem_sizes_ok(p) || !p->draft_logits || !tokens_out) return DSPARK_ERR_INVALID_ARG;
+  if (p->W1 != nullptr) {
+    if (p->W2t == nullptr) return DSPARK_ERR_INVALID_ARG;
+    if (!rank_ok(p->R)) return DSPARK_ERR_UNSUPPORTED;
+    if (!aligned16(p->W1) || !aligned16(p->W2t)) return DSPARK_ERR_UNSUPPORTED;
+  }
+  const Layout L = layout(p->B, p->k, p->V);
+  if (ws == nullptr || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
+    return DSPARK_ERR_WORKSPACE;
+  Args a;
+  memset(&a, 0, sizeof(a));
+  a.B = p->B; a.k = p->k; a.V = p->V; a.R = p->W1 ? p->R : 0;
+  a.NG = (p->V + kGroup - 1) / kGroup;
+  a.dtype = p->dtype;
+  const int esz = p->dtype == DSPARK_BF16 ? 2 : 4;
+  a.vec_ok = ((size_t)p->V * esz) % 16 == 0 && aligned16(p->draft_logits);
+  a.draft = p->draft_logits;
+  a.tokens = tokens_out;          // slot j reads x_{j-1} from the tokens drawn so far
+  a.num_drafts = p->num_drafts;
+  a.temperature = p->temperature;
+  a.W1 = p->W1;
+  a.W2t = p->W1 ? p->W2t : nullptr;
+  a.anchor = p->anchor_tokens;
+  a.key0 = (uint32_t)(p->seed & 0xffffffffu);
+  a.key1 = (uint32_t)(p->seed >> 32);
+  a.step = p->step;
+  a.ws.tpart = reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) + L.off[0]);   // [NG][B] partials
+  if (launch_walk(a, tokens_out, logq_out, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return DSPARK_ERR_HIP;
+  return DSPARK_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+dspark_status dspark_draft_sample(const dspark_verify_problem* p, int32_t* tokens_out, double* logq_out,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  return walk_common(p, tokens_out, logq_out, ws, ws_bytes, stream);
+}
 
 size_t dspark_workspace_bytes(const dspark_verify_problem* p) {
   if (!problem_sizes_ok(p)) return 0;

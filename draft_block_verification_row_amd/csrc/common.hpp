@@ -18,6 +18,9 @@ constexpr double kLog2e = 1.4426950408889634074;
 constexpr double kLn2 = 0.69314718055994530942;
 
 enum Purpose : uint32_t { kPurposeDraft = 0, kPurposeAccept = 1, kPurposeRaceGroup = 2, kPurposeRaceItem = 3 };
+// The drafter walk's race clocks for slot j: purpose 16 + 2j (groups), 17 + 2j (ids).
+__host__ __device__ constexpr uint32_t walk_purpose_group(int j) { return 16u + 2u * (uint32_t)j; }
+__host__ __device__ constexpr uint32_t walk_purpose_item(int j) { return 17u + 2u * (uint32_t)j; }
 enum Dtype : int { kF32 = 0, kBF16 = 1 };
 
 // ---------------------------------------------------------------------------
@@ -210,6 +213,7 @@ constexpr size_t kMaxPassLds = 32 * 1024;
 
 // launchers (kernels.hip)
 hipError_t launch_verify(const Args& a, hipStream_t st, void* const* events);
+hipError_t launch_walk(const Args& a, int32_t* tokens_out, double* logq_out, hipStream_t st);
 hipError_t launch_markov_bias(const BiasArgs& ba, int NG, hipStream_t st);
 hipError_t launch_adaptive(const AdaptArgs& aa, hipStream_t st);
 

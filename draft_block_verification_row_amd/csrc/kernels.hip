@@ -1044,6 +1044,169 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// The drafter's Markov walk [P2 §6 "Why the Markov Head Helps"; P1 §3 "The Markov
+// fix-up", Figure 2]: x_j ~ softmax((d_j + W1[x_{j-1}] . W2) / T), x_{-1} = anchor.
+// Slot j needs x_{j-1}, so each slot is two launches: group partials of the
+// biased logits of every stream (MFMA, like pass 1's draft rows), then one
+// workgroup per stream draws x_j with the two-level race (fp64 inside the group).
+// ---------------------------------------------------------------------------
+constexpr int kWalkRows = 64;   // streams per LDS block in the partial pass
+
+template <int DT, int KS, bool MARKOV, bool VEC>
+__global__ __launch_bounds__(kThreads, 2) void walk_partials_kernel(Args a, int j) {
+  __shared__ float2 part[kWalkRows][kWaves];
+  __shared__ int s_prev[kWalkRows];
+  __shared__ float s_c[kWalkRows];
+  __shared__ uint4 w1s[MARKOV ? kWalkRows * (4 * KS + 1) : 1];   // W1 rows, padded stride
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, q = l >> 4;
+  const int cb = g * kGroup + w * kWaveCols;
+  const int cw = cb + 16 * q;
+  const int c0 = VEC ? min(cw, a.V - 16) : cw;
+  const int shift = VEC ? (cw >= a.V ? 16 : cw - c0) : 0;
+  const bool rag = VEC && cb + kWaveCols > a.V;
+  const size_t rb = (size_t)a.V * (DT == kBF16 ? 2 : 4);
+  const char* base = reinterpret_cast<const char*>(a.draft);
+  bf16x8 A[4][KS];
+  if (MARKOV) load_w2_slab<KS, VEC>(a, cb, n, q, A);
+  for (int r0 = 0; r0 < a.B; r0 += kWalkRows) {
+    if (tid < kWalkRows) {
+      const int b = min(r0 + tid, a.B - 1);
+      s_prev[tid] = draft_prev(a, b, j);   // the anchor, or x_{j-1} from the previous slot
+      const float T = stream_temp(a, b);
+      s_c[tid] = T > 0.f ? (float)(kLog2e / (double)T) : 1e-30f;
+    }
+    __syncthreads();
+    if (MARKOV) {   // stage the block's W1 rows: whole rows per wave instruction
+      u32x4* d = reinterpret_cast<u32x4*>(w1s);
+      for (int u = tid; u < kWalkRows * 4 * KS; u += kThreads) {
+        const int row = u / (4 * KS), piece = u % (4 * KS);
+        const int pv = s_prev[row];
+        const u32x4 v = *reinterpret_cast<const u32x4*>(a.W1 + (size_t)(pv >= 0 ? pv : 0) * a.R + 8 * piece);
+        d[row * (4 * KS + 1) + piece] = pv >= 0 ? v : u32x4{0u, 0u, 0u, 0u};
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int cc = 0; cc < kWalkRows / kChunk; ++cc) {
+      const int rr = cc * kChunk + n;              // row within the block
+      const int b = min(r0 + rr, a.B - 1);
+      Raw16<DT> xr;
+      raw_load<DT, VEC>(xr, base + ((size_t)b * a.k + j) * rb, c0, a.V);
+      float x[16];
+      raw_to_f32<DT>(xr, x);
+      if (MARKOV) {
+        bf16x8 Bop[KS];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+          Bop[kk] = __builtin_bit_cast(bf16x8, w1s[rr * (4 * KS + 1) + 4 * kk + q]);
+        markov_mma<KS>(A, Bop, x);
+      }
+      if (rag) mask_shift(x, shift);
+      const float2 pw = row_partial<0>(x, s_c[rr]);
+      if (q == 0) part[rr][w] = pw;
+    }
+    __syncthreads();
+    if (tid < kWalkRows && r0 + tid < a.B) {
+      float2 p[kWaves];
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) p[ww] = part[tid][ww];
+      a.ws.tpart[(size_t)g * a.B + r0 + tid] = combine_waves(p, s_c[tid]);
+    }
+    __syncthreads();
+  }
+}
+
+// (value, index) maximum over the workgroup, lowest index among equal values.
+__device__ void block_max_index(double& val, int& idx, double* rs, int* ri) {
+  const int tid = threadIdx.x;
+  for (int off = 32; off >= 1; off >>= 1) {
+    const double ov = __shfl_xor(val, off);
+    const int oi = __shfl_xor(idx, off);
+    if (ov > val || (ov == val && oi < idx)) { val = ov; idx = oi; }
+  }
+  if ((tid & 63) == 0) { rs[tid >> 6] = val; ri[tid >> 6] = idx; }
+  __syncthreads();
+  val = rs[0]; idx = ri[0];
+  for (int ww = 1; ww < kWaves; ++ww)
+    if (rs[ww] > val || (rs[ww] == val && ri[ww] < idx)) { val = rs[ww]; idx = ri[ww]; }
+  __syncthreads();
+}
+
+template <int DT, int KS>
+__global__ __launch_bounds__(kThreads) void walk_pick_kernel(Args a, int j, int32_t* tokens_out, double* logq_out) {
+  __shared__ double rs[kWaves];
+  __shared__ int ri[kWaves];
+  __shared__ double red[kWaves];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int NG = a.NG;
+  if (j >= stream_gamma(a, b)) {
+    if (tid == 0) {
+      tokens_out[b * a.k + j] = -1;
+      if (logq_out != nullptr) logq_out[b * a.k + j] = NAN;
+    }
+    return;
+  }
+  const float Tf = stream_temp(a, b);
+  const bool greedy = Tf == 0.f;
+  const double invT = greedy ? 0.0 : 1.0 / (double)Tf;
+  const int prev = draft_prev(a, b, j);
+  const size_t esz = DT == kBF16 ? 2 : 4;
+  const char* drow = reinterpret_cast<const char*>(a.draft) + ((size_t)b * a.k + j) * a.V * esz;
+  // group choice: the largest maximum (greedy) or the race over group masses
+  double best = -INFINITY;
+  int gbest = 0x7fffffff;
+  double lmax = -INFINITY;   // for log q: max over groups of m_g / T + ln s_g
+  for (int gi = tid; gi < NG; gi += kThreads) {
+    const float2 p = a.ws.tpart[(size_t)gi * a.B + b];
+    if (p.x == -INFINITY) continue;
+    double sc;
+    if (greedy) {
+      sc = (double)p.x;
+    } else {
+      const double lw = (double)p.x * invT + log((double)p.y);   // ln W_g (unnormalised)
+      lmax = fmax(lmax, lw);
+      sc = lw - log(race_clock(a.key0, a.key1, (uint32_t)b, (uint32_t)gi, walk_purpose_group(j), a.step));
+    }
+    if (sc > best) { best = sc; gbest = gi; }
+  }
+  block_max_index(best, gbest, rs, ri);
+  const int gsel = gbest < NG ? gbest : 0;
+  // inside the group: biased logits in fp64
+  const int v = gsel * kGroup + tid;
+  double xv = -INFINITY, sc = -INFINITY;
+  if (v < a.V) {
+    xv = (double)load1<DT>(drow, v);
+    if (a.W1 != nullptr && prev >= 0) xv += bias_at<KS>(a, prev, v);
+    sc = greedy ? xv
+                : xv * invT - log(race_clock(a.key0, a.key1, (uint32_t)b, (uint32_t)v, walk_purpose_item(j), a.step));
+  }
+  int vbest = v < a.V ? v : 0x7fffffff;
+  block_max_index(sc, vbest, rs, ri);
+  const int x = vbest < a.V ? vbest : gsel * kGroup;
+  if (logq_out != nullptr && !greedy) {
+    // log q_j(x) = x_v / T - ln sum_g W_g, the sum from the fp32 group partials
+    double m = lmax;
+    for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    m = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+    __syncthreads();
+    double s = 0.0;
+    for (int gi = tid; gi < NG; gi += kThreads) {
+      const float2 p = a.ws.tpart[(size_t)gi * a.B + b];
+      if (p.x != -INFINITY) s += exp((double)p.x * invT + log((double)p.y) - m);
+    }
+    s = block_sum(s, red);
+    if (tid == x - gsel * kGroup) logq_out[b * a.k + j] = xv * invT - (m + log(s));
+  } else if (tid == 0 && logq_out != nullptr) {
+    logq_out[b * a.k + j] = NAN;
+  }
+  if (tid == 0) tokens_out[b * a.k + j] = x;
+}
+
+// ---------------------------------------------------------------------------
 // Markov bias alone: out[i, v] = logits_in[i, v] + W1[prev_i] . W2[:, v]
 // ---------------------------------------------------------------------------
 template <int DT, int KS>
@@ -1177,6 +1340,36 @@ static hipError_t launch_dt(const Args& a, hipStream_t st, void* const* ev) {
 
 hipError_t launch_verify(const Args& a, hipStream_t st, void* const* ev) {
   return a.dtype == kBF16 ? launch_dt<kBF16>(a, st, ev) : launch_dt<kF32>(a, st, ev);
+}
+
+template <int DT, int KS, bool MARKOV, bool VEC>
+static hipError_t launch_walk_t(const Args& a, int32_t* tokens_out, double* logq_out, hipStream_t st) {
+  for (int j = 0; j < a.k; ++j) {
+    hipLaunchKernelGGL((walk_partials_kernel<DT, KS, MARKOV, VEC>), dim3(a.NG), dim3(kThreads), 0, st, a, j);
+    hipLaunchKernelGGL((walk_pick_kernel<DT, KS>), dim3(a.B), dim3(kThreads), 0, st, a, j, tokens_out, logq_out);
+  }
+  return hipGetLastError();
+}
+
+template <int DT, bool VEC>
+static hipError_t launch_walk_vec(const Args& a, int32_t* t, double* lq, hipStream_t st) {
+  if (a.W1 == nullptr) return launch_walk_t<DT, 1, false, VEC>(a, t, lq, st);
+  switch (a.R) {
+    case 32: return launch_walk_t<DT, 1, true, VEC>(a, t, lq, st);
+    case 64: return launch_walk_t<DT, 2, true, VEC>(a, t, lq, st);
+    case 128: return launch_walk_t<DT, 4, true, VEC>(a, t, lq, st);
+    default: return launch_walk_t<DT, 8, true, VEC>(a, t, lq, st);
+  }
+}
+
+template <int DT>
+static hipError_t launch_walk_dt(const Args& a, int32_t* t, double* lq, hipStream_t st) {
+  return (a.vec_ok && a.V >= 16) ? launch_walk_vec<DT, true>(a, t, lq, st) : launch_walk_vec<DT, false>(a, t, lq, st);
+}
+
+hipError_t launch_walk(const Args& a, int32_t* tokens_out, double* logq_out, hipStream_t st) {
+  return a.dtype == kBF16 ? launch_walk_dt<kBF16>(a, tokens_out, logq_out, st)
+                          : launch_walk_dt<kF32>(a, tokens_out, logq_out, st);
 }
 
 size_t verify_lds_bytes(int B) { return stream_table_bytes(B); }

@@ -140,6 +140,24 @@ dspark_status dspark_verify_block(const dspark_verify_problem* problem,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The drafter's walk with its Markov head [P2 §6 "Why the Markov Head Helps";
+ * P1 §3 "The Markov fix-up", Figure 2]: for each stream b and slot j < gamma_b,
+ *   x_j ~ softmax((d_j + W1[x_{j-1}] . W2) / T_b),   x_{-1} = anchor_tokens[b]
+ * (anchor < 0 or W1 NULL: no bias at that slot), drawn with the two-level race on
+ * Philox purposes 16 + 2j (groups) and 17 + 2j (ids); T_b = 0 takes the largest
+ * biased logit (first id among equal ones).  Uses from `problem`: B, k, V, dtype,
+ * draft_logits [B, k, V], num_drafts (NULL = k), temperature, W1, W2t, R,
+ * anchor_tokens, seed, step; target_logits and draft_tokens are ignored and may be
+ * NULL.  tokens_out: device int32 [B, k], -1 past gamma_b; it may be passed as the
+ * verify call's draft_tokens.  logq_out: device fp64 [B, k] of log q_j(x_j) (NaN for
+ * T_b = 0 and past gamma_b), or NULL.  workspace: as dspark_workspace_bytes(problem).
+ * 2k launches on `stream` (slot j needs x_{j-1}).
+ */
+dspark_status dspark_draft_sample(const dspark_verify_problem* problem, int32_t* tokens_out,
+                                  double* logq_out, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
  * DSpark Markov-head bias alone [P2 §6 "Why the Markov Head Helps"]:
  * out[i, v] = logits_in[i, v] + sum_r W1[prev_tokens[i], r] * W2t[v, r]  (fp32).
  * W1, W2t: device bf16 [V, R], R in {32, 64, 128, 256}.  prev_tokens: device

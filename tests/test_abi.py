@@ -29,7 +29,7 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("dspark_verify_tokenwise", "dspark_verify_block", "dspark_markov_bias", "dspark_adaptive_k",
-              "dspark_workspace_bytes", "dspark_status_string"):
+              "dspark_draft_sample", "dspark_workspace_bytes", "dspark_status_string"):
         assert n in names
 
 
@@ -105,3 +105,10 @@ def test_host_side_errors_without_gpu():
     ms = (ctypes.c_float * 3)(1.0, 2.0, 3.0)
     assert L.dspark_adaptive_k(256, 256, 0.0, 4, 5, 16, ctypes.cast(ms, ctypes.c_void_p), 3, 256, None, None,
                                None) == 1
+    # draft walk: no output buffer (1), no workspace (3), unsupported rank (2)
+    q = m.VerifyProblem(B=2, k=5, V=100, dtype=1, draft_logits=256)
+    assert L.dspark_draft_sample(ctypes.byref(q), None, None, 256, 1 << 30, None) == 1
+    assert L.dspark_draft_sample(ctypes.byref(q), 256, None, None, 0, None) == 3
+    q.W1 = q.W2t = 256
+    q.R = 48
+    assert L.dspark_draft_sample(ctypes.byref(q), 256, None, 256, 1 << 30, None) == 2
