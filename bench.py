@@ -238,6 +238,33 @@ def main() -> int:
         "accepted_mean": {m: round(float(np.mean(realized[m])), 4) for m in realized},
     }
 
+    # the drafter's Markov walk at the same shape (the step before verification)
+    log("timing the drafter walk (B=64, k=5 slots)")
+    wtoks = torch.empty(B, k, dtype=torch.int32, device=dev)
+    for i in range(5):
+        s = sets[i % len(sets)]
+        dv.draft_sample(s["draft"], temperature=s["temp"], W1=s["W1"], W2t=s["W2t"], anchor=s["anchor"],
+                        seed=wl.seed, step=i, workspace=ws, out=wtoks)
+    nwalk = 30
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(nwalk):
+        s = sets[i % len(sets)]
+        dv.draft_sample(s["draft"], temperature=s["temp"], W1=s["W1"], W2t=s["W2t"], anchor=s["anchor"],
+                        seed=wl.seed, step=1000 + i, workspace=ws, out=wtoks)
+    t1.record()
+    torch.cuda.synchronize()
+    walk_ms = t0.elapsed_time(t1) / nwalk
+    walk_alg = 2.0 * V * B * k + 2.0 * R * V + 2.0 * R * B * k   # draft rows once, W2 once, W1 rows
+    walk_read = 2.0 * V * B * k + k * 2.0 * R * V + 2.0 * R * B * k   # W2 is read again for every slot
+    result["draft_walk"] = {
+        "ms_per_call": round(walk_ms, 5),
+        "drafts_per_s": round(B * k / (walk_ms * 1e-3), 1),
+        "alg_GBps": round(walk_alg / (walk_ms * 1e-3) / 1e9, 1),
+        "bytes_read_by_design_GBps": round(walk_read / (walk_ms * 1e-3) / 1e9, 1),
+        "launches": 2 * k,
+    }
+
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)

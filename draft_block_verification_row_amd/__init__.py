@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
             f.restype = i32
         L.dspark_draft_sample.argtypes = [ctypes.POINTER(VerifyProblem), vp, vp, vp, sz, vp]
         L.dspark_draft_sample.restype = i32
+        L.dspark_draft_scatter.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
+        L.dspark_draft_scatter.restype = i32
+        L.dspark_k_for_batch.argtypes = [vp, i32, i32, i32]
+        L.dspark_k_for_batch.restype = i32
         L.dspark_markov_bias.argtypes = [vp, vp, i32, i32, vp, i32, vp, i32, vp, vp]
         L.dspark_markov_bias.restype = i32
         L.dspark_adaptive_k.argtypes = [vp, vp, ctypes.c_float, i32, i32, i32, vp, i32, vp, vp, vp, vp]
@@ -226,6 +230,33 @@ def draft_sample(draft, num_drafts=None, temperature=None, W1=None, W2t=None, an
     _check(lib().dspark_draft_sample(ctypes.byref(p), _ptr(toks), _ptr(lq), _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(dev)))
     return toks, lq
+
+
+def draft_scatter(reduced, vocab_ids, V: int, out=None):
+    """Scatter reduced-vocabulary draft logits [..., K] into [..., V] columns, -inf elsewhere."""
+    dev = reduced.device
+    K = int(reduced.shape[-1])
+    rows = int(reduced.numel() // K) if K else 0
+    if reduced.dtype == torch.float32:
+        dt, dts = DSPARK_F32, (torch.float32,)
+    elif reduced.dtype in _BF16:
+        dt, dts = DSPARK_BF16, _BF16
+    else:
+        raise ValueError("logits must be float32 or bf16")
+    _need(reduced, "reduced", tuple(reduced.shape), dts, dev)
+    _need(vocab_ids, "vocab_ids", (K,), (torch.int32,), dev)
+    if out is None:
+        out = torch.empty(*reduced.shape[:-1], V, dtype=reduced.dtype, device=dev)
+    _need(out, "out", tuple(reduced.shape[:-1]) + (V,), dts, dev)
+    _check(lib().dspark_draft_scatter(_ptr(reduced), _ptr(vocab_ids), rows, K, V, dt, _ptr(out), _stream(dev)))
+    return out
+
+
+def k_for_batch(schedule, batch: int, k_default: int) -> int:
+    """Draft count for a batch size from (lo, hi, k) triples, e.g. [[1, 4, 5], [5, 8, 3], [9, 32, 3]]."""
+    flat = [int(x) for t in schedule for x in t]
+    arr = (ctypes.c_int32 * len(flat))(*flat)
+    return int(lib().dspark_k_for_batch(ctypes.cast(arr, ctypes.c_void_p), len(schedule), int(batch), int(k_default)))
 
 
 def markov_bias(W1, W2t, prev_tokens, logits_in=None, out=None):

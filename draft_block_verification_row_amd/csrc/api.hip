@@ -221,6 +221,23 @@ dspark_status dspark_adaptive_k(const uint16_t* hidden, const uint16_t* w, float
   return DSPARK_OK;
 }
 
+dspark_status dspark_draft_scatter(const void* reduced, const int32_t* vocab_ids, int32_t rows, int32_t K,
+                                   int32_t V, int32_t dtype, void* out, void* stream) {
+  if (!reduced || !vocab_ids || !out || rows < 0 || K < 1 || V < 1 || K > V) return DSPARK_ERR_INVALID_ARG;
+  if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return DSPARK_ERR_INVALID_ARG;
+  if (rows == 0) return DSPARK_OK;
+  if (launch_scatter(reduced, vocab_ids, rows, K, V, dtype, out, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return DSPARK_ERR_HIP;
+  return DSPARK_OK;
+}
+
+int32_t dspark_k_for_batch(const int32_t* schedule, int32_t n, int32_t batch, int32_t k_default) {
+  if (schedule == nullptr) return k_default;
+  for (int32_t i = 0; i < n; ++i)
+    if (schedule[3 * i] <= batch && batch <= schedule[3 * i + 1]) return schedule[3 * i + 2];
+  return k_default;
+}
+
 const char* dspark_status_string(dspark_status s) {
   switch (s) {
     case DSPARK_OK: return "ok";

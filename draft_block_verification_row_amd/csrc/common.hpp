@@ -216,5 +216,7 @@ hipError_t launch_verify(const Args& a, hipStream_t st, void* const* events);
 hipError_t launch_walk(const Args& a, int32_t* tokens_out, double* logq_out, hipStream_t st);
 hipError_t launch_markov_bias(const BiasArgs& ba, int NG, hipStream_t st);
 hipError_t launch_adaptive(const AdaptArgs& aa, hipStream_t st);
+hipError_t launch_scatter(const void* in, const int32_t* ids, int rows, int K, int V, int dtype, void* out,
+                          hipStream_t st);
 
 }  // namespace dspark

@@ -1207,6 +1207,36 @@ __global__ __launch_bounds__(kThreads) void walk_pick_kernel(Args a, int j, int3
 }
 
 // ---------------------------------------------------------------------------
+// Reduced draft vocabulary [P1 §3 "The Markov fix-up": the drafter scores a reduced
+// vocabulary and scatters its logits into target-vocabulary columns]: every other
+// column is -inf, so q = 0 there and the residual keeps the target's mass.
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(kThreads) void fill_ninf_kernel(void* out, size_t n) {
+  const size_t stride = (size_t)gridDim.x * kThreads;
+  for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
+    if (DT == kBF16) reinterpret_cast<uint16_t*>(out)[i] = 0xFF80u;   // bf16 -inf
+    else reinterpret_cast<float*>(out)[i] = -INFINITY;
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void scatter_kernel(const void* in, const int32_t* ids, int rows, int K, int V,
+                                                           void* out) {
+  const size_t n = (size_t)rows * K;
+  const size_t stride = (size_t)gridDim.x * kThreads;
+  for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
+    const int r = (int)(i / K), c = (int)(i - (size_t)r * K);
+    const int v = ids[c];
+    if (v < 0 || v >= V) continue;   // ids are the caller's: out-of-range ones are dropped
+    if (DT == kBF16)
+      reinterpret_cast<uint16_t*>(out)[(size_t)r * V + v] = reinterpret_cast<const uint16_t*>(in)[i];
+    else
+      reinterpret_cast<float*>(out)[(size_t)r * V + v] = reinterpret_cast<const float*>(in)[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Markov bias alone: out[i, v] = logits_in[i, v] + W1[prev_i] . W2[:, v]
 // ---------------------------------------------------------------------------
 template <int DT, int KS>
@@ -1387,6 +1417,21 @@ static hipError_t launch_bias_dt(const BiasArgs& ba, int NG, hipStream_t st) {
 
 hipError_t launch_markov_bias(const BiasArgs& ba, int NG, hipStream_t st) {
   return ba.dtype == kBF16 ? launch_bias_dt<kBF16>(ba, NG, st) : launch_bias_dt<kF32>(ba, NG, st);
+}
+
+hipError_t launch_scatter(const void* in, const int32_t* ids, int rows, int K, int V, int dtype, void* out,
+                          hipStream_t st) {
+  const size_t n_out = (size_t)rows * V, n_in = (size_t)rows * K;
+  auto grid = [](size_t n) { const size_t g = (n + kThreads - 1) / kThreads; return (int)(g < 4096 ? g : 4096); };
+  const int g1 = grid(n_out), g2 = grid(n_in);
+  if (dtype == kBF16) {
+    hipLaunchKernelGGL(fill_ninf_kernel<kBF16>, dim3(g1), dim3(kThreads), 0, st, out, n_out);
+    hipLaunchKernelGGL(scatter_kernel<kBF16>, dim3(g2), dim3(kThreads), 0, st, in, ids, rows, K, V, out);
+  } else {
+    hipLaunchKernelGGL(fill_ninf_kernel<kF32>, dim3(g1), dim3(kThreads), 0, st, out, n_out);
+    hipLaunchKernelGGL(scatter_kernel<kF32>, dim3(g2), dim3(kThreads), 0, st, in, ids, rows, K, V, out);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_adaptive(const AdaptArgs& aa, hipStream_t st) {

@@ -158,6 +158,27 @@ dspark_status dspark_draft_sample(const dspark_verify_problem* problem, int32_t*
                                   void* stream);
 
 /*
+ * Reduced draft vocabulary [P1 §3 "The Markov fix-up": the drafter scores a reduced
+ * vocabulary and scatters those logits into target-vocabulary columns]:
+ *   out[r, vocab_ids[i]] = reduced[r, i],  out[r, v] = -inf for every other v,
+ * so that q = 0 outside the drafter's vocabulary (the verifiers then keep the
+ * target's mass there in the residual).  reduced: device [rows, K] of `dtype`;
+ * vocab_ids: device int32 [K], distinct ids in [0, V) (others are dropped);
+ * out: device [rows, V] of `dtype` (for example the draft_logits of a verify call,
+ * rows = B k).  Two launches (fill, scatter).
+ */
+dspark_status dspark_draft_scatter(const void* reduced, const int32_t* vocab_ids, int32_t rows,
+                                   int32_t K, int32_t V, int32_t dtype, void* out, void* stream);
+
+/*
+ * Draft count for a batch size [P1 §5: num_speculative_tokens_per_batch_size, a list
+ * of (lowest batch, highest batch, drafts) triples]: the drafts of the first triple
+ * whose range holds `batch`, else k_default.  Host only, pure; schedule: host
+ * int32 [n][3] or NULL.
+ */
+int32_t dspark_k_for_batch(const int32_t* schedule, int32_t n, int32_t batch, int32_t k_default);
+
+/*
  * DSpark Markov-head bias alone [P2 §6 "Why the Markov Head Helps"]:
  * out[i, v] = logits_in[i, v] + sum_r W1[prev_tokens[i], r] * W2t[v, r]  (fp32).
  * W1, W2t: device bf16 [V, R], R in {32, 64, 128, 256}.  prev_tokens: device

@@ -29,7 +29,8 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("dspark_verify_tokenwise", "dspark_verify_block", "dspark_markov_bias", "dspark_adaptive_k",
-              "dspark_draft_sample", "dspark_workspace_bytes", "dspark_status_string"):
+              "dspark_draft_sample", "dspark_draft_scatter", "dspark_k_for_batch", "dspark_workspace_bytes",
+              "dspark_status_string"):
         assert n in names
 
 
@@ -112,3 +113,19 @@ def test_host_side_errors_without_gpu():
     q.W1 = q.W2t = 256
     q.R = 48
     assert L.dspark_draft_sample(ctypes.byref(q), 256, None, 256, 1 << 30, None) == 2
+
+
+def test_k_for_batch_schedule():
+    """The pages' production schedule [[1, 4, 5], [5, 8, 3], [9, 32, 3]] (host only)."""
+    m = _built_lib()
+    sched = [[1, 4, 5], [5, 8, 3], [9, 32, 3]]
+    assert [m.k_for_batch(sched, b, 2) for b in (1, 4, 5, 8, 9, 32, 33)] == [5, 5, 3, 3, 3, 3, 2]
+    assert m.k_for_batch([], 7, 4) == 4
+
+
+def test_draft_scatter_host_errors():
+    m = _built_lib()
+    L = m.lib()
+    assert L.dspark_draft_scatter(None, 256, 2, 4, 10, 1, 256, None) == 1
+    assert L.dspark_draft_scatter(256, 256, 2, 11, 10, 1, 256, None) == 1   # K > V
+    assert L.dspark_draft_scatter(256, 256, 0, 4, 10, 1, 256, None) == 0    # nothing to do

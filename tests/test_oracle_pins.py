@@ -381,3 +381,49 @@ def test_greedy_ignores_seed_step_and_method():
         assert np.array_equal(o["accepted_len"], outs[0]["accepted_len"])
         assert np.array_equal(o["out_tokens"], outs[0]["out_tokens"])
     assert np.all(np.isnan(outs[0]["diag"]))
+
+
+# ----------------------------------------------------------------------------
+# reduced draft vocabulary [P1 §3: the drafter scores a reduced vocabulary and
+# scatters its logits into target columns; q = 0 on every other id]
+# ----------------------------------------------------------------------------
+def _reduced(q_rows, keep):
+    """q restricted to the ids in `keep` (renormalised), zero elsewhere."""
+    r = np.where(keep[None, :], q_rows, 0.0)
+    return r / r.sum(axis=-1, keepdims=True)
+
+
+@pytest.mark.parametrize("method", ["tokenwise", "block"])
+def test_lossless_with_reduced_draft_vocab(method):
+    """Target mass on ids the drafter cannot propose must still reach the output: the
+    residual max(0, P p - q) keeps P p where q = 0, and the law stays target-only."""
+    rng = np.random.Generator(np.random.PCG64(5))
+    V, gamma = 7, 3
+    keep = np.zeros(V, dtype=bool)
+    keep[[0, 2, 3, 6]] = True
+    p = np.exp(dspark.log_softmax(rng.standard_normal((gamma + 1, V)) * 1.5))
+    q = _reduced(np.exp(dspark.log_softmax(rng.standard_normal((gamma, V)) * 1.5)), keep)
+    pf, qf = _position_only(p, q)
+    with np.errstate(divide="ignore"):
+        E = en.emitted_distribution(pf, qf, gamma, V, method)
+    assert en.lossless_error(E, en.target_joint(pf, gamma, V)) < 1e-12
+
+
+def test_planted_residual_over_draft_vocab_only_is_caught(monkeypatch):
+    """A residual that skips the ids outside the draft vocabulary loses their target mass."""
+    rng = np.random.Generator(np.random.PCG64(6))
+    V, gamma = 7, 2
+    keep = np.zeros(V, dtype=bool)
+    keep[[1, 4, 5]] = True
+    p = np.exp(dspark.log_softmax(rng.standard_normal((gamma + 1, V)) * 1.5))
+    q = _reduced(np.exp(dspark.log_softmax(rng.standard_normal((gamma, V)) * 1.5)), keep)
+    pf, qf = _position_only(p, q)
+    real = dspark.residual_weights
+
+    def draft_vocab_only(logP, p_row, q_row):
+        return np.where(q_row > 0, real(logP, p_row, q_row), 0.0)
+    monkeypatch.setattr(dspark, "residual_weights", draft_vocab_only)
+    with np.errstate(all="ignore"):
+        E = en.emitted_distribution(pf, qf, gamma, V, "tokenwise")
+        err = en.lossless_error(E, en.target_joint(pf, gamma, V))
+    assert not err <= 1e-6

@@ -135,14 +135,18 @@ def make_tiny(seed: int = 1, B: int = 4, k: int = 3, V: int = 16, rho: float = 0
 def make_zipf(name: str, seed: int, B: int, k: int, V: int = V_FULL, dtype: str = "bf16",
               rho=(0.3, 0.95), temp=(0.6, 1.0), markov: bool = True, R: int = RANK,
               sigma: float = 3.0, zipf_s: float = 1.1, rho_per_slot=None,
-              confidence: bool = False, H: int = HIDDEN, greedy_every: int = 0) -> Workload:
+              confidence: bool = False, H: int = HIDDEN, greedy_every: int = 0,
+              draft_vocab: int = 0) -> Workload:
     """Zipf-biased Gaussian target logits with a correlated draft (c2..c5 recipes).
 
     ``rho`` / ``temp`` are a fixed value or a (lo, hi) range drawn per stream;
     ``rho_per_slot`` (length k) overrides rho slot by slot.  ``greedy_every`` = m > 0
     sets T = 0 on every m-th stream (mixed batches); such a stream's drafts copy the
     position of the target row's largest logit with probability 3/4 and of the draft
-    row's otherwise, so that greedy blocks are partly kept.
+    row's otherwise, so that greedy blocks are partly kept.  ``draft_vocab`` = K > 0
+    gives the drafter a reduced vocabulary: a seeded set of K ids keeps its draft
+    logits and every other id gets -inf (the drafter's logits scattered into the
+    target's columns); ``meta["draft_vocab"]`` holds the sorted ids.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     target = np.empty((B, k + 1, V), dtype=np.uint16 if dtype == "bf16" else np.float32)
@@ -161,6 +165,11 @@ def make_zipf(name: str, seed: int, B: int, k: int, V: int = V_FULL, dtype: str 
         noise = rng.standard_normal((k, V), dtype=np.float32) * np.float32(sigma)
         r = rhos[b][:, None].astype(np.float32)
         d = r * t[:k] + np.sqrt(1.0 - r * r) * noise
+        if draft_vocab > 0:
+            if b == 0:
+                keep = np.zeros(V, dtype=bool)
+                keep[rng.choice(V, size=draft_vocab, replace=False)] = True
+            d = np.where(keep[None, :], d, np.float32(-np.inf)).astype(np.float32)
         target[b] = _store(t, dtype)
         draft[b] = _store(d, dtype)
     stored_draft = bf16_bits_to_f32(draft) if dtype == "bf16" else draft
@@ -183,6 +192,8 @@ def make_zipf(name: str, seed: int, B: int, k: int, V: int = V_FULL, dtype: str 
     wl = Workload(name=name, B=B, k=k, V=V, dtype=dtype, target=target, draft=draft,
                   draft_tokens=toks, temperature=temperature, anchor=anchor, W1=W1, W2t=W2t,
                   seed=seed, step=0, meta={"rho": rhos})
+    if draft_vocab > 0:
+        wl.meta["draft_vocab"] = np.nonzero(keep)[0].astype(np.int32)
     if confidence:
         wl.hidden = f32_to_bf16_bits(rng.standard_normal((B, k, H), dtype=np.float32))
         wl.conf_w = f32_to_bf16_bits(rng.standard_normal(H, dtype=np.float32) / np.float32(np.sqrt(H)))
