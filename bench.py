@@ -265,6 +265,77 @@ def main() -> int:
         "launches": 2 * k,
     }
 
+    # batch-level scheduler at the adaptive ragged shape (B=256 streams, k=5), and the
+    # host cost of the online cost table's event pairs around each call
+    log("timing the batch scheduler (B=256, k=5) and the online cost table")
+    Bs, ks = 256, 5
+    gsch = np.random.Generator(np.random.PCG64(5))
+    c_s = torch.from_numpy(gsch.uniform(0.5, 0.95, size=(Bs, ks)).astype(np.float32)).to(dev)
+    ms_s = torch.from_numpy((10.0 + 0.05 * np.arange(Bs * (ks + 1) + 1)).astype(np.float32)).to(dev)
+    n_s = torch.empty(Bs, dtype=torch.int32, device=dev)
+    for _ in range(10):
+        dv.schedule_batch(c_s, ms_s, n_out=n_s)
+    nsch = 200
+    tot_s = torch.empty(1, dtype=torch.int32, device=dev)
+    exp_s = torch.empty(1, dtype=torch.float64, device=dev)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(nsch):
+        dv.schedule_batch(c_s, ms_s, n_out=n_s, total_out=tot_s, expected_out=exp_s)
+    t1.record()
+    torch.cuda.synchronize()
+    sched_ms = t0.elapsed_time(t1) / nsch   # bounded by the Python call, not the kernel
+    n_eager = n_s.clone()
+    # the kernel alone: 20 launches captured in a HIP graph, replayed 10 times, every
+    # replay's counts checked against the eager ones
+    sched_graph_ms = None
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                for _ in range(20):
+                    dv.schedule_batch(c_s, ms_s, n_out=n_s, total_out=tot_s, expected_out=exp_s)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        total_ms = 0.0
+        for _ in range(10):
+            n_s.fill_(-1)
+            t0.record()
+            graph.replay()
+            t1.record()
+            torch.cuda.synchronize()
+            total_ms += t0.elapsed_time(t1)
+            if not torch.equal(n_s, n_eager):
+                raise RuntimeError("graph replay of the scheduler disagrees with the eager call")
+        sched_graph_ms = total_ms / 200
+        del graph
+    except RuntimeError as e:
+        log(f"scheduler graph timing skipped: {e}")
+    table = dv.CostTable((10.0 + 0.05 * np.arange(Bs * (ks + 1) + 1)).astype(np.float32))
+    host_s = 0.0
+    for _ in range(nsch):
+        h0 = time.perf_counter()
+        table.begin(Bs + ks)
+        host_s += time.perf_counter() - h0
+        dv.schedule_batch(c_s, ms_s, n_out=n_s, total_out=tot_s, expected_out=exp_s)
+        h0 = time.perf_counter()
+        table.end()
+        table.poll()
+        host_s += time.perf_counter() - h0
+    torch.cuda.synchronize()
+    table.poll()
+    result["batch_schedule"] = {
+        "B": Bs, "k": ks,
+        "us_per_call_python": round(sched_ms * 1e3, 2),
+        "us_per_launch_graph": None if sched_graph_ms is None else round(sched_graph_ms * 1e3, 2),
+        "drafts_chosen": int(n_s.sum().item()),
+        "cost_table_host_us_per_step": round(host_s / nsch * 1e6, 2),
+        "cost_table_filed": table.stats()["filed"],
+    }
+    del table
+
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)

@@ -70,6 +70,27 @@ def lib() -> ctypes.CDLL:
         L.dspark_markov_bias.restype = i32
         L.dspark_adaptive_k.argtypes = [vp, vp, ctypes.c_float, i32, i32, i32, vp, i32, vp, vp, vp, vp]
         L.dspark_adaptive_k.restype = i32
+        L.dspark_schedule_batch.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp, vp]
+        L.dspark_schedule_batch.restype = i32
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        L.dspark_cost_table_create.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(vp)]
+        L.dspark_cost_table_create.restype = i32
+        L.dspark_cost_table_destroy.argtypes = [vp]
+        L.dspark_cost_table_destroy.restype = None
+        L.dspark_cost_table_begin.argtypes = [vp, i32, vp]
+        L.dspark_cost_table_begin.restype = i32
+        L.dspark_cost_table_end.argtypes = [vp, vp]
+        L.dspark_cost_table_end.restype = i32
+        L.dspark_cost_table_poll.argtypes = [vp, ctypes.POINTER(i32)]
+        L.dspark_cost_table_poll.restype = i32
+        L.dspark_cost_table_observe.argtypes = [vp, i32, ctypes.c_float]
+        L.dspark_cost_table_observe.restype = i32
+        L.dspark_cost_table_read.argtypes = [vp, vp, i32]
+        L.dspark_cost_table_read.restype = i32
+        L.dspark_cost_table_stats.argtypes = [vp, i64p, i64p, ctypes.POINTER(i32)]
+        L.dspark_cost_table_stats.restype = i32
+        L.dspark_cost_table_log.argtypes = [vp, vp, vp, i32]
+        L.dspark_cost_table_log.restype = i32
         L.dspark_status_string.argtypes = [i32]
         L.dspark_status_string.restype = ctypes.c_char_p
         del u32
@@ -292,3 +313,90 @@ def adaptive_k(hidden, w, bias: float, verify_ms, want_c: bool = True):
     _check(lib().dspark_adaptive_k(_ptr(hidden), _ptr(w), float(bias), B, k, H, ctypes.cast(ms, ctypes.c_void_p),
                                    len(verify_ms), _ptr(n), _ptr(c), _ptr(a), _stream(dev)))
     return n, c, a
+
+
+MAX_SCHEDULE = 4096
+
+
+def schedule_batch(c, verify_ms, n_out=None, total_out=None, expected_out=None):
+    """Batch-level scheduler: per-stream draft counts for one verify batch.
+
+    c: [B, k] fp32 confidences on the GPU; verify_ms: fp32 cost table on the same
+    device indexed by the batch's token count (at least B (k + 1) + 1 entries).
+    Returns (n [B] int32, total tokens [1] int32, expected accepted tokens [1]
+    fp64), all device tensors; no host synchronisation.
+    """
+    dev = c.device
+    B, k = c.shape
+    _need(c, "c", (B, k), (torch.float32,), dev)
+    _need(verify_ms, "verify_ms", None, (torch.float32,), dev)
+    if verify_ms.dim() != 1:
+        raise ValueError("verify_ms must be 1-D")
+    n = torch.empty(B, dtype=torch.int32, device=dev) if n_out is None else n_out
+    _need(n, "n_out", (B,), (torch.int32,), dev)
+    total = torch.empty(1, dtype=torch.int32, device=dev) if total_out is None else total_out
+    expected = torch.empty(1, dtype=torch.float64, device=dev) if expected_out is None else expected_out
+    _need(total, "total_out", (1,), (torch.int32,), dev)
+    _need(expected, "expected_out", (1,), (torch.float64,), dev)
+    _check(lib().dspark_schedule_batch(_ptr(c), B, k, _ptr(verify_ms), verify_ms.numel(), _ptr(n), _ptr(total),
+                                       _ptr(expected), _stream(dev)))
+    return n, total, expected
+
+
+class CostTable:
+    """Online verify-cost table: boot curve + live medians of timed verify steps.
+
+    Bracket each pure verify step with ``begin(num_tokens)`` / ``end()`` on the
+    stream it runs on; completed timings are read back by ``poll()`` (or the next
+    ``begin``) without waiting on the GPU.
+    """
+
+    def __init__(self, boot_ms, window: int = 32, min_samples: int = 3, rebuild_every: int = 32):
+        boot = [float(x) for x in boot_ms]
+        arr = (ctypes.c_float * len(boot))(*boot)
+        h = ctypes.c_void_p()
+        self._h = None
+        _check(lib().dspark_cost_table_create(ctypes.cast(arr, ctypes.c_void_p), len(boot), window, min_samples,
+                                              rebuild_every, ctypes.byref(h)))
+        self._h = h
+        self.n = len(boot)
+
+    def __del__(self):
+        if getattr(self, "_h", None) is not None and _lib is not None:
+            _lib.dspark_cost_table_destroy(self._h)
+            self._h = None
+
+    def begin(self, num_tokens: int, stream=None) -> None:
+        st = torch.cuda.current_stream().cuda_stream if stream is None else stream.cuda_stream
+        _check(lib().dspark_cost_table_begin(self._h, int(num_tokens), st))
+
+    def end(self, stream=None) -> None:
+        st = torch.cuda.current_stream().cuda_stream if stream is None else stream.cuda_stream
+        _check(lib().dspark_cost_table_end(self._h, st))
+
+    def poll(self) -> int:
+        n = ctypes.c_int32(0)
+        _check(lib().dspark_cost_table_poll(self._h, ctypes.byref(n)))
+        return n.value
+
+    def observe(self, num_tokens: int, ms: float) -> None:
+        _check(lib().dspark_cost_table_observe(self._h, int(num_tokens), float(ms)))
+
+    def table(self):
+        import numpy as np
+        out = np.empty(self.n, dtype=np.float32)
+        _check(lib().dspark_cost_table_read(self._h, out.ctypes.data, self.n))
+        return out
+
+    def stats(self):
+        f, d, q = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int32(0)
+        _check(lib().dspark_cost_table_stats(self._h, ctypes.byref(f), ctypes.byref(d), ctypes.byref(q)))
+        return dict(filed=f.value, dropped=d.value, in_flight=q.value)
+
+    def log(self):
+        import numpy as np
+        cap = 65536
+        t = np.empty(cap, dtype=np.int32)
+        m = np.empty(cap, dtype=np.float32)
+        n = lib().dspark_cost_table_log(self._h, t.ctypes.data, m.ctypes.data, cap)
+        return t[:n].copy(), m[:n].copy()

@@ -8,7 +8,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", f) for f in ("api.hip", "kernels.hip")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("api.hip", "kernels.hip", "schedule.hip")]
 LIB = os.path.join(PKG, "libdspark_verify.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

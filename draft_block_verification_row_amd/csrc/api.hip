@@ -245,6 +245,7 @@ const char* dspark_status_string(dspark_status s) {
     case DSPARK_ERR_UNSUPPORTED: return "unsupported configuration";
     case DSPARK_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case DSPARK_ERR_HIP: return "HIP launch failed";
+    case DSPARK_ERR_NO_MEMORY: return "host allocation failed";
   }
   return "unknown status";
 }

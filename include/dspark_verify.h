@@ -18,6 +18,8 @@
  *   - The caller owns every buffer, including the workspace.  The library never
  *     allocates, frees or synchronises; all work is enqueued on `stream`
  *     (a hipStream_t; NULL means the default stream) and completes in order.
+ *     The one exception is the online cost table, a host object whose create
+ *     and destroy calls allocate and free host memory and HIP events.
  *   - Host-checkable errors return a status and enqueue nothing.  A failed
  *     launch returns DSPARK_ERR_HIP.  Device-data preconditions (token ids in
  *     range, temperatures >= 0, num_drafts in [0, k]) are the caller's: the
@@ -47,7 +49,8 @@ typedef enum {
   DSPARK_ERR_UNSUPPORTED = 2, /* valid but not implemented: rank R not in {32,64,128,256},
                                  W1/W2t not 16-byte aligned, or B > 4096 */
   DSPARK_ERR_WORKSPACE = 3,   /* workspace NULL, misaligned (256 B) or smaller than required */
-  DSPARK_ERR_HIP = 4          /* a HIP launch or device query failed */
+  DSPARK_ERR_HIP = 4,         /* a HIP launch or device query failed */
+  DSPARK_ERR_NO_MEMORY = 5    /* a host allocation of the cost table failed */
 } dspark_status;
 
 typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
@@ -206,6 +209,67 @@ dspark_status dspark_adaptive_k(const uint16_t* hidden, const uint16_t* w, float
                                 int32_t B, int32_t k, int32_t H,
                                 const float* verify_ms, int32_t n_ms,
                                 int32_t* n_out, float* c_out, float* a_out, void* stream);
+
+/*
+ * Batch-level draft scheduler [P2 §9 "Why It Is Called Prefix Survival
+ * Probability": candidates are added greedily in descending prefix survival and
+ * the low-confidence tail is cut once the expected accepted tokens stop paying;
+ * P3 "The controller, and the table it reads from": the cost of a verify pass is
+ * a table indexed by its token count].  With a_{b,j} = c_{b,0} ... c_{b,j}
+ * (fp64, multiplied left to right), the (b, j) pairs are ranked by descending a,
+ * ties by j then b, so every leading part of the ranking holds slots 0..n_b-1 of
+ * each stream b.  Taking the first m puts B + m tokens in the verify batch (n_b
+ * drafts plus each stream's own target position) and expects E(m) = B + the sum
+ * of their a, added one at a time in rank order.  The scheduler keeps the m in
+ * [0, B k] with the largest E(m) / verify_ms[B + m] (the smallest m on ties) and
+ * writes n_b, the count of stream b's slots among the first m.
+ * c: device fp32 [B, k], values in [0, 1] (for example c_out of dspark_adaptive_k);
+ * verify_ms: device fp32 [n_ms], positive, n_ms >= B (k + 1) + 1 (batch token
+ * counts B .. B (k + 1) are read); n_out: device int32 [B] (usable as num_drafts
+ * of dspark_verify_block); total_out: device int32 [1] = B + m, or NULL;
+ * expected_out: device fp64 [1] = E(m), or NULL.  One launch of one workgroup;
+ * B k > DSPARK_MAX_SCHEDULE returns DSPARK_ERR_UNSUPPORTED.
+ */
+#define DSPARK_MAX_SCHEDULE 4096
+dspark_status dspark_schedule_batch(const float* c, int32_t B, int32_t k, const float* verify_ms, int32_t n_ms,
+                                    int32_t* n_out, int32_t* total_out, double* expected_out, void* stream);
+
+/*
+ * Online verify-cost table [P3 "What we changed"].  The caller brackets each real
+ * verify step with begin (which records a start event on `stream` and notes the
+ * step's token count) and end (a stop event).  Completed pairs are read back
+ * later, by poll or the next begin, without ever waiting on the GPU, and filed
+ * under their token count; observe files a time measured elsewhere.  After every
+ * `rebuild_every` filed observations the served table becomes the boot table
+ * with, at each token count that holds at least `min_samples` of its last
+ * `window` observations, their median (the mean of the two middle values for an
+ * even count, rounded once to fp32).  An observation whose token count lies
+ * outside [0, n) is dropped; so is a step begun while DSPARK_COST_EVENTS pairs
+ * are still in flight.  Bracket only pure verify steps (drafts present, no
+ * prompt prefill in the batch) so that prefill cost stays out of the curve.
+ * The table is host state: create copies boot_ms (host fp32 [n], positive and
+ * finite; 1 <= min_samples <= window, rebuild_every >= 1); the event pairs are
+ * created on the current device at the first begin, and the table belongs to
+ * that device.  Not thread-safe.  read copies the first n served entries to host
+ * memory (upload them for dspark_schedule_batch or dspark_adaptive_k); stats
+ * reports the filed, dropped and in-flight counts; log copies up to `cap` of the
+ * first DSPARK_COST_LOG_MAX filed observations, in filing order, and returns how
+ * many it copied.
+ */
+#define DSPARK_COST_EVENTS 64
+#define DSPARK_COST_LOG_MAX 65536
+typedef struct dspark_cost_table dspark_cost_table;
+dspark_status dspark_cost_table_create(const float* boot_ms, int32_t n, int32_t window, int32_t min_samples,
+                                       int32_t rebuild_every, dspark_cost_table** out);
+void dspark_cost_table_destroy(dspark_cost_table* table);
+dspark_status dspark_cost_table_begin(dspark_cost_table* table, int32_t num_tokens, void* stream);
+dspark_status dspark_cost_table_end(dspark_cost_table* table, void* stream);
+dspark_status dspark_cost_table_poll(dspark_cost_table* table, int32_t* filed);
+dspark_status dspark_cost_table_observe(dspark_cost_table* table, int32_t num_tokens, float ms);
+dspark_status dspark_cost_table_read(const dspark_cost_table* table, float* out, int32_t n);
+dspark_status dspark_cost_table_stats(const dspark_cost_table* table, int64_t* filed, int64_t* dropped,
+                                      int32_t* in_flight);
+int32_t dspark_cost_table_log(const dspark_cost_table* table, int32_t* tokens, float* ms, int32_t cap);
 
 /* Static description of a status code. */
 const char* dspark_status_string(dspark_status status);

@@ -20,7 +20,10 @@ def _rng(seed):
 
 
 def _brute_force(a, ms):
-    """max over all n in [0, k]^B of (B + sum_b sum_{j<n_b} a[b, j]) / ms[B + sum n]."""
+    """max over all n in [0, k]^B of (B + sum_b sum_{j<n_b} a[b, j]) / ms[B + sum n].
+
+    Called with the rounded survivals (multiples of 2^-40): every such sum is exact
+    in fp64, so the optimum is compared for equality."""
     B, k = a.shape
     best = -1.0
     for n in itertools.product(range(k + 1), repeat=B):
@@ -46,11 +49,13 @@ def test_batch_schedule_matches_brute_force(B, k, seed):
             ms = g.uniform(1.0, 20.0, size=t.shape)                 # arbitrary positive table
         ms = ms.astype(np.float32)
         r = schedule.batch_schedule(c, ms)
-        bf = _brute_force(r["a"], ms)
-        assert abs(r["ratio"][r["m"]] - bf) <= 1e-12 * bf
+        aq = r["a_fixed"] / float(1 << schedule.FIXED_BITS)
+        assert np.all(np.abs(aq - r["a"]) <= 2.0 ** -41)
+        bf = _brute_force(aq, ms)
+        assert r["ratio"][r["m"]] == bf
         # the returned counts realise that optimum
-        E = B + sum(float(np.sum(r["a"][b, :r["n"][b]])) for b in range(B))
-        assert abs(E / float(ms[B + int(r["n"].sum())]) - bf) <= 1e-12 * bf
+        E = B + sum(float(np.sum(aq[b, :r["n"][b]])) for b in range(B))
+        assert E / float(ms[B + int(r["n"].sum())]) == bf
         assert int(r["n"].sum()) == r["m"]
 
 
@@ -59,8 +64,7 @@ def test_greedy_order_takes_prefixes_of_each_stream():
     c = g.uniform(0.0, 1.0, size=(6, 5)).astype(np.float32)
     c[1, 2:] = 1.0
     c[2, 1] = 0.0
-    a = schedule.prefix_survival_rows(c)
-    order = schedule.greedy_order(a)
+    order = schedule.greedy_order(schedule.fixed_survival(schedule.prefix_survival_rows(c)))
     for m in range(len(order) + 1):
         taken = {}
         for (b, j) in order[:m]:
@@ -126,8 +130,8 @@ def test_marginal_price_threshold():
         alpha, beta = float(g.uniform(5, 40)), float(g.uniform(0.1, 1.5))
         ms = (alpha + beta * np.arange(B * (k + 1) + 1)).astype(np.float32).astype(np.float64)
         r = schedule.batch_schedule(c, ms)
-        a = r["a"]
-        order = schedule.greedy_order(a)
+        a = r["a_fixed"] / float(1 << schedule.FIXED_BITS)
+        order = schedule.greedy_order(r["a_fixed"])
         m = r["m"]
         if m > 0:
             b, j = order[m - 1]
@@ -135,6 +139,13 @@ def test_marginal_price_threshold():
         if m < len(order):
             b, j = order[m]
             assert a[b, j] <= (ms[B + m + 1] - ms[B + m]) * r["ratio"][m] * (1 + 1e-12)
+
+
+def test_fixed_survival_rounding():
+    """Multiples of 2^-40 stay put, half-units round to even, the range clips."""
+    u = 2.0 ** -40
+    a = np.array([0.0, 1.0, 3 * u, 2.5 * u, 3.5 * u, 1.5, -0.25, np.nan, 0.5])
+    assert schedule.fixed_survival(a).tolist() == [0, 1 << 40, 3, 2, 4, 1 << 40, 0, 0, 1 << 39]
 
 
 def test_schedule_rejects_short_table():
