@@ -510,38 +510,73 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_kernel(Args a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// scan: one workgroup per stream.
-// ---------------------------------------------------------------------------
-// Row normaliser from its group partials (group-major, `nrows` rows per group):
-// M = max m_g, log2 S = log2 sum s_g 2^((m_g - M) c).  One wave per row; each lane
-// loads 8 partials at a time, and the wave-uniform running max rescales the sums.
-__device__ __forceinline__ void row_norm(const float2* __restrict__ part, int row, int nrows, int ng, double c, int l,
-                                         float& M_out, double& l2s_out) {
-  float M = -INFINITY;
-  double S = 0.0;
-  for (int g0 = 0; g0 < ng; g0 += 512) {
-    float2 v[8];
+// Row normalisers from the group partials (m_g, s_g) of pass 1, NR rows per wave at
+// once so that all their loads are in flight together: M = max_g m_g and
+// S = sum_g s_g 2^((m_g - M) c), returned as (M, log2 S).  The exponent is formed in
+// fp64 and rounded once to fp32 for v_exp_f32; its rounding moves a term by a relative
+// |e| 2^-24 ln 2 and terms with large |e| are negligible, so S is within ~2e-7 relative,
+// summed in fp64.  NG <= 512 groups (V <= 131072) per pass of the loop.
+template <int NR>
+struct RowBatch {
+  float2 v[NR][8];
+};
+
+template <int NR>
+__device__ __forceinline__ void row_norm_load(RowBatch<NR>& rb, const float2* const (&part)[NR], const int (&row)[NR],
+                                              const int (&nrows)[NR], int g0, int ng, int l) {
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int g = g0 + l + 64 * i;
-      v[i] = g < ng ? part[(size_t)g * nrows + row] : make_float2(-INFINITY, 0.f);
+      rb.v[r][i] = part[r][(size_t)min(g, ng - 1) * nrows[r] + row[r]];
+      if (g >= ng) rb.v[r][i] = make_float2(-INFINITY, 0.f);
     }
-    float m = v[0].x;
+}
+
+template <int NR>
+__device__ __forceinline__ void row_norm_batch(const float2* const (&part)[NR], const int (&row)[NR],
+                                               const int (&nrows)[NR], int ng, double c, int l, RowBatch<NR>& rb,
+                                               float (&M_out)[NR], double (&l2s_out)[NR]) {
+  float M[NR];
+  double S[NR];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) m = fmaxf(m, v[i].x);
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    if (m > M) {
-      if (M != -INFINITY) S *= exp2(((double)M - (double)m) * c);
-      M = m;
+  for (int r = 0; r < NR; ++r) { M[r] = -INFINITY; S[r] = 0.0; }
+  for (int g0 = 0; g0 < ng; g0 += 512) {
+    if (g0 > 0) row_norm_load<NR>(rb, part, row, nrows, g0, ng, l);
+    float m[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      m[r] = rb.v[r][0].x;
+#pragma unroll
+      for (int i = 1; i < 8; ++i) m[r] = fmaxf(m[r], rb.v[r][i].x);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (v[i].x != -INFINITY) S += (double)v[i].y * exp2(((double)v[i].x - (double)M) * c);
+    for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) m[r] = fmaxf(m[r], __shfl_xor(m[r], off));
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      if (m[r] > M[r]) {
+        if (M[r] != -INFINITY) S[r] *= exp2(((double)M[r] - (double)m[r]) * c);
+        M[r] = m[r];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float e = (float)(((double)rb.v[r][i].x - (double)M[r]) * c);
+        S[r] += rb.v[r][i].x == -INFINITY ? 0.0 : (double)rb.v[r][i].y * (double)exp2f(e);
+      }
+    }
   }
-  S = wave_sum(S);
-  M_out = M;
-  l2s_out = log2(S);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+    for (int r = 0; r < NR; ++r) S[r] += __shfl_xor(S[r], off);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    M_out[r] = M[r];
+    l2s_out[r] = log2(S[r]);
+  }
 }
 
 // Temperature 0 [P1 §4 "Greedy is a different code path"]: a draft is kept iff it is
@@ -594,6 +629,8 @@ __device__ __forceinline__ void greedy_scan(const Args& a, int b, int gamma) {
   }
 }
 
+constexpr int kRowBatch = 3;   // row-statistics rows per wave in flight at once
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
   __shared__ float s_M[2 * kMaxK + 1];
@@ -615,6 +652,25 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
   const int NT = a.B * k1, ND = a.B * a.k;
   const size_t esz = DT == kBF16 ? 2 : 4;
   const int nrows = 2 * gamma + 1;
+
+  // the first batch of row-statistics loads goes out before the gathers below, so that
+  // both wait on memory together.  Row r < nrows: target rows 0..gamma, then draft rows
+  // 0..gamma-1; rows past nrows re-read the stream's first target row (ignored).
+  const float2* rpart[kRowBatch];
+  int rrow[kRowBatch], rn[kRowBatch];
+  auto row_setup = [&](int r0) {
+#pragma unroll
+    for (int i = 0; i < kRowBatch; ++i) {
+      const int r = r0 + w + kWaves * i;
+      const bool is_t = r <= gamma || r >= nrows;
+      rpart[i] = is_t ? a.ws.tpart : a.ws.dpart;
+      rrow[i] = r >= nrows ? b * k1 : (is_t ? b * k1 + r : b * a.k + (r - gamma - 1));
+      rn[i] = is_t ? NT : ND;
+    }
+  };
+  RowBatch<kRowBatch> rbatch;
+  row_setup(0);
+  row_norm_load<kRowBatch>(rbatch, rpart, rrow, rn, 0, a.NG, l);
 
   if (tid < gamma) s_u[tid] = accept_uniform(a.key0, a.key1, (uint32_t)b, (uint32_t)tid, a.step);
 
@@ -651,18 +707,25 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
     }
   }
 
-  // row normalisers, one wave per row
-  for (int r = w; r < nrows; r += kWaves) {
-    const bool is_t = r <= gamma;
-    const int row = is_t ? b * k1 + r : b * a.k + (r - gamma - 1);
-    float M;
-    double l2s;
-    row_norm(is_t ? a.ws.tpart : a.ws.dpart, row, is_t ? NT : ND, a.NG, c, l, M, l2s);
-    if (l == 0) {
-      s_M[r] = M;
-      s_l2s[r] = l2s;
-      if (is_t) { a.ws.tm[row] = M; a.ws.tl2s[row] = l2s; }
-      else { a.ws.dm[row] = M; a.ws.dl2s[row] = l2s; }
+  // row normalisers: rows w, w + 4, w + 8 of the first batch were loaded above; later
+  // batches (k > 5) load in turn
+  for (int r0 = 0; r0 < nrows; r0 += kRowBatch * kWaves) {
+    if (r0 > 0) {
+      row_setup(r0);
+      row_norm_load<kRowBatch>(rbatch, rpart, rrow, rn, 0, a.NG, l);
+    }
+    float M[kRowBatch];
+    double l2s[kRowBatch];
+    row_norm_batch<kRowBatch>(rpart, rrow, rn, a.NG, c, l, rbatch, M, l2s);
+#pragma unroll
+    for (int i = 0; i < kRowBatch; ++i) {
+      const int r = r0 + w + kWaves * i;
+      if (l == 0 && r < nrows) {
+        s_M[r] = M[i];
+        s_l2s[r] = l2s[i];
+        if (r <= gamma) { a.ws.tm[rrow[i]] = M[i]; a.ws.tl2s[rrow[i]] = l2s[i]; }
+        else { a.ws.dm[rrow[i]] = M[i]; a.ws.dl2s[rrow[i]] = l2s[i]; }
+      }
     }
   }
   __syncthreads();
@@ -866,28 +929,56 @@ __device__ void block_argmax(double& score, int& idx, double* rs, int* ri) {
   __syncthreads();
 }
 
-// Markov bias at one vocabulary id in fp64: sum_r W1[prev, r] W2t[v, r] (R = 32 KS).
+// Markov bias of the 256 ids of group gsel after one previous token, by the whole
+// workgroup: sum_r W1[prev, r] W2t[v, r] (R = 32 KS).  A row of W2t is 4 KS slices of
+// 16 bytes; lane l reads slice l mod 4KS of consecutive rows, so one wave instruction
+// covers 16 / KS whole rows, and dots it with the same slice of W1[prev] (each bf16
+// product is exact in fp32; v_dot2c_f32_bf16 adds two per instruction).  The slice
+// sums of a row meet in LDS (rows padded by one float against bank conflicts) and
+// thread t returns the bias of id 256 gsel + t.  The bias carries an absolute error of
+// a few 1e-9 for weights of the drafter's scale, as fine as the fp32 row statistics it
+// is combined with.  Contains a barrier: every thread of the workgroup must call it.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot8_bf16(const uint4& p, const uint4& q) {
+  float acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p.x), __builtin_bit_cast(bf16x2, q.x), 0.f,
+                                              false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p.y), __builtin_bit_cast(bf16x2, q.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p.z), __builtin_bit_cast(bf16x2, q.z), acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p.w), __builtin_bit_cast(bf16x2, q.w), acc, false);
+}
+
 template <int KS>
-__device__ __forceinline__ double bias_at(const Args& a, int prev, int v) {
-  const uint4* p1 = reinterpret_cast<const uint4*>(a.W1 + (size_t)prev * (32 * KS));
-  const uint4* p2 = reinterpret_cast<const uint4*>(a.W2t + (size_t)v * (32 * KS));
-  uint4 u[4 * KS], x[4 * KS];
+struct GroupBiasLds {
+  float part[kGroup * (4 * KS + 1)];
+};
+
+template <int KS>
+__device__ __forceinline__ float group_bias(const Args& a, int prev, int gsel, GroupBiasLds<KS>& sh) {
+  constexpr int SL = 4 * KS;                      // 16-byte slices per row
+  constexpr int RPI = 64 / SL;                    // rows per wave instruction
+  constexpr int NI = kGroup / kWaves / RPI;       // instructions per wave
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int sl = l % SL, ri = l / SL;
+  const uint4 w1 = *reinterpret_cast<const uint4*>(a.W1 + (size_t)prev * (32 * KS) + 8 * sl);
+  uint4 x[NI];
 #pragma unroll
-  for (int i = 0; i < 4 * KS; ++i) { u[i] = p1[i]; x[i] = p2[i]; }
-  double acc = 0.0;
-#pragma unroll
-  for (int i = 0; i < 4 * KS; ++i) {
-    const uint32_t wa[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
-    const uint32_t wb[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      acc += (double)bf16lo(wa[e]) * (double)bf16lo(wb[e]) + (double)bf16hi(wa[e]) * (double)bf16hi(wb[e]);
+  for (int n = 0; n < NI; ++n) {
+    const int v = min(gsel * kGroup + w * 64 + n * RPI + ri, a.V - 1);   // rows past V: ignored
+    x[n] = *reinterpret_cast<const uint4*>(a.W2t + (size_t)v * (32 * KS) + 8 * sl);
   }
+#pragma unroll
+  for (int n = 0; n < NI; ++n) sh.part[(w * 64 + n * RPI + ri) * (SL + 1) + sl] = dot8_bf16(w1, x[n]);
+  __syncthreads();
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < SL; ++e) acc += sh.part[tid * (SL + 1) + e];
   return acc;
 }
 
 template <int DT, int KS>
 __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
+  __shared__ GroupBiasLds<KS> gb;
   __shared__ double red[kWaves];
   __shared__ double rs[kWaves];
   __shared__ int ri[kWaves];
@@ -997,8 +1088,11 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
   block_argmax(best, gbest, rs, ri);
   const int gsel = gbest < NG ? gbest : 0;
 
-  // race inside the winning group, weights recomputed in fp64
+  // race inside the winning group, weights recomputed in fp64 (the Markov bias of the
+  // group's ids from one cooperative pass over their W2t rows)
   const int v = gsel * kGroup + tid;
+  const int prev = (!use_p && a.W1 != nullptr) ? draft_prev(a, b, s) : -1;
+  const float bias = prev >= 0 ? group_bias<KS>(a, prev, gsel, gb) : 0.f;
   double sc = -1.0;
   if (v < a.V) {
     const double E = race_clock(a.key0, a.key1, (uint32_t)b, (uint32_t)v, kPurposeRaceItem, a.step);
@@ -1007,9 +1101,8 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
     if (use_p) {
       wv = exp2((lt - Mt) * c);
     } else {
-      double d = load1<DT>(reinterpret_cast<const char*>(a.draft) + (size_t)dr * a.V * esz, v);
-      const int prev = a.W1 != nullptr ? draft_prev(a, b, s) : -1;
-      if (prev >= 0) d += bias_at<KS>(a, prev, v);
+      const double d = (double)load1<DT>(reinterpret_cast<const char*>(a.draft) + (size_t)dr * a.V * esz, v) +
+                       (double)bias;
       const double lpP = a.method == 1 ? a.ws.logP[tr] * kLog2e : 0.0;
       const double pv = exp2((lt - Mt) * c - a.ws.tl2s[tr] + lpP);
       const double qv = exp2((d - (double)a.ws.dm[dr]) * c - a.ws.dl2s[dr]);
@@ -1135,6 +1228,7 @@ __device__ void block_max_index(double& val, int& idx, double* rs, int* ri) {
 
 template <int DT, int KS>
 __global__ __launch_bounds__(kThreads) void walk_pick_kernel(Args a, int j, int32_t* tokens_out, double* logq_out) {
+  __shared__ GroupBiasLds<KS> gb;
   __shared__ double rs[kWaves];
   __shared__ int ri[kWaves];
   __shared__ double red[kWaves];
@@ -1173,12 +1267,13 @@ __global__ __launch_bounds__(kThreads) void walk_pick_kernel(Args a, int j, int3
   }
   block_max_index(best, gbest, rs, ri);
   const int gsel = gbest < NG ? gbest : 0;
-  // inside the group: biased logits in fp64
+  // inside the group: biased logits in fp64 (the Markov bias from one cooperative pass
+  // over the group's W2t rows)
   const int v = gsel * kGroup + tid;
+  const float bias = (a.W1 != nullptr && prev >= 0) ? group_bias<KS>(a, prev, gsel, gb) : 0.f;
   double xv = -INFINITY, sc = -INFINITY;
   if (v < a.V) {
-    xv = (double)load1<DT>(drow, v);
-    if (a.W1 != nullptr && prev >= 0) xv += bias_at<KS>(a, prev, v);
+    xv = (double)load1<DT>(drow, v) + (double)bias;
     sc = greedy ? xv
                 : xv * invT - log(race_clock(a.key0, a.key1, (uint32_t)b, (uint32_t)v, walk_purpose_item(j), a.step));
   }
