@@ -146,6 +146,8 @@ struct Workspace {
   Item* items;        // [B*k]         compact pass-2 list
   int32_t* nitems;    // [1]
   uint4* btile;       // [ceil(B*k/16)][R/32][64] W1 tiles in MFMA lane order (pass 1, then pass 2)
+  double* glt;        // [B*k]         target logit at the draft token, t_j(x_j)
+  double* gld;        // [B*k]         biased draft logit at the draft token, d_j(x_j) + bias (fp64)
 };
 
 struct Args {

@@ -218,30 +218,67 @@ __device__ __forceinline__ float2 row_partial(const float (&x)[16], float c) {
 __device__ __forceinline__ int div_small(int i, float hd) { return (int)((float)(2 * i + 1) * hd); }
 
 // ---------------------------------------------------------------------------
-// pack: W1 tiles in MFMA lane order.  Tile c, k-step kk, lane l holds
-// W1[prev(16c + l%16)][32kk + 8(l/16) .. +8] (zero for a row without bias or an
-// inactive row).  One wave per tile; the first also clears the pass-2 row count.
+// pack: one wave per 16 draft rows (lane n + 16 q: row n, quarter q of each k-step).
+// (1) The W1 rows of the rows' previous tokens go into `btile` in MFMA lane order, so
+// that pass 1 reads a k-step of 16 rows as one contiguous 1 KB load.  (2) The logits
+// at each row's draft token: the target's t_j(x_j) and the drafter's d_j(x_j) plus
+// the Markov bias W1[prev] . W2t[x_j], summed in fp64 (each lane a quarter of the
+// rank, then the 4 lanes of the row), for the scan's log p_j(x_j) and log q_j(x_j).
+// Also clears the pass-2 list count.
 // ---------------------------------------------------------------------------
+template <int DT>
 __global__ __launch_bounds__(64) void pack_kernel(Args a) {
   const int c = blockIdx.x, l = threadIdx.x, n = l & 15, q = l >> 4;
   if (c == 0 && l == 0) *a.ws.nitems = 0;
-  if (a.W1 == nullptr) return;
-  const int dr = c * kChunk + n;
-  int prev = -1;
-  if (dr < a.B * a.k) {
-    const int b = dr / a.k, j = dr - b * a.k;
-    if (j < stream_gamma(a, b)) prev = draft_prev(a, b, j);
+  const int ND = a.B * a.k;
+  const int dr = c * kChunk + n, drc = min(dr, ND - 1);
+  const int b = drc / a.k, j = drc - b * a.k;
+  // the three small loads go out together; the row loads below depend only on them
+  const int gam = stream_gamma(a, b);
+  const int pv = a.W1 != nullptr ? draft_prev(a, b, j) : -1;
+  const int x = clamp_tok(a.tokens[drc], a.V);
+  const bool act = dr < ND && j < gam;
+  const size_t esz = DT == kBF16 ? 2 : 4;
+  double lt = 0.0, ld = 0.0;
+  if (q == 0) {
+    lt = load1<DT>(reinterpret_cast<const char*>(a.target) + (size_t)(b * (a.k + 1) + j) * a.V * esz, x);
+    ld = load1<DT>(reinterpret_cast<const char*>(a.draft) + (size_t)drc * a.V * esz, x);
   }
-  const int ks = a.R / 32;   // <= 8
-  uint4 v[8];
+  double bias = 0.0;
+  if (a.W1 != nullptr) {
+    const int ks = a.R / 32;   // <= 8
+    const bool use = act && pv >= 0;
+    uint4 v[8], y[8];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-    v[kk] = (kk < ks && prev >= 0) ? *reinterpret_cast<const uint4*>(a.W1 + (size_t)prev * a.R + kk * 32 + 8 * q)
-                                   : make_uint4(0, 0, 0, 0);
-  uint4* dst = a.ws.btile + (size_t)c * ks * 64 + l;
+    for (int kk = 0; kk < 8; ++kk) {   // unconditional loads (clamped row), masked after
+      const int kc = kk < ks ? kk : 0;
+      v[kk] = *reinterpret_cast<const uint4*>(a.W1 + (size_t)max(pv, 0) * a.R + kc * 32 + 8 * q);
+      y[kk] = *reinterpret_cast<const uint4*>(a.W2t + (size_t)x * a.R + kc * 32 + 8 * q);
+    }
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-    if (kk < ks) dst[kk * 64] = v[kk];
+    for (int kk = 0; kk < 8; ++kk)
+      if (!use || kk >= ks) v[kk] = make_uint4(0, 0, 0, 0);
+    uint4* dst = a.ws.btile + (size_t)c * ks * 64 + l;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      if (kk < ks) dst[kk * 64] = v[kk];
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const uint32_t wa[4] = {v[kk].x, v[kk].y, v[kk].z, v[kk].w};
+      const uint32_t wb[4] = {y[kk].x, y[kk].y, y[kk].z, y[kk].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[i] += (double)bf16lo(wa[i]) * (double)bf16lo(wb[i]) + (double)bf16hi(wa[i]) * (double)bf16hi(wb[i]);
+    }
+    bias = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    bias += __shfl_xor(bias, 16);
+    bias += __shfl_xor(bias, 32);
+  }
+  if (q == 0 && act) {
+    a.ws.glt[dr] = lt;
+    a.ws.gld[dr] = ld + bias;
+  }
 }
 
 // One k-step slice of a packed tile per lane: the B operand of 16 rows.
@@ -510,72 +547,79 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_kernel(Args a) {
   }
 }
 
-// Row normalisers from the group partials (m_g, s_g) of pass 1, NR rows per wave at
-// once so that all their loads are in flight together: M = max_g m_g and
-// S = sum_g s_g 2^((m_g - M) c), returned as (M, log2 S).  The exponent is formed in
-// fp64 and rounded once to fp32 for v_exp_f32; its rounding moves a term by a relative
-// |e| 2^-24 ln 2 and terms with large |e| are negligible, so S is within ~2e-7 relative,
-// summed in fp64.  NG <= 512 groups (V <= 131072) per pass of the loop.
-template <int NR>
-struct RowBatch {
-  float2 v[NR][8];
+// Row normalisers from the group partials (m_g, s_g) of pass 1: M = max_g m_g and
+// S = sum_g s_g 2^((m_g - M) c), returned as (M, log2 S).  A stream's partials of one
+// group are contiguous (its target rows, then, in the other buffer, its draft rows),
+// so the workgroup first copies up to 6 target and 6 draft rows of 512 groups into
+// LDS, row-major, with consecutive lanes on consecutive 8-byte words (a wave
+// instruction touches ~11 groups' worth of lines instead of 64); then each wave
+// reduces 3 rows from LDS.  The exponent is formed in fp64 and rounded once to fp32
+// for v_exp_f32; its rounding moves a term by a relative |e| 2^-24 ln 2 and terms
+// with large |e| are negligible, so S is within ~2e-7 relative, summed in fp64.
+constexpr int kScanRows = 6;                               // target (and draft) rows per pass
+constexpr int kScanGroups = 512;                           // groups per pass
+constexpr int kStageIter = kScanRows * kScanGroups / kThreads;
+struct ScanLds {
+  float2 t[kScanRows][kScanGroups + 1];   // +1: stores of one instruction spread over banks
+  float2 d[kScanRows][kScanGroups + 1];
+};
+struct StageRegs {
+  float2 t[kStageIter], d[kStageIter];
 };
 
-template <int NR>
-__device__ __forceinline__ void row_norm_load(RowBatch<NR>& rb, const float2* const (&part)[NR], const int (&row)[NR],
-                                              const int (&nrows)[NR], int g0, int ng, int l) {
+// Loads rows [r0, r0 + nt) of the stream's target partials and [r0, r0 + nd) of its
+// draft partials for groups [g0, g0 + ng); element e = tid + 256 i is group e / 6,
+// row e % 6.  Rows or groups past the range re-read a valid word (ignored).
+__device__ __forceinline__ void stage_load(StageRegs& sr, const Args& a, int b, int r0, int nt, int nd, int g0,
+                                           int ng, int tid) {
+  const int k1 = a.k + 1, NT = a.B * k1, ND = a.B * a.k;
 #pragma unroll
-  for (int r = 0; r < NR; ++r)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int g = g0 + l + 64 * i;
-      rb.v[r][i] = part[r][(size_t)min(g, ng - 1) * nrows[r] + row[r]];
-      if (g >= ng) rb.v[r][i] = make_float2(-INFINITY, 0.f);
-    }
+  for (int i = 0; i < kStageIter; ++i) {
+    const int e = tid + kThreads * i;
+    const int gl = min(e / kScanRows, ng - 1), r = e % kScanRows;
+    const size_t gg = (size_t)(g0 + gl);
+    sr.t[i] = a.ws.tpart[gg * NT + b * k1 + r0 + (r < nt ? r : 0)];
+    sr.d[i] = a.ws.dpart[gg * ND + b * a.k + min(r0 + (r < nd ? r : 0), a.k - 1)];
+  }
 }
 
-template <int NR>
-__device__ __forceinline__ void row_norm_batch(const float2* const (&part)[NR], const int (&row)[NR],
-                                               const int (&nrows)[NR], int ng, double c, int l, RowBatch<NR>& rb,
-                                               float (&M_out)[NR], double (&l2s_out)[NR]) {
-  float M[NR];
-  double S[NR];
+__device__ __forceinline__ void stage_store(const StageRegs& sr, ScanLds& sh, int tid) {
 #pragma unroll
-  for (int r = 0; r < NR; ++r) { M[r] = -INFINITY; S[r] = 0.0; }
-  for (int g0 = 0; g0 < ng; g0 += 512) {
-    if (g0 > 0) row_norm_load<NR>(rb, part, row, nrows, g0, ng, l);
-    float m[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      m[r] = rb.v[r][0].x;
-#pragma unroll
-      for (int i = 1; i < 8; ++i) m[r] = fmaxf(m[r], rb.v[r][i].x);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-#pragma unroll
-      for (int r = 0; r < NR; ++r) m[r] = fmaxf(m[r], __shfl_xor(m[r], off));
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      if (m[r] > M[r]) {
-        if (M[r] != -INFINITY) S[r] *= exp2(((double)M[r] - (double)m[r]) * c);
-        M[r] = m[r];
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float e = (float)(((double)rb.v[r][i].x - (double)M[r]) * c);
-        S[r] += rb.v[r][i].x == -INFINITY ? 0.0 : (double)rb.v[r][i].y * (double)exp2f(e);
-      }
-    }
+  for (int i = 0; i < kStageIter; ++i) {
+    const int e = tid + kThreads * i;
+    const int gl = e / kScanRows, r = e % kScanRows;
+    sh.t[r][gl] = sr.t[i];
+    sh.d[r][gl] = sr.d[i];
   }
+}
+
+// One pass of groups [g0, g0 + ng) over the 3 LDS rows of this wave (slot q: row
+// w + 4q of the 12, target rows first), folded into the running (M, S) of each.
+__device__ __forceinline__ void stage_reduce(const ScanLds& sh, int w, int l, int ng, double c, float (&M)[3],
+                                             double (&S)[3]) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1)
+  for (int q = 0; q < 3; ++q) {
+    const int slot = w + kWaves * q;
+    const float2* row = slot < kScanRows ? sh.t[slot] : sh.d[slot - kScanRows];
+    float2 v[8];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) S[r] += __shfl_xor(S[r], off);
+    for (int i = 0; i < 8; ++i) {
+      const int g = l + 64 * i;
+      v[i] = g < ng ? row[g] : make_float2(-INFINITY, 0.f);
+    }
+    float m = v[0].x;
 #pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    M_out[r] = M[r];
-    l2s_out[r] = log2(S[r]);
+    for (int i = 1; i < 8; ++i) m = fmaxf(m, v[i].x);
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (m > M[q]) {
+      if (M[q] != -INFINITY) S[q] *= exp2(((double)M[q] - (double)m) * c);
+      M[q] = m;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float e = (float)(((double)v[i].x - (double)M[q]) * c);
+      S[q] += v[i].x == -INFINITY ? 0.0 : (double)v[i].y * (double)exp2f(e);
+    }
   }
 }
 
@@ -629,10 +673,9 @@ __device__ __forceinline__ void greedy_scan(const Args& a, int b, int gamma) {
   }
 }
 
-constexpr int kRowBatch = 3;   // row-statistics rows per wave in flight at once
-
 template <int DT>
 __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
+  __shared__ ScanLds sh;
   __shared__ float s_M[2 * kMaxK + 1];
   __shared__ double s_l2s[2 * kMaxK + 1];
   __shared__ double s_lt[kMaxK], s_ld[kMaxK], s_u[kMaxK], s_lr[kMaxK], s_lp[kMaxK + 1];
@@ -651,80 +694,51 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
   const int k1 = a.k + 1;
   const int NT = a.B * k1, ND = a.B * a.k;
   const size_t esz = DT == kBF16 ? 2 : 4;
-  const int nrows = 2 * gamma + 1;
 
-  // the first batch of row-statistics loads goes out before the gathers below, so that
-  // both wait on memory together.  Row r < nrows: target rows 0..gamma, then draft rows
-  // 0..gamma-1; rows past nrows re-read the stream's first target row (ignored).
-  const float2* rpart[kRowBatch];
-  int rrow[kRowBatch], rn[kRowBatch];
-  auto row_setup = [&](int r0) {
-#pragma unroll
-    for (int i = 0; i < kRowBatch; ++i) {
-      const int r = r0 + w + kWaves * i;
-      const bool is_t = r <= gamma || r >= nrows;
-      rpart[i] = is_t ? a.ws.tpart : a.ws.dpart;
-      rrow[i] = r >= nrows ? b * k1 : (is_t ? b * k1 + r : b * a.k + (r - gamma - 1));
-      rn[i] = is_t ? NT : ND;
-    }
-  };
-  RowBatch<kRowBatch> rbatch;
-  row_setup(0);
-  row_norm_load<kRowBatch>(rbatch, rpart, rrow, rn, 0, a.NG, l);
+  // the first row-statistics loads go out before the gathers below, so that both wait
+  // on memory together
+  const int ngp = min(a.NG, kScanGroups);
+  StageRegs sreg;
+  stage_load(sreg, a, b, 0, min(kScanRows, gamma + 1), min(kScanRows, gamma), 0, ngp, tid);
 
   if (tid < gamma) s_u[tid] = accept_uniform(a.key0, a.key1, (uint32_t)b, (uint32_t)tid, a.step);
 
-  // gathered logits at the drafts, 16 lanes per slot; the bias dot product in fp64
-  for (int j0 = 0; j0 < gamma; j0 += kThreads / 16) {
-    const int j = j0 + (tid >> 4), l16 = tid & 15;
-    double bias = 0.0;
-    double lt = 0.0, ld = 0.0;
-    if (j < gamma) {
-      const int x = clamp_tok(a.tokens[b * a.k + j], a.V);
-      const int tr = b * k1 + j, dr = b * a.k + j;
-      if (l16 == 0) {
-        lt = load1<DT>(reinterpret_cast<const char*>(a.target) + (size_t)tr * a.V * esz, x);
-        ld = load1<DT>(reinterpret_cast<const char*>(a.draft) + (size_t)dr * a.V * esz, x);
-      }
-      const int prev = a.W1 != nullptr ? draft_prev(a, b, j) : -1;
-      if (prev >= 0) {
-        for (int r = 16 * l16; r < a.R; r += 256) {
-          const uint4* p1 = reinterpret_cast<const uint4*>(a.W1 + (size_t)prev * a.R + r);
-          const uint4* p2 = reinterpret_cast<const uint4*>(a.W2t + (size_t)x * a.R + r);
-          const uint4 u0 = p1[0], u1 = p1[1], v0 = p2[0], v1 = p2[1];
-          const uint32_t wa[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-          const uint32_t wb[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            bias += (double)bf16lo(wa[i]) * (double)bf16lo(wb[i]) + (double)bf16hi(wa[i]) * (double)bf16hi(wb[i]);
-        }
-      }
-    }
-    for (int off = 8; off >= 1; off >>= 1) bias += __shfl_xor(bias, off);
-    if (j < gamma && l16 == 0) {
-      s_lt[j] = lt;
-      s_ld[j] = ld + bias;
-    }
+  // the logits at the drafts, gathered by the pack launch
+  if (tid < gamma) {
+    s_lt[tid] = a.ws.glt[b * a.k + tid];
+    s_ld[tid] = a.ws.gld[b * a.k + tid];
   }
 
-  // row normalisers: rows w, w + 4, w + 8 of the first batch were loaded above; later
-  // batches (k > 5) load in turn
-  for (int r0 = 0; r0 < nrows; r0 += kRowBatch * kWaves) {
-    if (r0 > 0) {
-      row_setup(r0);
-      row_norm_load<kRowBatch>(rbatch, rpart, rrow, rn, 0, a.NG, l);
+  // row normalisers: passes of 6 target and 6 draft rows (the first pass's loads were
+  // issued above), each over groups in runs of 512 staged through LDS
+  for (int r0 = 0; r0 <= gamma; r0 += kScanRows) {
+    const int nt = min(kScanRows, gamma + 1 - r0), nd = max(0, min(kScanRows, gamma - r0));
+    float M[3] = {-INFINITY, -INFINITY, -INFINITY};
+    double S[3] = {0.0, 0.0, 0.0};
+    for (int g0 = 0; g0 < a.NG; g0 += kScanGroups) {
+      const int ng = min(kScanGroups, a.NG - g0);
+      if (r0 > 0 || g0 > 0) stage_load(sreg, a, b, r0, nt, nd, g0, ng, tid);
+      __syncthreads();   // the previous pass's readers are done with the LDS rows
+      stage_store(sreg, sh, tid);
+      __syncthreads();
+      stage_reduce(sh, w, l, ng, c, M, S);
     }
-    float M[kRowBatch];
-    double l2s[kRowBatch];
-    row_norm_batch<kRowBatch>(rpart, rrow, rn, a.NG, c, l, rbatch, M, l2s);
 #pragma unroll
-    for (int i = 0; i < kRowBatch; ++i) {
-      const int r = r0 + w + kWaves * i;
-      if (l == 0 && r < nrows) {
-        s_M[r] = M[i];
-        s_l2s[r] = l2s[i];
-        if (r <= gamma) { a.ws.tm[rrow[i]] = M[i]; a.ws.tl2s[rrow[i]] = l2s[i]; }
-        else { a.ws.dm[rrow[i]] = M[i]; a.ws.dl2s[rrow[i]] = l2s[i]; }
+    for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+      for (int q = 0; q < 3; ++q) S[q] += __shfl_xor(S[q], off);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int slot = w + kWaves * q;
+      const bool is_t = slot < kScanRows;
+      const int j = r0 + (is_t ? slot : slot - kScanRows);   // slot within the stream
+      if (l == 0 && (is_t ? j <= gamma : j < gamma)) {
+        const int r = is_t ? j : gamma + 1 + j;                 // index into s_M / s_l2s
+        const double l2s = log2(S[q]);
+        s_M[r] = M[q];
+        s_l2s[r] = l2s;
+        if (is_t) { a.ws.tm[b * k1 + j] = M[q]; a.ws.tl2s[b * k1 + j] = l2s; }
+        else { a.ws.dm[b * a.k + j] = M[q]; a.ws.dl2s[b * a.k + j] = l2s; }
       }
     }
   }
@@ -1434,7 +1448,7 @@ static hipError_t launch_passes(const Args& a, hipStream_t st, void* const* ev) 
   };
   const int nchd = (a.B * a.k + kChunk - 1) / kChunk;
   mark(0);
-  hipLaunchKernelGGL(pack_kernel, dim3(nchd), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((pack_kernel<DT>), dim3(nchd), dim3(64), 0, st, a);
   mark(1);
   hipLaunchKernelGGL((pass1_kernel<DT, KS, MARKOV, VEC>), dim3(a.NG), dim3(kThreads), stream_table_bytes(a.B), st, a);
   mark(2);
