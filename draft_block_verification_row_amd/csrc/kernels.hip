@@ -122,9 +122,68 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dppf<0x140>(v);
   return v;
 }
+// Whole-wave reductions on VALU lane moves only (every lane gets the result): DPP
+// within rows of 16 (xor 1, xor 2, half-row mirror, row mirror), then the gfx950 row
+// swaps (permlane16_swap, permlane32_swap) across the four rows.
+__device__ __forceinline__ float wave_max_dpp(float v) { return max4lanes(row16_max(v)); }
+template <int CTRL>
+__device__ __forceinline__ double dppd(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+template <int CTRL>
+__device__ __forceinline__ int dppi(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ double swap_sum16(double v) {
+  const auto lo = __builtin_amdgcn_permlane16_swap(__double2loint(v), __double2loint(v), false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap(__double2hiint(v), __double2hiint(v), false, false);
+  return __hiloint2double(hi[0], lo[0]) + __hiloint2double(hi[1], lo[1]);
+}
+__device__ __forceinline__ double swap_sum32(double v) {
+  const auto lo = __builtin_amdgcn_permlane32_swap(__double2loint(v), __double2loint(v), false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap(__double2hiint(v), __double2hiint(v), false, false);
+  return __hiloint2double(hi[0], lo[0]) + __hiloint2double(hi[1], lo[1]);
+}
 __device__ __forceinline__ double wave_sum(double v) {
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v += dppd<0xB1>(v);
+  v += dppd<0x4E>(v);
+  v += dppd<0x141>(v);
+  v += dppd<0x140>(v);
+  return swap_sum32(swap_sum16(v));
+}
+// (score, index) arg-max over the wave: larger score, then smaller index.
+__device__ __forceinline__ void take_better(double& s, int& i, double os, int oi) {
+  if (os > s || (os == s && oi < i)) { s = os; i = oi; }
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(double& s, int& i) {
+  const double os = dppd<CTRL>(s);
+  const int oi = dppi<CTRL>(i);
+  take_better(s, i, os, oi);
+}
+__device__ __forceinline__ void wave_argmax(double& s, int& i) {
+  argmax_step<0xB1>(s, i);
+  argmax_step<0x4E>(s, i);
+  argmax_step<0x141>(s, i);
+  argmax_step<0x140>(s, i);
+  {
+    const auto lo = __builtin_amdgcn_permlane16_swap(__double2loint(s), __double2loint(s), false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap(__double2hiint(s), __double2hiint(s), false, false);
+    const auto ix = __builtin_amdgcn_permlane16_swap(i, i, false, false);
+    s = __hiloint2double(hi[0], lo[0]);
+    i = ix[0];
+    take_better(s, i, __hiloint2double(hi[1], lo[1]), ix[1]);
+  }
+  {
+    const auto lo = __builtin_amdgcn_permlane32_swap(__double2loint(s), __double2loint(s), false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap(__double2hiint(s), __double2hiint(s), false, false);
+    const auto ix = __builtin_amdgcn_permlane32_swap(i, i, false, false);
+    s = __hiloint2double(hi[0], lo[0]);
+    i = ix[0];
+    take_better(s, i, __hiloint2double(hi[1], lo[1]), ix[1]);
+  }
 }
 
 // 16 logits kept packed until use: bf16 as 8 words, fp32 as 16 floats.
@@ -553,9 +612,9 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_kernel(Args a) {
 // so the workgroup first copies up to 6 target and 6 draft rows of 512 groups into
 // LDS, row-major, with consecutive lanes on consecutive 8-byte words (a wave
 // instruction touches ~11 groups' worth of lines instead of 64); then each wave
-// reduces 3 rows from LDS.  The exponent is formed in fp64 and rounded once to fp32
-// for v_exp_f32; its rounding moves a term by a relative |e| 2^-24 ln 2 and terms
-// with large |e| are negligible, so S is within ~2e-7 relative, summed in fp64.
+// reduces 3 rows from LDS.  The terms use pass 1's fp32 c and its three-operation
+// exponent (M c split into hi + lo exactly), so each moves by a relative
+// (m_g - M) c 2^-24 at most and S is within ~2e-7 relative, summed in fp64.
 constexpr int kScanRows = 6;                               // target (and draft) rows per pass
 constexpr int kScanGroups = 512;                           // groups per pass
 constexpr int kStageIter = kScanRows * kScanGroups / kThreads;
@@ -594,32 +653,42 @@ __device__ __forceinline__ void stage_store(const StageRegs& sr, ScanLds& sh, in
 }
 
 // One pass of groups [g0, g0 + ng) over the 3 LDS rows of this wave (slot q: row
-// w + 4q of the 12, target rows first), folded into the running (M, S) of each.
+// w + 4q of the 12, target rows first), folded into the running (M, S) of each.  The
+// three rows go through each step together so that their latencies overlap.
 __device__ __forceinline__ void stage_reduce(const ScanLds& sh, int w, int l, int ng, double c, float (&M)[3],
                                              double (&S)[3]) {
+  float2 v[3][8];
+  float m[3];
 #pragma unroll
   for (int q = 0; q < 3; ++q) {
     const int slot = w + kWaves * q;
     const float2* row = slot < kScanRows ? sh.t[slot] : sh.d[slot - kScanRows];
-    float2 v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int g = l + 64 * i;
-      v[i] = g < ng ? row[g] : make_float2(-INFINITY, 0.f);
+      v[q][i] = g < ng ? row[g] : make_float2(-INFINITY, 0.f);
     }
-    float m = v[0].x;
+    m[q] = v[q][0].x;
 #pragma unroll
-    for (int i = 1; i < 8; ++i) m = fmaxf(m, v[i].x);
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    if (m > M[q]) {
-      if (M[q] != -INFINITY) S[q] *= exp2(((double)M[q] - (double)m) * c);
-      M[q] = m;
-    }
+    for (int i = 1; i < 8; ++i) m[q] = fmaxf(m[q], v[q][i].x);
+  }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float e = (float)(((double)v[i].x - (double)M[q]) * c);
-      S[q] += v[i].x == -INFINITY ? 0.0 : (double)v[i].y * (double)exp2f(e);
+  for (int q = 0; q < 3; ++q) m[q] = wave_max_dpp(m[q]);
+  const float cf = (float)c;   // log2(e) / T in fp32, as pass 1 used inside each group
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    if (m[q] > M[q]) {
+      if (M[q] != -INFINITY) S[q] *= exp2(((double)M[q] - (double)m[q]) * c);
+      M[q] = m[q];
     }
+    // 2^((m_g - M) cf) as 2^(fma(m_g, cf, -mh)) 2^(-ml) with M cf = mh + ml exactly;
+    // an empty group (m_g = -inf, s_g = 0) adds 0
+    const float mh = M[q] * cf, ml = fmaf(M[q], cf, -mh);
+    double part = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      part += (double)v[q][i].y * (double)__builtin_amdgcn_exp2f(fmaf(v[q][i].x, cf, -mh));
+    S[q] += part * (double)__builtin_amdgcn_exp2f(-ml);
   }
 }
 
@@ -679,6 +748,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
   __shared__ float s_M[2 * kMaxK + 1];
   __shared__ double s_l2s[2 * kMaxK + 1];
   __shared__ double s_lt[kMaxK], s_ld[kMaxK], s_u[kMaxK], s_lr[kMaxK], s_lp[kMaxK + 1];
+  __shared__ double s_thr[kMaxK], s_eP[kMaxK + 1];
   __shared__ int s_base;
   __shared__ uint32_t s_mask;
   const int b = blockIdx.x;
@@ -724,17 +794,16 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
       stage_reduce(sh, w, l, ng, c, M, S);
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-#pragma unroll
-      for (int q = 0; q < 3; ++q) S[q] += __shfl_xor(S[q], off);
+    for (int q = 0; q < 3; ++q) S[q] = wave_sum(S[q]);
+    // one log2 per wave: lane q takes row q
+    const double l2s = log2(l == 0 ? S[0] : (l == 1 ? S[1] : S[2]));
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
       const int slot = w + kWaves * q;
       const bool is_t = slot < kScanRows;
       const int j = r0 + (is_t ? slot : slot - kScanRows);   // slot within the stream
-      if (l == 0 && (is_t ? j <= gamma : j < gamma)) {
+      if (l == q && (is_t ? j <= gamma : j < gamma)) {
         const int r = is_t ? j : gamma + 1 + j;                 // index into s_M / s_l2s
-        const double l2s = log2(S[q]);
         s_M[r] = M[q];
         s_l2s[r] = l2s;
         if (is_t) { a.ws.tm[b * k1 + j] = M[q]; a.ws.tl2s[b * k1 + j] = l2s; }
@@ -752,34 +821,38 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
     a.ws.lpx[b * a.k + j] = lpx;
     a.ws.lqx[b * a.k + j] = lqx;
     s_lr[j] = lpx - lqx;
+    s_thr[j] = s_lr[j] >= 0.0 ? 1.0 : exp(s_lr[j]);   // token-wise threshold min(1, r_j)
+  }
+  __syncthreads();
+  // clipped prefix log P_i (each slot recomputes it, in the same order) and P_i itself
+  if (tid <= gamma) {
+    double lp = 0.0;
+    for (int i = 1; i <= tid; ++i) {
+      const double v = lp + s_lr[i - 1];
+      lp = v < 0.0 ? v : 0.0;
+    }
+    s_lp[tid] = lp;
+    s_eP[tid] = exp(lp);
   }
   __syncthreads();
   if (tid == 0) {
     // token-wise stop t: first j with u_j > min(1, r_j)
     int t = gamma;
-    for (int j = 0; j < gamma; ++j) {
-      const double thr = s_lr[j] >= 0.0 ? 1.0 : exp(s_lr[j]);
-      if (!(s_u[j] <= thr)) { t = j; break; }
-    }
-    // clipped prefix log P_i
-    s_lp[0] = 0.0;
-    for (int i = 1; i <= gamma; ++i) {
-      const double v = s_lp[i - 1] + s_lr[i - 1];
-      s_lp[i] = v < 0.0 ? v : 0.0;
-    }
+    for (int j = 0; j < gamma; ++j)
+      if (!(s_u[j] <= s_thr[j])) { t = j; break; }
     uint32_t mask = 0;
     int stop = 0, f = 0;
     if (a.method == 0) {
       stop = t;
       if (t < gamma) mask = 1u << t;
     } else {
-      if (gamma == 0 || s_u[gamma - 1] <= exp(s_lp[gamma])) {
+      if (gamma == 0 || s_u[gamma - 1] <= s_eP[gamma]) {
         stop = gamma;   // top test passed (or no drafts): tau = gamma
       } else {
         for (int i = gamma - 1; i >= 0; --i) if (s_lp[i] == 0.0) { f = i; break; }
         mask = 1u << f;  // tau >= f; row f may be sampled
         for (int i = f + 1; i < gamma; ++i)
-          if (s_u[i - 1] <= exp(s_lp[i])) mask |= 1u << i;   // h_i <= P_i: only these can pass
+          if (s_u[i - 1] <= s_eP[i]) mask |= 1u << i;   // h_i <= P_i: only these can pass
         stop = -1;
       }
     }
@@ -930,16 +1003,11 @@ __device__ double block_sum(double v, double* red) {
 // Arg-max of score with the lowest index on ties; score < 0 means "not a contestant".
 __device__ void block_argmax(double& score, int& idx, double* rs, int* ri) {
   const int tid = threadIdx.x;
-  for (int off = 32; off >= 1; off >>= 1) {
-    const double os = __shfl_xor(score, off);
-    const int oi = __shfl_xor(idx, off);
-    if (os > score || (os == score && oi < idx)) { score = os; idx = oi; }
-  }
+  wave_argmax(score, idx);
   if ((tid & 63) == 0) { rs[tid >> 6] = score; ri[tid >> 6] = idx; }
   __syncthreads();
   score = rs[0]; idx = ri[0];
-  for (int ww = 1; ww < kWaves; ++ww)
-    if (rs[ww] > score || (rs[ww] == score && ri[ww] < idx)) { score = rs[ww]; idx = ri[ww]; }
+  for (int ww = 1; ww < kWaves; ++ww) take_better(score, idx, rs[ww], ri[ww]);
   __syncthreads();
 }
 
@@ -1103,23 +1171,25 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
   const int gsel = gbest < NG ? gbest : 0;
 
   // race inside the winning group, weights recomputed in fp64 (the Markov bias of the
-  // group's ids from one cooperative pass over their W2t rows)
+  // group's ids from one cooperative pass over their W2t rows).  The logits, the
+  // row constants and the clock do not wait for the bias pass and its barrier.
   const int v = gsel * kGroup + tid;
+  const int vc = v < a.V ? v : a.V - 1;
+  const double lt = load1<DT>(reinterpret_cast<const char*>(a.target) + (size_t)tr * a.V * esz, vc);
+  const double dl = load1<DT>(reinterpret_cast<const char*>(a.draft) + (size_t)dr * a.V * esz, vc);
+  const double lpP = a.method == 1 ? a.ws.logP[tr] * kLog2e : 0.0;
+  const double tl2s = a.ws.tl2s[tr], dm = (double)a.ws.dm[dr], dl2s = a.ws.dl2s[dr];
+  const double E = race_clock(a.key0, a.key1, (uint32_t)b, (uint32_t)v, kPurposeRaceItem, a.step);
   const int prev = (!use_p && a.W1 != nullptr) ? draft_prev(a, b, s) : -1;
   const float bias = prev >= 0 ? group_bias<KS>(a, prev, gsel, gb) : 0.f;
   double sc = -1.0;
   if (v < a.V) {
-    const double E = race_clock(a.key0, a.key1, (uint32_t)b, (uint32_t)v, kPurposeRaceItem, a.step);
-    const double lt = load1<DT>(reinterpret_cast<const char*>(a.target) + (size_t)tr * a.V * esz, v);
     double wv;
     if (use_p) {
       wv = exp2((lt - Mt) * c);
     } else {
-      const double d = (double)load1<DT>(reinterpret_cast<const char*>(a.draft) + (size_t)dr * a.V * esz, v) +
-                       (double)bias;
-      const double lpP = a.method == 1 ? a.ws.logP[tr] * kLog2e : 0.0;
-      const double pv = exp2((lt - Mt) * c - a.ws.tl2s[tr] + lpP);
-      const double qv = exp2((d - (double)a.ws.dm[dr]) * c - a.ws.dl2s[dr]);
+      const double pv = exp2((lt - Mt) * c - tl2s + lpP);
+      const double qv = exp2((dl + (double)bias - dm) * c - dl2s);
       wv = pv - qv;
     }
     if (wv > 0.0) sc = wv / E;
@@ -1225,20 +1295,7 @@ __global__ __launch_bounds__(kThreads, 2) void walk_partials_kernel(Args a, int 
 }
 
 // (value, index) maximum over the workgroup, lowest index among equal values.
-__device__ void block_max_index(double& val, int& idx, double* rs, int* ri) {
-  const int tid = threadIdx.x;
-  for (int off = 32; off >= 1; off >>= 1) {
-    const double ov = __shfl_xor(val, off);
-    const int oi = __shfl_xor(idx, off);
-    if (ov > val || (ov == val && oi < idx)) { val = ov; idx = oi; }
-  }
-  if ((tid & 63) == 0) { rs[tid >> 6] = val; ri[tid >> 6] = idx; }
-  __syncthreads();
-  val = rs[0]; idx = ri[0];
-  for (int ww = 1; ww < kWaves; ++ww)
-    if (rs[ww] > val || (rs[ww] == val && ri[ww] < idx)) { val = rs[ww]; idx = ri[ww]; }
-  __syncthreads();
-}
+__device__ void block_max_index(double& val, int& idx, double* rs, int* ri) { block_argmax(val, idx, rs, ri); }
 
 template <int DT, int KS>
 __global__ __launch_bounds__(kThreads) void walk_pick_kernel(Args a, int j, int32_t* tokens_out, double* logq_out) {
