@@ -925,17 +925,17 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
   // the W2 slab does not depend on the list: its loads go out before the count is read
   bf16x8 A[4][KS];
   if (MARKOV) load_w2_slab<KS, VEC>(a, cb, n, q, A);
-  const int NI = *a.ws.nitems;
-  if (NI == 0) return;
-  const int nch = (NI + kChunk - 1) / kChunk;
-  bf16x8 Bc[KS];
-  if (MARKOV) load_btile<KS>(a, 0, l, Bc);
-  // Item of this lane's row in chunk c (clamped: chunks past the list re-read the last item)
-  auto item_at = [&](int c) {
-    const int it = min(c, nch - 1) * kChunk + n;
-    return it < NI ? it : NI - 1;
+  // The first chunks' rows do not wait for the list count either: row indices are
+  // read speculatively (entries past the count are stale, clamped to valid rows and
+  // never written back), so the first logits loads follow one dependent load.
+  const int NT = a.B * (a.k + 1);
+  auto item_at = [&](int c) { return min(c * kChunk + n, ND - 1); };
+  auto rows_of = [&](int c) {   // (dr, tr) of this lane's row in chunk c, clamped
+    int2 h = *reinterpret_cast<const int2*>(&a.ws.items[item_at(c)].dr);
+    h.x = min(max(h.x, 0), ND - 1);
+    h.y = min(max(h.y, 0), NT - 1);
+    return h;
   };
-  auto rows_of = [&](int c) { return *reinterpret_cast<const int2*>(&a.ws.items[item_at(c)].dr); };   // (dr, tr)
   auto fetch = [&](int2 h, Raw16<DT>& t, Raw16<DT>& d) {
     raw_load<DT, VEC>(t, reinterpret_cast<const char*>(a.target) + (size_t)h.y * rb, c0, a.V);
     raw_load<DT, VEC>(d, reinterpret_cast<const char*>(a.draft) + (size_t)h.x * rb, c0, a.V);
@@ -944,6 +944,11 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
   Raw16<DT> tb, db;
   fetch(rows_of(0), tb, db);
   int2 hn = rows_of(1);
+  const int NI = *a.ws.nitems;
+  if (NI == 0) return;
+  const int nch = (NI + kChunk - 1) / kChunk;
+  bf16x8 Bc[KS];
+  if (MARKOV) load_btile<KS>(a, 0, l, Bc);
   for (int c = 0; c < nch; ++c) {
     const int2 hnn = rows_of(c + 2);
     const float4* kc = reinterpret_cast<const float4*>(&a.ws.items[item_at(c)].Mt);
