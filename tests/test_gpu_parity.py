@@ -66,6 +66,24 @@ def test_small_shapes(mod, method, V, dtype, R, B, k, markov):
     _run(mod, wl, method, range(20), f"V{V}-{dtype}-R{R}")
 
 
+LARGE_V = [
+    # (V, dtype, R, B, k): more than 512 groups (V > 131072), one pass of the scan per
+    # 512 groups; k > 5 also splits the rows into passes of 6; odd V takes the
+    # unaligned (non-vector) loads.  Small ranks keep the fp64 oracle fast.
+    (140001, "bf16", 32, 2, 7),
+    (200000, "bf16", 64, 3, 5),
+    (150000, "f32", 32, 2, 3),
+]
+
+
+@pytest.mark.parametrize("V,dtype,R,B,k", LARGE_V)
+@pytest.mark.parametrize("method", ["tokenwise", "block"])
+def test_vocab_past_512_groups(mod, method, V, dtype, R, B, k):
+    wl = workloads.make_zipf(f"largeV{V}", seed=V % 1000 + k, B=B, k=k, V=V, dtype=dtype, R=R, sigma=1.5,
+                             rho=(0.6, 0.99), greedy_every=3 if B > 2 else 0)
+    _run(mod, wl, method, range(3), f"V{V}-{dtype}-k{k}")
+
+
 @pytest.mark.parametrize("method", ["tokenwise", "block"])
 def test_single_stream_fp32_full_vocab(mod, method):
     wl = workloads.make("c2")

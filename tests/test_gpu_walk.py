@@ -56,6 +56,7 @@ SHAPES = [
     (333, "bf16", 64, True),
     (4099, "f32", 128, True),
     (777, "f32", 256, False),
+    (200000, "bf16", 32, True),   # more than 512 groups
 ]
 
 
