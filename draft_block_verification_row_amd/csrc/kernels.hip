@@ -1452,37 +1452,59 @@ __global__ __launch_bounds__(kThreads) void markov_bias_kernel(BiasArgs ba) {
 }
 
 // ---------------------------------------------------------------------------
-// Confidence head + adaptive count.  One workgroup per stream, one wave per slot:
-// the wave's lanes take 8 consecutive hidden features each, 512 per step, and the
-// dot product accumulates in fp64.
+// Confidence head + adaptive count.  One workgroup per stream: for 4 slots at a time
+// every thread takes 8 consecutive hidden features per step (2048 per step), so the
+// loads of all 4 slots are in flight together; the dot products accumulate in fp64.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void adaptive_kernel(AdaptArgs aa) {
+  constexpr int kSlots = 4;   // slots whose hidden states are in flight together
+  __shared__ double s_part[kWaves][kMaxK];
   __shared__ double s_c[kMaxK];
   const int b = blockIdx.x;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  for (int j = w; j < aa.k; j += kWaves) {
-    const uint16_t* h = aa.hidden + ((size_t)b * aa.k + j) * aa.H;
-    double acc = 0.0;
+  // w . h for every slot: the whole workgroup splits H, each wave sums its share in
+  // fp64 and the 4 wave sums meet in LDS
+  for (int j0 = 0; j0 < aa.k; j0 += kSlots) {
+    double acc[kSlots] = {0.0, 0.0, 0.0, 0.0};
+    const uint16_t* h[kSlots];
+#pragma unroll
+    for (int sl = 0; sl < kSlots; ++sl) h[sl] = aa.hidden + ((size_t)b * aa.k + min(j0 + sl, aa.k - 1)) * aa.H;
     if (aa.vec_ok) {   // H % 8 == 0 and 16-byte aligned rows
-#pragma unroll 4
-      for (int c0 = 8 * l; c0 < aa.H; c0 += 512) {
-        const uint4 hv = *reinterpret_cast<const uint4*>(h + c0);
+#pragma unroll 2
+      for (int c0 = 8 * tid; c0 < aa.H; c0 += 8 * kThreads) {
         const uint4 wv = *reinterpret_cast<const uint4*>(aa.w + c0);
-        const uint32_t hh[4] = {hv.x, hv.y, hv.z, hv.w};
+        uint4 hv[kSlots];
+#pragma unroll
+        for (int sl = 0; sl < kSlots; ++sl) hv[sl] = *reinterpret_cast<const uint4*>(h[sl] + c0);
         const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc += (double)bf16lo(hh[i]) * (double)bf16lo(ww[i]) + (double)bf16hi(hh[i]) * (double)bf16hi(ww[i]);
+        for (int sl = 0; sl < kSlots; ++sl) {
+          const uint32_t hh[4] = {hv[sl].x, hv[sl].y, hv[sl].z, hv[sl].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[sl] += (double)bf16lo(hh[i]) * (double)bf16lo(ww[i]) + (double)bf16hi(hh[i]) * (double)bf16hi(ww[i]);
+        }
       }
     } else {
-      for (int c = l; c < aa.H; c += 64) acc += (double)bf16_to_f32(h[c]) * (double)bf16_to_f32(aa.w[c]);
+      for (int c = tid; c < aa.H; c += kThreads) {
+        const double wc = (double)bf16_to_f32(aa.w[c]);
+#pragma unroll
+        for (int sl = 0; sl < kSlots; ++sl) acc[sl] += (double)bf16_to_f32(h[sl][c]) * wc;
+      }
     }
-    acc = wave_sum(acc);
-    if (l == 0) {
-      const double cj = 1.0 / (1.0 + exp(-(acc + (double)aa.bias)));
-      s_c[j] = cj;
-      if (aa.c_out) aa.c_out[b * aa.k + j] = (float)cj;
-    }
+#pragma unroll
+    for (int sl = 0; sl < kSlots; ++sl) acc[sl] = wave_sum(acc[sl]);
+    if (l == 0)
+#pragma unroll
+      for (int sl = 0; sl < kSlots; ++sl)
+        if (j0 + sl < aa.k) s_part[w][j0 + sl] = acc[sl];
+  }
+  __syncthreads();
+  if (tid < aa.k) {
+    const double z = (s_part[0][tid] + s_part[1][tid]) + (s_part[2][tid] + s_part[3][tid]);
+    const double cj = 1.0 / (1.0 + exp(-(z + (double)aa.bias)));
+    s_c[tid] = cj;
+    if (aa.c_out) aa.c_out[b * aa.k + tid] = (float)cj;
   }
   __syncthreads();
   if (tid == 0) {
