@@ -283,12 +283,12 @@ __device__ __forceinline__ int div_small(int i, float hd) { return (int)((float)
 // at each row's draft token: the target's t_j(x_j) and the drafter's d_j(x_j) plus
 // the Markov bias W1[prev] . W2t[x_j], summed in fp64 (each lane a quarter of the
 // rank, then the 4 lanes of the row), for the scan's log p_j(x_j) and log q_j(x_j).
-// Also clears the pass-2 list count.
+// Also clears the pass-2 list counts.
 // ---------------------------------------------------------------------------
 template <int DT>
 __global__ __launch_bounds__(64) void pack_kernel(Args a) {
   const int c = blockIdx.x, l = threadIdx.x, n = l & 15, q = l >> 4;
-  if (c == 0 && l == 0) *a.ws.nitems = 0;
+  if (c == 0 && l < 2) a.ws.nitems[l] = 0;
   const int ND = a.B * a.k;
   const int dr = c * kChunk + n, drc = min(dr, ND - 1);
   const int b = drc / a.k, j = drc - b * a.k;
@@ -369,25 +369,35 @@ __device__ __forceinline__ void markov_mma(const bf16x8 (&A)[4][KS], const bf16x
 __host__ __device__ __forceinline__ size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
 __host__ __device__ __forceinline__ size_t stream_table_bytes(int B) {
-  return align16((size_t)B * sizeof(float)) + align16((size_t)B * sizeof(int));
+  return align16((size_t)B * sizeof(float)) + align16((size_t)B * sizeof(int)) + 16;
 }
+
+// Stand-in temperature constant of a greedy stream (T = 0) in the stream table; no
+// sampled stream comes near it (log2(e) / T < 1e-20 would need T > 1e20).
+constexpr float kGreedyTcValue = 1e-30f;
+constexpr float kGreedyTc = 1e-20f;
 
 struct StreamTable {
   const float* tc;
   const int* gam;
+  bool any_greedy;
 };
 
 __device__ __forceinline__ StreamTable build_stream_table(const Args& a, char* smem) {
   float* tc = reinterpret_cast<float*>(smem);
   int* gam = reinterpret_cast<int*>(smem + align16((size_t)a.B * sizeof(float)));
+  int* flag = reinterpret_cast<int*>(smem + align16((size_t)a.B * sizeof(float)) + align16((size_t)a.B * sizeof(int)));
+  if (threadIdx.x == 0) flag[0] = 0;
+  __syncthreads();
   for (int b = threadIdx.x; b < a.B; b += kThreads) {
     const float T = stream_temp(a, b);
     // T = 0 (greedy) only needs the row maxima: any finite positive c keeps the sums finite
-    tc[b] = T > 0.f ? (float)(kLog2e / (double)T) : 1e-30f;
+    tc[b] = T > 0.f ? (float)(kLog2e / (double)T) : kGreedyTcValue;
     gam[b] = stream_gamma(a, b);
+    if (!(T > 0.f)) flag[0] = 1;
   }
   __syncthreads();
-  return StreamTable{tc, gam};
+  return StreamTable{tc, gam, flag[0] != 0};
 }
 
 // ---------------------------------------------------------------------------
@@ -550,42 +560,56 @@ __device__ __forceinline__ void pass1_target(const Args& a, const StreamTable& s
   const int NT = a.B * k1;
   const size_t rb = (size_t)a.V * (DT == kBF16 ? 2 : 4);
   const char* base = reinterpret_cast<const char*>(a.target);
-  const float hk1 = 0.5f / (float)k1;
-  auto row_ok = [&](int tr, int& b) {
-    b = div_small(tr, hk1);
-    return tr < NT && tr - b * k1 <= st.gam[b < a.B ? b : a.B - 1];
+  const float hk = 0.5f / (float)a.k;
+  // Rows 0..gamma-1 of every stream, enumerated as p = b k + j; then, only if the batch
+  // has a greedy stream, one more row per stream: the bonus row gamma of a greedy
+  // stream (its argmax is needed by the scan).  A sampled stream's bonus row is read
+  // by pass 2, and only when the verifier stops there.  map(p) gives the stream, the
+  // row and whether it is needed; an unneeded row re-reads its stream's first row.
+  auto slot_rows = [&](int p, int& b, int& tr) {
+    b = min(div_small(p, hk), a.B - 1);
+    const int j = p - b * a.k;
+    tr = b * k1 + min(j, a.k - 1);
+    return p < a.B * a.k && j < st.gam[b];
   };
-  auto load_batch = [&](int r0, Raw16<DT>(&raw)[U]) {   // unconditional, as in the draft phase
+  auto bonus_rows = [&](int p, int& b, int& tr) {
+    b = min(p, a.B - 1);
+    tr = b * k1 + st.gam[b];
+    return p < a.B && st.tc[b] < kGreedyTc;
+  };
+  auto rows = [&](int NR, auto map) {
+    auto load_batch = [&](int r0, Raw16<DT>(&raw)[U]) {   // unconditional, as in the draft phase
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int tr = min(r0 + RS * u + rq, NT - 1);
-      int b;
-      const int src = row_ok(tr, b) ? tr : b * k1;
-      raw_load<DT, VEC>(raw[u], base + (size_t)src * rb, c0, a.V);
+      for (int u = 0; u < U; ++u) {
+        int b, tr;
+        const bool act = map(min(r0 + RS * u + rq, NR - 1), b, tr);
+        raw_load<DT, VEC>(raw[u], base + (size_t)(act ? tr : b * k1) * rb, c0, a.V);
+      }
+    };
+    auto consume = [&](int r0, const Raw16<DT>(&raw)[U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        int b, tr;
+        const bool act = map(r0 + RS * u + rq, b, tr);
+        float x[16];
+        raw_to_f32<DT>(raw[u], x);
+        if (rag) mask_shift(x, shift);
+        const float2 pw = row_partial<1>(x, act ? st.tc[b] : 0.f);
+        if (l16 == 0 && act) a.ws.tpart[(size_t)g * NT + tr] = pw;
+      }
+    };
+    Raw16<DT> ra[U], rbuf[U];
+    load_batch(0, ra);
+    for (int r0 = 0; r0 < NR; r0 += 2 * RS * U) {
+      load_batch(r0 + RS * U, rbuf);
+      consume(r0, ra);
+      if (r0 + RS * U >= NR) break;
+      load_batch(r0 + 2 * RS * U, ra);
+      consume(r0 + RS * U, rbuf);
     }
   };
-  auto consume = [&](int r0, const Raw16<DT>(&raw)[U]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int tr = r0 + RS * u + rq;
-      int b;
-      const bool act = row_ok(tr, b);
-      float x[16];
-      raw_to_f32<DT>(raw[u], x);
-      if (rag) mask_shift(x, shift);
-      const float2 pw = row_partial<1>(x, act ? st.tc[b] : 0.f);
-      if (l16 == 0 && act) a.ws.tpart[(size_t)g * NT + tr] = pw;
-    }
-  };
-  Raw16<DT> ra[U], rbuf[U];
-  load_batch(0, ra);
-  for (int r0 = 0; r0 < NT; r0 += 2 * RS * U) {
-    load_batch(r0 + RS * U, rbuf);
-    consume(r0, ra);
-    if (r0 + RS * U >= NT) break;
-    load_batch(r0 + 2 * RS * U, ra);
-    consume(r0 + RS * U, rbuf);
-  }
+  rows(a.B * a.k, slot_rows);
+  if (st.any_greedy) rows(a.B, bonus_rows);
 }
 
 // VEC (rows 16-byte aligned, V >= 16) is a whole-kernel choice made on the host.
@@ -769,7 +793,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
   // on memory together
   const int ngp = min(a.NG, kScanGroups);
   StageRegs sreg;
-  stage_load(sreg, a, b, 0, min(kScanRows, gamma + 1), min(kScanRows, gamma), 0, ngp, tid);
+  stage_load(sreg, a, b, 0, min(kScanRows, gamma), min(kScanRows, gamma), 0, ngp, tid);
 
   if (tid < gamma) s_u[tid] = accept_uniform(a.key0, a.key1, (uint32_t)b, (uint32_t)tid, a.step);
 
@@ -779,10 +803,12 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
     s_ld[tid] = a.ws.gld[b * a.k + tid];
   }
 
-  // row normalisers: passes of 6 target and 6 draft rows (the first pass's loads were
-  // issued above), each over groups in runs of 512 staged through LDS
-  for (int r0 = 0; r0 <= gamma; r0 += kScanRows) {
-    const int nt = min(kScanRows, gamma + 1 - r0), nd = max(0, min(kScanRows, gamma - r0));
+  // row normalisers of target and draft rows 0..gamma-1 (the bonus row's statistics
+  // are taken by pass 2 if the verifier stops there): passes of 6 target and 6 draft
+  // rows (the first pass's loads were issued above), each over groups in runs of 512
+  // staged through LDS
+  for (int r0 = 0; r0 < gamma; r0 += kScanRows) {
+    const int nt = min(kScanRows, gamma - r0), nd = nt;
     float M[3] = {-INFINITY, -INFINITY, -INFINITY};
     double S[3] = {0.0, 0.0, 0.0};
     for (int g0 = 0; g0 < a.NG; g0 += kScanGroups) {
@@ -802,7 +828,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
       const int slot = w + kWaves * q;
       const bool is_t = slot < kScanRows;
       const int j = r0 + (is_t ? slot : slot - kScanRows);   // slot within the stream
-      if (l == q && (is_t ? j <= gamma : j < gamma)) {
+      if (l == q && j < gamma) {
         const int r = is_t ? j : gamma + 1 + j;                 // index into s_M / s_l2s
         s_M[r] = M[q];
         s_l2s[r] = l2s;
@@ -863,6 +889,15 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
     a.ws.rowmask[b] = mask;
     s_mask = mask;
     s_base = mask ? atomicAdd(a.ws.nitems, __popc(mask)) : 0;
+    if (stop == gamma) {   // the bonus row is sampled: pass 2 takes its group statistics
+      const int ib = atomicAdd(a.ws.nitems + 1, 1);
+      Item it{};
+      it.dr = -1;
+      it.tr = b * k1 + gamma;
+      it.prev = -1;
+      it.chi = (float)(kLog2e / T);   // pass 1's fp32 constant for this stream
+      a.ws.items[a.B * a.k - 1 - ib] = it;
+    }
   }
   __syncthreads();
   if (tid <= gamma) a.ws.logP[b * k1 + tid] = s_lp[tid];
@@ -912,6 +947,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
 template <int DT, int KS, bool MARKOV, bool VEC>
 __global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
   __shared__ float part[kFlush * kChunk][kWaves];
+  __shared__ float2 bpart[kChunk][kWaves];
   const int g = blockIdx.x;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, q = l >> 4;
   const int cb = (g * kWaves + w) * kWaveCols;
@@ -944,11 +980,10 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
   Raw16<DT> tb, db;
   fetch(rows_of(0), tb, db);
   int2 hn = rows_of(1);
-  const int NI = *a.ws.nitems;
-  if (NI == 0) return;
+  const int NI = a.ws.nitems[0], NB = a.ws.nitems[1];
   const int nch = (NI + kChunk - 1) / kChunk;
   bf16x8 Bc[KS];
-  if (MARKOV) load_btile<KS>(a, 0, l, Bc);
+  if (MARKOV && NI > 0) load_btile<KS>(a, 0, l, Bc);
   for (int c = 0; c < nch; ++c) {
     const int2 hnn = rows_of(c + 2);
     const float4* kc = reinterpret_cast<const float4*>(&a.ws.items[item_at(c)].Mt);
@@ -989,6 +1024,31 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
       }
       __syncthreads();
     }
+  }
+  // bonus rows the verifier stops at (listed from the back of the list): their group
+  // statistics (max, sum 2^((x - max) c)) with pass 1's constant, as pass 1 does for
+  // every other target row
+  const int NT2 = a.B * (a.k + 1);
+  for (int c = 0; c < (NB + kChunk - 1) / kChunk; ++c) {
+    const Item& it = a.ws.items[ND - 1 - min(c * kChunk + n, NB - 1)];
+    const int tr = min(max(it.tr, 0), NT2 - 1);
+    const float cb_ = it.chi;
+    Raw16<DT> t;
+    raw_load<DT, VEC>(t, reinterpret_cast<const char*>(a.target) + (size_t)tr * rb, c0, a.V);
+    float x[16];
+    raw_to_f32<DT>(t, x);
+    if (rag) mask_shift(x, shift);
+    const float2 pw = row_partial<0>(x, cb_);
+    if (q == 0) bpart[n][w] = pw;
+    __syncthreads();
+    if (tid < kChunk && c * kChunk + tid < NB) {
+      const Item& ib = a.ws.items[ND - 1 - (c * kChunk + tid)];
+      float2 p[kWaves];
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) p[ww] = bpart[tid][ww];
+      a.ws.tpart[(size_t)g * NT2 + ib.tr] = combine_waves(p, ib.chi);
+    }
+    __syncthreads();
   }
 }
 
@@ -1139,11 +1199,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
   // group masses of the sampled row: the residual (pass 2) or, for the bonus row
   // and an all-zero residual, the target's own partials.  A thread's first two
   // groups load both kinds at once; groups past 512 (V > 131072) are re-read.
-  const double Mt = (double)a.ws.tm[tr];
   const bool resid = s < gamma;
-  auto target_mass = [&](float2 p) {
-    return p.x == -INFINITY ? 0.0 : (double)p.y * exp2(((double)p.x - Mt) * c);
-  };
   float Wr[2];
   float2 Tp[2];
 #pragma unroll
@@ -1159,6 +1215,22 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
   if (resid)
     for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) rsum += (double)a.ws.wgrp[(size_t)gi * ND + dr];
   const bool use_p = !resid || !(block_sum(rsum, red) > 0.0);
+  // sampling from p_s: the target row's maximum over its group maxima (pass 2 took the
+  // bonus row's group statistics; any common reference works for the race, this one
+  // keeps every weight <= 1)
+  double Mt = resid ? (double)a.ws.tm[tr] : 0.0;   // the residual's weights use the scan's row maximum
+  if (use_p) {
+    float m = fmaxf(Tp[0].x, Tp[1].x);
+    for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) m = fmaxf(m, a.ws.tpart[(size_t)gi * NT + tr].x);
+    m = wave_max_dpp(m);
+    if (l == 0) red[w] = (double)m;
+    __syncthreads();
+    Mt = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+    __syncthreads();
+  }
+  auto target_mass = [&](float2 p) {
+    return p.x == -INFINITY ? 0.0 : (double)p.y * exp2(((double)p.x - Mt) * c);
+  };
   double best = -1.0;
   int gbest = 0x7fffffff;
   for (int gi = tid, t = 0; gi < NG; gi += kThreads, ++t) {
