@@ -276,6 +276,11 @@ __device__ __forceinline__ float2 row_partial(const float (&x)[16], float c) {
 // lies at least 1/(2d) from an integer and the two fp32 roundings move it by less.
 __device__ __forceinline__ int div_small(int i, float hd) { return (int)((float)(2 * i + 1) * hd); }
 
+// Pass 1 hands out its target items from kQueues counters (workgroup g uses counter
+// g % min(kQueues, grid), items of its own residue class), kQueueStride ints apart.
+constexpr int kQueues = 8;
+constexpr int kQueueStride = 32;
+
 // ---------------------------------------------------------------------------
 // pack: one wave per 16 draft rows (lane n + 16 q: row n, quarter q of each k-step).
 // (1) The W1 rows of the rows' previous tokens go into `btile` in MFMA lane order, so
@@ -283,12 +288,13 @@ __device__ __forceinline__ int div_small(int i, float hd) { return (int)((float)
 // at each row's draft token: the target's t_j(x_j) and the drafter's d_j(x_j) plus
 // the Markov bias W1[prev] . W2t[x_j], summed in fp64 (each lane a quarter of the
 // rank, then the 4 lanes of the row), for the scan's log p_j(x_j) and log q_j(x_j).
-// Also clears the pass-2 list counts.
+// Also clears the pass-2 list counts and the pass-1 item counter.
 // ---------------------------------------------------------------------------
 template <int DT>
 __global__ __launch_bounds__(64) void pack_kernel(Args a) {
   const int c = blockIdx.x, l = threadIdx.x, n = l & 15, q = l >> 4;
   if (c == 0 && l < 2) a.ws.nitems[l] = 0;
+  if (c == 0 && l < kQueues) a.ws.nitems[kQueueStride * (1 + l)] = 0;
   const int ND = a.B * a.k;
   const int dr = c * kChunk + n, drc = min(dr, ND - 1);
   const int b = drc / a.k, j = drc - b * a.k;
@@ -544,73 +550,113 @@ __device__ __forceinline__ void pass1_draft(const Args& a, const StreamTable& st
   }
 }
 
-// Target rows: a 16-lane DPP row covers the group's 256 ids of one row; the
-// workgroup takes 16 rows per step, U steps per batch, and loads the next batch
-// while reducing the current one.
+// Target rows, after the workgroup's draft rows, in items of kItemRows rows of one
+// group handed out by counters (zeroed by pack): the second workgroup resident on a
+// compute unit issues behind the first (its waves are younger), and with a fixed
+// split it would finish ~10 us after it; taking items until none is left, both end
+// together.  Item i covers group i % NG and rows [kItemRows (i / NG), +kItemRows) of
+// the row list: rows 0..gamma-1 of every stream, enumerated as p = b k + j; then, only
+// if the batch has a greedy stream, one more row per stream: the bonus row gamma of a
+// greedy stream (its argmax is needed by the scan).  A sampled stream's bonus row is
+// read by pass 2, and only when the verifier stops there.  A 16-lane DPP row covers
+// the group's 256 ids of one row; a workgroup step takes 16 rows, U steps an item.
+// Workgroup g draws from counter g % min(kQueues, grid), whose items are the indices
+// of that residue class (one counter for the whole grid serialises ~2500 atomics on
+// one address).  Thread 0 claims one item ahead (in `pend`), so the counter's round
+// trip is hidden behind an item's loads.
+template <int DT>
+struct TargetQueue {
+  static constexpr int U = DT == kBF16 ? 4 : 2;
+  static constexpr int kRS = kThreads / 16;      // rows per step
+  static constexpr int kItemRows = kRS * U;
+  int* slot;   // LDS [2]: the claimed index, seen by the whole workgroup
+  int par;     // which slot the next claim uses
+  int pend;    // thread 0: the index claimed for the next item
+};
+
 template <int DT, bool VEC>
-__device__ __forceinline__ void pass1_target(const Args& a, const StreamTable& st, int g) {
-  constexpr int U = DT == kBF16 ? 4 : 2;
-  constexpr int RS = kThreads / 16;   // rows per step
+__device__ __forceinline__ void pass1_target(const Args& a, const StreamTable& st, TargetQueue<DT>& tq) {
+  using Q = TargetQueue<DT>;
+  constexpr int U = Q::U, RS = Q::kRS, IR = Q::kItemRows;
   const int tid = threadIdx.x, rq = tid >> 4, l16 = tid & 15;
-  const int cw = g * kGroup + 16 * l16;
-  const int c0 = VEC ? min(cw, a.V - 16) : cw;
-  const int shift = VEC ? (cw >= a.V ? 16 : cw - c0) : 0;
-  const bool rag = VEC && (g + 1) * kGroup > a.V;
   const int k1 = a.k + 1;
-  const int NT = a.B * k1;
+  const int NT = a.B * k1, NS = a.B * a.k;
+  const int NR = NS + (st.any_greedy ? a.B : 0);
+  const int NI = (NR + IR - 1) / IR * a.NG;
   const size_t rb = (size_t)a.V * (DT == kBF16 ? 2 : 4);
   const char* base = reinterpret_cast<const char*>(a.target);
   const float hk = 0.5f / (float)a.k;
-  // Rows 0..gamma-1 of every stream, enumerated as p = b k + j; then, only if the batch
-  // has a greedy stream, one more row per stream: the bonus row gamma of a greedy
-  // stream (its argmax is needed by the scan).  A sampled stream's bonus row is read
-  // by pass 2, and only when the verifier stops there.  map(p) gives the stream, the
-  // row and whether it is needed; an unneeded row re-reads its stream's first row.
-  auto slot_rows = [&](int p, int& b, int& tr) {
-    b = min(div_small(p, hk), a.B - 1);
-    const int j = p - b * a.k;
-    tr = b * k1 + min(j, a.k - 1);
-    return p < a.B * a.k && j < st.gam[b];
-  };
-  auto bonus_rows = [&](int p, int& b, int& tr) {
-    b = min(p, a.B - 1);
+  // row p of the list -> stream b, target row tr, and whether it is needed
+  auto map = [&](int p, int& b, int& tr) {
+    if (p < NS) {
+      b = min(div_small(p, hk), a.B - 1);
+      const int j = p - b * a.k;
+      tr = b * k1 + j;
+      return j < st.gam[b];
+    }
+    b = min(p - NS, a.B - 1);
     tr = b * k1 + st.gam[b];
-    return p < a.B && st.tc[b] < kGreedyTc;
+    return p < NR && st.tc[b] < kGreedyTc;
   };
-  auto rows = [&](int NR, auto map) {
-    auto load_batch = [&](int r0, Raw16<DT>(&raw)[U]) {   // unconditional, as in the draft phase
+  const int nq = min(kQueues, (int)gridDim.x), qx = blockIdx.x % nq;
+  auto claim = [&]() {
+    if (tid == 0) {
+      tq.slot[tq.par] = tq.pend;
+      tq.pend = atomicAdd(a.ws.nitems + kQueueStride * (1 + qx), 1);
+    }
+    __syncthreads();
+    const int i = qx + nq * __builtin_amdgcn_readfirstlane(tq.slot[tq.par]);
+    tq.par ^= 1;
+    return i;
+  };
+  // unconditional loads, as in the draft phase: an unneeded row re-reads its stream's
+  // first row
+  auto load_item = [&](int i, Raw16<DT>(&raw)[U]) {
+    const int gi = i % a.NG, r0 = i / a.NG * IR;
+    const int cw = gi * kGroup + 16 * l16;
+    const int c0 = VEC ? min(cw, a.V - 16) : cw;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        int b, tr;
-        const bool act = map(min(r0 + RS * u + rq, NR - 1), b, tr);
-        raw_load<DT, VEC>(raw[u], base + (size_t)(act ? tr : b * k1) * rb, c0, a.V);
-      }
-    };
-    auto consume = [&](int r0, const Raw16<DT>(&raw)[U]) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        int b, tr;
-        const bool act = map(r0 + RS * u + rq, b, tr);
-        float x[16];
-        raw_to_f32<DT>(raw[u], x);
-        if (rag) mask_shift(x, shift);
-        const float2 pw = row_partial<1>(x, act ? st.tc[b] : 0.f);
-        if (l16 == 0 && act) a.ws.tpart[(size_t)g * NT + tr] = pw;
-      }
-    };
-    Raw16<DT> ra[U], rbuf[U];
-    load_batch(0, ra);
-    for (int r0 = 0; r0 < NR; r0 += 2 * RS * U) {
-      load_batch(r0 + RS * U, rbuf);
-      consume(r0, ra);
-      if (r0 + RS * U >= NR) break;
-      load_batch(r0 + 2 * RS * U, ra);
-      consume(r0 + RS * U, rbuf);
+    for (int u = 0; u < U; ++u) {
+      int b, tr;
+      const bool act = map(min(r0 + RS * u + rq, NR - 1), b, tr);
+      raw_load<DT, VEC>(raw[u], base + (size_t)(act ? tr : b * k1) * rb, c0, a.V);
     }
   };
-  rows(a.B * a.k, slot_rows);
-  if (st.any_greedy) rows(a.B, bonus_rows);
+  auto consume = [&](int i, const Raw16<DT>(&raw)[U]) {
+    const int gi = i % a.NG, r0 = i / a.NG * IR;
+    const int cw = gi * kGroup + 16 * l16;
+    const int c0 = VEC ? min(cw, a.V - 16) : cw;
+    const int shift = VEC ? (cw >= a.V ? 16 : cw - c0) : 0;   // columns of the window owned elsewhere
+    const bool rag = VEC && (gi + 1) * kGroup > a.V;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int b = 0, tr = 0;
+      const int p = r0 + RS * u + rq;
+      const bool act = p < NR && map(p, b, tr);
+      float x[16];
+      raw_to_f32<DT>(raw[u], x);
+      if (rag) mask_shift(x, shift);
+      const float2 pw = row_partial<1>(x, act ? st.tc[b] : 0.f);
+      if (l16 == 0 && act) a.ws.tpart[(size_t)gi * NT + tr] = pw;
+    }
+  };
+  int cur = claim();
+  if (cur >= NI) return;
+  Raw16<DT> ra[U], rbuf[U];
+  load_item(cur, ra);
+  for (;;) {   // past the last item, the current one is loaded again (cache hits), unused
+    const int nx = claim();
+    load_item(nx < NI ? nx : cur, rbuf);
+    consume(cur, ra);
+    if (nx >= NI) break;
+    const int nx2 = claim();
+    load_item(nx2 < NI ? nx2 : nx, ra);
+    consume(nx, rbuf);
+    if (nx2 >= NI) break;
+    cur = nx2;
+  }
 }
+
 
 // VEC (rows 16-byte aligned, V >= 16) is a whole-kernel choice made on the host.
 template <int DT, int KS, bool MARKOV, bool VEC>
@@ -618,16 +664,13 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_kernel(Args a) {
   extern __shared__ char smem[];
   __shared__ float2 part[kFlush * kChunk][kWaves];
   __shared__ uint4 bst[MARKOV ? 2 * TileStage<KS>::kUnits : 1];   // 64 KB at R = 256
+  __shared__ int qslot[2];
   const StreamTable st = build_stream_table(a, smem);
   const int g = blockIdx.x;
-  // alternate the phase order so that MFMA-heavy and streaming phases overlap across the chip
-  if (g & 1) {
-    pass1_target<DT, VEC>(a, st, g);
-    pass1_draft<DT, KS, MARKOV, VEC>(a, st, g, part, bst);
-  } else {
-    pass1_draft<DT, KS, MARKOV, VEC>(a, st, g, part, bst);
-    pass1_target<DT, VEC>(a, st, g);
-  }
+  TargetQueue<DT> tq{qslot, 0, 0};
+  if (threadIdx.x == 0) tq.pend = atomicAdd(a.ws.nitems + kQueueStride * (1 + g % min(kQueues, (int)gridDim.x)), 1);
+  pass1_draft<DT, KS, MARKOV, VEC>(a, st, g, part, bst);
+  pass1_target<DT, VEC>(a, st, tq);
 }
 
 // Row normalisers from the group partials (m_g, s_g) of pass 1: M = max_g m_g and
