@@ -21,7 +21,7 @@ bool rank_ok(int R) { return R == 32 || R == 64 || R == 128 || R == 256; }
 
 // Offsets of every workspace region, in the order of dspark::Workspace.
 struct Layout {
-  size_t off[17];
+  size_t off[15];
   size_t total;
 };
 
@@ -29,7 +29,7 @@ Layout layout(int B, int k, int V) {
   const size_t NG = (size_t)(V + kGroup - 1) / kGroup;
   const size_t BT = (size_t)B * (k + 1), BD = (size_t)B * k;
   const size_t tiles = (BD + kChunk - 1) / kChunk;
-  const size_t sizes[17] = {
+  const size_t sizes[15] = {
       BT * NG * sizeof(float2),           // tpart
       BD * NG * sizeof(float2),           // dpart
       BD * NG * sizeof(float),            // wgrp
@@ -45,12 +45,10 @@ Layout layout(int B, int k, int V) {
       BD * sizeof(Item),                // items
       9 * 32 * sizeof(int32_t),         // nitems (residual rows, bonus rows; pass-1 item counters)
       tiles * 8 * 64 * sizeof(uint4),   // btile (sized for the largest rank, R = 256)
-      BD * sizeof(double),              // glt
-      BD * sizeof(double),              // gld
   };
   Layout L;
   size_t o = 0;
-  for (int i = 0; i < 17; ++i) {
+  for (int i = 0; i < 15; ++i) {
     L.off[i] = o;
     o += align_up(sizes[i] > 0 ? sizes[i] : 1);
   }
@@ -119,8 +117,6 @@ dspark_status verify_common(const dspark_verify_problem* p, const dspark_verify_
   a.ws.items = reinterpret_cast<Item*>(base + L.off[12]);
   a.ws.nitems = reinterpret_cast<int32_t*>(base + L.off[13]);
   a.ws.btile = reinterpret_cast<uint4*>(base + L.off[14]);
-  a.ws.glt = reinterpret_cast<double*>(base + L.off[15]);
-  a.ws.gld = reinterpret_cast<double*>(base + L.off[16]);
   if (launch_verify(a, reinterpret_cast<hipStream_t>(stream), o->stage_events) != hipSuccess)
     return DSPARK_ERR_HIP;
   return DSPARK_OK;

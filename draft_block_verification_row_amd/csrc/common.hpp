@@ -145,9 +145,7 @@ struct Workspace {
   uint32_t* rowmask;  // [B]           pass-2 rows of each stream (bit i = slot i)
   Item* items;        // [B*k]         pass-2 list: residual rows from the front, bonus rows from the back
   int32_t* nitems;    // [4]           residual rows, bonus rows, pass-1 target items claimed
-  uint4* btile;       // [ceil(B*k/16)][R/32][64] W1 tiles in MFMA lane order (pass 1, then pass 2)
-  double* glt;        // [B*k]         target logit at the draft token, t_j(x_j)
-  double* gld;        // [B*k]         biased draft logit at the draft token, d_j(x_j) + bias (fp64)
+  uint4* btile;       // [ceil(B*k/16)][R/32][64] W1 tiles of pass 2's rows in MFMA lane order
 };
 
 struct Args {

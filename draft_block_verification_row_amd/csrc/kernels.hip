@@ -7,19 +7,21 @@
 //   pack      the B operand of the Markov product [P2 §6; P1 §3 "The Markov fix-up"]:
 //             W1[prev] of every draft row, 16 rows per tile, stored in MFMA lane
 //             order so that a wave reads one k-step of a tile as one contiguous
-//             1 KB load (gathering W1 rows per wave is the slow part otherwise).
-//   pass1     one workgroup per 256-id vocabulary group g.  Target rows (slots
-//             0..gamma_b): a 16-lane row reduces the group's 256 ids to a partial
-//             (max, sum 2^((l - max) log2e / T)).  Draft rows (slots 0..gamma_b-1):
-//             each wave keeps its 64 columns of W2 as MFMA A operands, streams the
-//             packed W1 tiles through the B operand and adds the bias; the wave
-//             partials meet in LDS once every 16 chunks (the only barriers).
-//   scan      one workgroup per stream: row normalisers from the partials (fp64),
-//             log p_j(x_j), log q_j(x_j) (gathered bias in fp64), the token-wise stop
-//             and the clipped prefix P_i [P1 §4], and the rows whose residual mass
-//             is needed.  Block verification needs R_i only where u_{i-1} <= P_i
-//             (h_i <= P_i always), plus the row the sampler may land on.  The scan
-//             also packs the W1 tiles of those rows.
+//             1 KB load (gathering W1 rows per wave is the slow part otherwise);
+//             clears the counters of the launches below.
+//   pass1     one workgroup per 256-id vocabulary group g.  Draft rows (slots
+//             0..gamma_b-1): each wave keeps its 64 columns of W2 as MFMA A operands,
+//             streams the packed W1 tiles through the B operand (staged in LDS) and
+//             adds the bias; the wave partials meet in LDS once every 16 chunks.
+//             Then target rows (slots 0..gamma_b-1): a 16-lane row reduces a group's
+//             256 ids to a partial (max, sum 2^((l - max) log2e / T)), in items drawn
+//             from shared counters so that all workgroups finish together.
+//   scan      one workgroup per stream: the logits at the draft tokens (bias in
+//             fp64), row normalisers from the partials (fp64), log p_j(x_j),
+//             log q_j(x_j), the token-wise stop and the clipped prefix P_i [P1 §4],
+//             and the rows whose residual mass is needed.  Block verification needs
+//             R_i only where u_{i-1} <= P_i (h_i <= P_i always), plus the row the
+//             sampler may land on.  The scan also packs the W1 tiles of those rows.
 //   pass2     like the draft half of pass1 over the listed rows only: per group,
 //             the residual mass sum max(0, P_i p_i - q_i) (Markov bias recomputed).
 //   finalize  one workgroup per stream: R_i, h_i, tau (top-down), then the
@@ -283,36 +285,51 @@ constexpr int kQueueStride = 32;
 
 // ---------------------------------------------------------------------------
 // pack: one wave per 16 draft rows (lane n + 16 q: row n, quarter q of each k-step).
-// (1) The W1 rows of the rows' previous tokens go into `btile` in MFMA lane order, so
-// that pass 1 reads a k-step of 16 rows as one contiguous 1 KB load.  (2) The logits
-// at each row's draft token: the target's t_j(x_j) and the drafter's d_j(x_j) plus
-// the Markov bias W1[prev] . W2t[x_j], summed in fp64 (each lane a quarter of the
-// rank, then the 4 lanes of the row), for the scan's log p_j(x_j) and log q_j(x_j).
-// Also clears the pass-2 list counts and the pass-1 item counter.
+// The W1 rows of the rows' previous tokens go into `btile` in MFMA lane order, so
+// that pass 1 reads a k-step of 16 rows as one contiguous 1 KB load; gathered here,
+// before pass 1 floods memory with logits, the scattered W1 rows arrive fast.  Rows
+// with no previous token get a zero tile.  Also clears the pass-2 list counts and
+// pass 1's item counters.
 // ---------------------------------------------------------------------------
-template <int DT>
 __global__ __launch_bounds__(64) void pack_kernel(Args a) {
   const int c = blockIdx.x, l = threadIdx.x, n = l & 15, q = l >> 4;
   if (c == 0 && l < 2) a.ws.nitems[l] = 0;
   if (c == 0 && l < kQueues) a.ws.nitems[kQueueStride * (1 + l)] = 0;
+  if (a.W1 == nullptr) return;
   const int ND = a.B * a.k;
-  const int dr = c * kChunk + n, drc = min(dr, ND - 1);
+  const int drc = min(c * kChunk + n, ND - 1);
   const int b = drc / a.k, j = drc - b * a.k;
-  // the three small loads go out together; the row loads below depend only on them
-  const int gam = stream_gamma(a, b);
-  const int pv = a.W1 != nullptr ? draft_prev(a, b, j) : -1;
-  const int x = clamp_tok(a.tokens[drc], a.V);
-  const bool act = dr < ND && j < gam;
-  const size_t esz = DT == kBF16 ? 2 : 4;
-  double lt = 0.0, ld = 0.0;
-  if (q == 0) {
-    lt = load1<DT>(reinterpret_cast<const char*>(a.target) + (size_t)(b * (a.k + 1) + j) * a.V * esz, x);
-    ld = load1<DT>(reinterpret_cast<const char*>(a.draft) + (size_t)drc * a.V * esz, x);
+  const int pv = draft_prev(a, b, j);
+  const int ks = a.R / 32;   // <= 8
+  uint4 v[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {   // unconditional loads (clamped row), masked after
+    const int kc = kk < ks ? kk : 0;
+    v[kk] = *reinterpret_cast<const uint4*>(a.W1 + (size_t)max(pv, 0) * a.R + kc * 32 + 8 * q);
   }
+  uint4* dst = a.ws.btile + (size_t)c * ks * 64 + l;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+    if (kk < ks) dst[kk * 64] = pv >= 0 ? v[kk] : make_uint4(0, 0, 0, 0);
+}
+
+// The logits at the token x_j of draft slot j of stream b, for log p_j(x_j) and
+// log q_j(x_j): the target's t_j(x_j), and the drafter's d_j(x_j) plus the Markov bias
+// W1[prev] . W2t[x_j], summed in fp64: lane (n, q) of the wave takes quarter q of
+// every 32-wide k-step (four running sums, one per 32-bit word), then the 4 lanes of
+// the row add up (xor 16, then xor 32).  The whole wave calls it; every lane gets its
+// row's (t, d + bias).  Loads are unconditional (clamped rows).
+// The caller reads pv = draft_prev(b, j) (or -1 without W1) and x = x_j beforehand,
+// so that their loads go out ahead of its other loads.
+template <int DT>
+__device__ __forceinline__ double2 token_logits(const Args& a, int b, int j, int pv, int x, int q) {
+  const int dr = b * a.k + j;
+  const size_t esz = DT == kBF16 ? 2 : 4;
+  const double lt = load1<DT>(reinterpret_cast<const char*>(a.target) + (size_t)(b * (a.k + 1) + j) * a.V * esz, x);
+  const double ld = load1<DT>(reinterpret_cast<const char*>(a.draft) + (size_t)dr * a.V * esz, x);
   double bias = 0.0;
   if (a.W1 != nullptr) {
     const int ks = a.R / 32;   // <= 8
-    const bool use = act && pv >= 0;
     uint4 v[8], y[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {   // unconditional loads (clamped row), masked after
@@ -322,11 +339,7 @@ __global__ __launch_bounds__(64) void pack_kernel(Args a) {
     }
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
-      if (!use || kk >= ks) v[kk] = make_uint4(0, 0, 0, 0);
-    uint4* dst = a.ws.btile + (size_t)c * ks * 64 + l;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      if (kk < ks) dst[kk * 64] = v[kk];
+      if (pv < 0 || kk >= ks) v[kk] = make_uint4(0, 0, 0, 0);
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
@@ -340,10 +353,7 @@ __global__ __launch_bounds__(64) void pack_kernel(Args a) {
     bias += __shfl_xor(bias, 16);
     bias += __shfl_xor(bias, 32);
   }
-  if (q == 0 && act) {
-    a.ws.glt[dr] = lt;
-    a.ws.gld[dr] = ld + bias;
-  }
+  return make_double2(lt, ld + bias);
 }
 
 // One k-step slice of a packed tile per lane: the B operand of 16 rows.
@@ -832,18 +842,28 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
   const int NT = a.B * k1, ND = a.B * a.k;
   const size_t esz = DT == kBF16 ? 2 : 4;
 
-  // the first row-statistics loads go out before the gathers below, so that both wait
-  // on memory together
+  // the draft tokens and their previous tokens first, then the first row-statistics
+  // loads, then the gathers at the tokens: each wait covers only what it needs
+  const bool gath = w < 2 && 16 * w < gamma;   // waves 0 and 1: slots 16 w + n (lane n + 16 q)
+  const int jg = min(16 * w + (l & 15), max(gamma - 1, 0));
+  int pv = -1, xg = 0;
+  if (gath) {
+    pv = a.W1 != nullptr ? draft_prev(a, b, jg) : -1;
+    xg = clamp_tok(a.tokens[b * a.k + jg], a.V);
+  }
   const int ngp = min(a.NG, kScanGroups);
   StageRegs sreg;
   stage_load(sreg, a, b, 0, min(kScanRows, gamma), min(kScanRows, gamma), 0, ngp, tid);
 
   if (tid < gamma) s_u[tid] = accept_uniform(a.key0, a.key1, (uint32_t)b, (uint32_t)tid, a.step);
 
-  // the logits at the drafts, gathered by the pack launch
-  if (tid < gamma) {
-    s_lt[tid] = a.ws.glt[b * a.k + tid];
-    s_ld[tid] = a.ws.gld[b * a.k + tid];
+  // the logits at the drafts
+  if (gath) {
+    const double2 tl = token_logits<DT>(a, b, jg, pv, xg, l >> 4);
+    if ((l >> 4) == 0 && 16 * w + (l & 15) < gamma) {
+      s_lt[jg] = tl.x;
+      s_ld[jg] = tl.y;
+    }
   }
 
   // row normalisers of target and draft rows 0..gamma-1 (the bonus row's statistics
@@ -1647,7 +1667,7 @@ static hipError_t launch_passes(const Args& a, hipStream_t st, void* const* ev) 
   };
   const int nchd = (a.B * a.k + kChunk - 1) / kChunk;
   mark(0);
-  hipLaunchKernelGGL((pack_kernel<DT>), dim3(nchd), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(pack_kernel, dim3(nchd), dim3(64), 0, st, a);
   mark(1);
   hipLaunchKernelGGL((pass1_kernel<DT, KS, MARKOV, VEC>), dim3(a.NG), dim3(kThreads), stream_table_bytes(a.B), st, a);
   mark(2);
