@@ -124,7 +124,9 @@ size_t dspark_workspace_bytes(const dspark_verify_problem* problem);
  * q_j includes the Markov bias W1[prev_j] . W2 [P2 §6; P1 §3 "The Markov fix-up"],
  * prev_0 = anchor, prev_j = x_{j-1}.
  * workspace: device, >= dspark_workspace_bytes(problem), 256-byte aligned; its
- * contents need no initialisation and are scratch after the call.
+ * contents need no initialisation and are scratch after the call.  It holds the
+ * call's work counters: calls that may run at the same time (other streams) need
+ * workspaces of their own; calls in order on one stream may share one.
  */
 dspark_status dspark_verify_tokenwise(const dspark_verify_problem* problem,
                                       const dspark_verify_outputs* out,
