@@ -15,10 +15,6 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # Atomics stay plain single-lane operations: the wave-level rewrite reads the
-    # result back at once, which would make pass 1's work-item claims wait for every
-    # load in flight instead of one item later.
-    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I", os.path.join(ROOT, "include"),
 ]
 

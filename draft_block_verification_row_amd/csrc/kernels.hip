@@ -574,6 +574,18 @@ __device__ __forceinline__ void pass1_draft(const Args& a, const StreamTable& st
 // of that residue class (one counter for the whole grid serialises ~2500 atomics on
 // one address).  Thread 0 claims one item ahead (in `pend`), so the counter's round
 // trip is hidden behind an item's loads.
+// One claim: a plain single-lane atomic.  The address goes through a VGPR the compiler
+// cannot see into, so the atomic optimizer (which rewrites an atomic on a uniform
+// address into a wave-level one whose result is read back at once) leaves it alone,
+// and the result is waited for only where it is used, one item later.
+typedef __attribute__((address_space(1))) int global_int;   // a global (not flat) address
+
+__device__ __forceinline__ int claim_add(int* p) {
+  uintptr_t v = reinterpret_cast<uintptr_t>(p);
+  asm volatile("" : "+v"(v));
+  return __hip_atomic_fetch_add(reinterpret_cast<global_int*>(v), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int DT>
 struct TargetQueue {
   static constexpr int U = DT == kBF16 ? 4 : 2;
@@ -612,7 +624,7 @@ __device__ __forceinline__ void pass1_target(const Args& a, const StreamTable& s
   auto claim = [&]() {
     if (tid == 0) {
       tq.slot[tq.par] = tq.pend;
-      tq.pend = atomicAdd(a.ws.nitems + kQueueStride * (1 + qx), 1);
+      tq.pend = claim_add(a.ws.nitems + kQueueStride * (1 + qx));
     }
     __syncthreads();
     const int i = qx + nq * __builtin_amdgcn_readfirstlane(tq.slot[tq.par]);
@@ -678,7 +690,7 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_kernel(Args a) {
   const StreamTable st = build_stream_table(a, smem);
   const int g = blockIdx.x;
   TargetQueue<DT> tq{qslot, 0, 0};
-  if (threadIdx.x == 0) tq.pend = atomicAdd(a.ws.nitems + kQueueStride * (1 + g % min(kQueues, (int)gridDim.x)), 1);
+  if (threadIdx.x == 0) tq.pend = claim_add(a.ws.nitems + kQueueStride * (1 + g % min(kQueues, (int)gridDim.x)));
   pass1_draft<DT, KS, MARKOV, VEC>(a, st, g, part, bst);
   pass1_target<DT, VEC>(a, st, tq);
 }
