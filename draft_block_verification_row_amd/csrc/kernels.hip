@@ -399,19 +399,23 @@ struct StreamTable {
   bool any_greedy;
 };
 
-__device__ __forceinline__ StreamTable build_stream_table(const Args& a, char* smem) {
+// T0, gam0: stream threadIdx.x's temperature and draft count when the caller has
+// loaded them already (pass 1 issues those loads ahead of its W2 slab); NaN = not loaded.
+__device__ __forceinline__ StreamTable build_stream_table(const Args& a, char* smem, float T0 = NAN, int gam0 = 0) {
   float* tc = reinterpret_cast<float*>(smem);
   int* gam = reinterpret_cast<int*>(smem + align16((size_t)a.B * sizeof(float)));
   int* flag = reinterpret_cast<int*>(smem + align16((size_t)a.B * sizeof(float)) + align16((size_t)a.B * sizeof(int)));
   if (threadIdx.x == 0) flag[0] = 0;
   __syncthreads();
-  for (int b = threadIdx.x; b < a.B; b += kThreads) {
-    const float T = stream_temp(a, b);
+  auto put = [&](int b, float T, int gm) {
     // T = 0 (greedy) only needs the row maxima: any finite positive c keeps the sums finite
     tc[b] = T > 0.f ? (float)(kLog2e / (double)T) : kGreedyTcValue;
-    gam[b] = stream_gamma(a, b);
+    gam[b] = gm;
     if (!(T > 0.f)) flag[0] = 1;
-  }
+  };
+  const bool pre = !isnan(T0);
+  if (pre && (int)threadIdx.x < a.B) put(threadIdx.x, T0, gam0);
+  for (int b = threadIdx.x + (pre ? kThreads : 0); b < a.B; b += kThreads) put(b, stream_temp(a, b), stream_gamma(a, b));
   __syncthreads();
   return StreamTable{tc, gam, flag[0] != 0};
 }
@@ -478,7 +482,8 @@ __device__ __forceinline__ void tile_stage_store(const TileStage<KS>& t, uint4* 
 // batch (at most kStage - 1) run with clamped loads and write nothing.
 template <int DT, int KS, bool MARKOV, bool VEC>
 __device__ __forceinline__ void pass1_draft(const Args& a, const StreamTable& st, int g,
-                                            float2 (*part)[kWaves], uint4* bst) {
+                                            float2 (*part)[kWaves], uint4* bst, const bf16x8 (&A)[4][KS],
+                                            TileStage<KS>& stage) {
   constexpr int PD = 2;   // logits prefetch distance (chunks)
   static_assert(kStage % PD == 0 && kFlush % kStage == 0, "block, ring and flush sizes must nest");
   static_assert(TileStage<KS>::kUnits % kThreads == 0, "a staged block must split evenly");
@@ -508,14 +513,6 @@ __device__ __forceinline__ void pass1_draft(const Args& a, const StreamTable& st
     raw_load<DT, VEC>(x, base + (size_t)src * rb, c0, a.V);
   };
 
-  bf16x8 A[4][KS];
-  TileStage<KS> stage;
-  if (MARKOV) {
-    load_w2_slab<KS, VEC>(a, cb, n, q, A);
-    tile_stage_load<KS>(a, 0, nch, stage);
-    tile_stage_store<KS>(stage, bst);
-    tile_stage_load<KS>(a, 1, nch, stage);
-  }
   auto chunk = [&](int c, const uint4* tiles, Raw16<DT>& xb) {
     float x[16];
     raw_to_f32<DT>(xb, x);
@@ -544,9 +541,15 @@ __device__ __forceinline__ void pass1_draft(const Args& a, const StreamTable& st
       __syncthreads();
     }
   };
+  // the first chunks' logits go out before the wait for the W2 slab and tile block 0
+  // (issued by the kernel before the stream table), so they arrive meanwhile
   Raw16<DT> xb[PD];   // ring of logits buffers, indexed at compile time
 #pragma unroll
   for (int i = 0; i < PD; ++i) load_x(i, xb[i]);
+  if (MARKOV) {
+    tile_stage_store<KS>(stage, bst);
+    tile_stage_load<KS>(a, 1, nch, stage);
+  }
   __syncthreads();   // block 0 of the tiles is in LDS
   for (int j = 0; j < nblk; ++j) {
     const uint4* tiles = bst + (j & 1) * TileStage<KS>::kUnits;
@@ -687,11 +690,27 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_kernel(Args a) {
   __shared__ float2 part[kFlush * kChunk][kWaves];
   __shared__ uint4 bst[MARKOV ? 2 * TileStage<KS>::kUnits : 1];   // 64 KB at R = 256
   __shared__ int qslot[2];
-  const StreamTable st = build_stream_table(a, smem);
   const int g = blockIdx.x;
+  // Issue order: this thread's stream's temperature and draft count, then the W2 slab
+  // and the first W1 tile block (which do not depend on the stream table), so that
+  // building the table waits only for its own two loads and the slab, the launch's
+  // longest wait, starts at once.
+  const int tb = min((int)threadIdx.x, a.B - 1);
+  const float T0 = a.temperature != nullptr ? a.temperature[tb] : 1.0f;    // raw: used after the
+  const int n0 = a.num_drafts != nullptr ? a.num_drafts[tb] : a.k;          // slab loads below
+  bf16x8 A[4][KS];
+  TileStage<KS> stage;
+  if (MARKOV) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    load_w2_slab<KS, VEC>(a, g * kGroup + w * kWaveCols, l & 15, l >> 4, A);
+    tile_stage_load<KS>(a, 0, (a.B * a.k + kChunk - 1) / kChunk, stage);
+  }
+  __builtin_amdgcn_sched_barrier(0);   // keep the uses of T0 and n0 after the loads above
+  const StreamTable st = build_stream_table(a, smem, (int)threadIdx.x < a.B ? T0 : NAN,
+                                            n0 < 0 ? 0 : (n0 > a.k ? a.k : n0));
   TargetQueue<DT> tq{qslot, 0, 0};
   if (threadIdx.x == 0) tq.pend = claim_add(a.ws.nitems + kQueueStride * (1 + g % min(kQueues, (int)gridDim.x)));
-  pass1_draft<DT, KS, MARKOV, VEC>(a, st, g, part, bst);
+  pass1_draft<DT, KS, MARKOV, VEC>(a, st, g, part, bst, A, stage);
   pass1_target<DT, VEC>(a, st, tq);
 }
 
