@@ -1415,14 +1415,35 @@ __global__ __launch_bounds__(kThreads, 2) void walk_partials_kernel(Args a, int 
   const bool rag = VEC && cb + kWaveCols > a.V;
   const size_t rb = (size_t)a.V * (DT == kBF16 ? 2 : 4);
   const char* base = reinterpret_cast<const char*>(a.draft);
+  // A block's inputs (previous tokens, temperatures, the slot's logits rows) are loaded
+  // one block ahead; the first block's go out before the W2 slab, so that staging
+  // them waits only for them while the slab is in flight.
+  constexpr int NC = kWalkRows / kChunk;
+  // raw values, loaded without branches (a load under a branch makes the compiler wait
+  // for every load in flight where the paths join) and checked at use
+  int pv = -1;     // the anchor, or x_{j-1} from the previous slot
+  float T = 1.f;   // the stream's temperature
+  Raw16<DT> xr[NC];
+  auto load_block = [&](int r0) {
+    const int b = min(r0 + (tid & (kWalkRows - 1)), a.B - 1);
+    const int32_t* ps = j > 0 ? a.tokens + b * a.k + j - 1 : (a.anchor ? a.anchor + b : a.tokens + b * a.k);
+    const float* ts = a.temperature ? a.temperature + b : reinterpret_cast<const float*>(a.tokens + b * a.k);
+    pv = *ps;
+    T = *ts;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+      raw_load<DT, VEC>(xr[cc], base + ((size_t)min(r0 + cc * kChunk + n, a.B - 1) * a.k + j) * rb, c0, a.V);
+  };
+  load_block(0);
   bf16x8 A[4][KS];
   if (MARKOV) load_w2_slab<KS, VEC>(a, cb, n, q, A);
+  __builtin_amdgcn_sched_barrier(0);   // keep the uses of the block's inputs after the slab loads
   for (int r0 = 0; r0 < a.B; r0 += kWalkRows) {
     if (tid < kWalkRows) {
-      const int b = min(r0 + tid, a.B - 1);
-      s_prev[tid] = draft_prev(a, b, j);   // the anchor, or x_{j-1} from the previous slot
-      const float T = stream_temp(a, b);
-      s_c[tid] = T > 0.f ? (float)(kLog2e / (double)T) : 1e-30f;
+      const bool has = j > 0 || a.anchor != nullptr;
+      s_prev[tid] = (has && pv >= 0 && pv < a.V) ? pv : -1;   // as draft_prev
+      const float Tb = a.temperature ? T : 1.f;                  // as stream_temp
+      s_c[tid] = Tb > 0.f ? (float)(kLog2e / (double)Tb) : 1e-30f;
     }
     __syncthreads();
     if (MARKOV) {   // stage the block's W1 rows: whole rows per wave instruction
@@ -1436,13 +1457,10 @@ __global__ __launch_bounds__(kThreads, 2) void walk_partials_kernel(Args a, int 
       __syncthreads();
     }
 #pragma unroll
-    for (int cc = 0; cc < kWalkRows / kChunk; ++cc) {
+    for (int cc = 0; cc < NC; ++cc) {
       const int rr = cc * kChunk + n;              // row within the block
-      const int b = min(r0 + rr, a.B - 1);
-      Raw16<DT> xr;
-      raw_load<DT, VEC>(xr, base + ((size_t)b * a.k + j) * rb, c0, a.V);
       float x[16];
-      raw_to_f32<DT>(xr, x);
+      raw_to_f32<DT>(xr[cc], x);
       if (MARKOV) {
         bf16x8 Bop[KS];
 #pragma unroll
@@ -1461,6 +1479,7 @@ __global__ __launch_bounds__(kThreads, 2) void walk_partials_kernel(Args a, int 
       for (int ww = 0; ww < kWaves; ++ww) p[ww] = part[tid][ww];
       a.ws.tpart[(size_t)g * a.B + r0 + tid] = combine_waves(p, s_c[tid]);
     }
+    if (r0 + kWalkRows < a.B) load_block(r0 + kWalkRows);   // uniform
     __syncthreads();
   }
 }
