@@ -43,7 +43,7 @@ Layout layout(int B, int k, int V) {
       (size_t)B * 4 * sizeof(int32_t),  // info
       (size_t)B * sizeof(uint32_t),     // rowmask
       BD * sizeof(Item),                // items
-      9 * 32 * sizeof(int32_t),         // nitems (residual rows, bonus rows; pass-1 item counters)
+      kCounterInts * sizeof(int32_t),   // nitems: list counts and pass-1 item counters
       tiles * 8 * 64 * sizeof(uint4),   // btile (sized for the largest rank, R = 256)
   };
   Layout L;

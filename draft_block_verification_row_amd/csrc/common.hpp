@@ -14,6 +14,14 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kMaxK = 32;
 constexpr int kChunk = 16;         // rows per MFMA chunk
 
+// Counters in the workspace's `nitems` region: [0] residual rows and [1] bonus rows of
+// the pass-2 list, then pass 1's target-item counters, kQueueStride ints (a 128-byte
+// line) apart from each other (workgroup g draws from counter g % min(kQueues, grid),
+// items of its own residue class).  All are cleared by the pack launch.
+constexpr int kQueues = 8;
+constexpr int kQueueStride = 32;
+constexpr int kCounterInts = kQueueStride * (1 + kQueues);
+
 constexpr double kLog2e = 1.4426950408889634074;
 constexpr double kLn2 = 0.69314718055994530942;
 
@@ -144,7 +152,7 @@ struct Workspace {
   int32_t* info;      // [B*4]         gamma, stop (token-wise t / block provisional), f, flags
   uint32_t* rowmask;  // [B]           pass-2 rows of each stream (bit i = slot i)
   Item* items;        // [B*k]         pass-2 list: residual rows from the front, bonus rows from the back
-  int32_t* nitems;    // [4]           residual rows, bonus rows, pass-1 target items claimed
+  int32_t* nitems;    // [kCounterInts] list counts and work counters (see kQueues)
   uint4* btile;       // [ceil(B*k/16)][R/32][64] W1 tiles of pass 2's rows in MFMA lane order
 };
 

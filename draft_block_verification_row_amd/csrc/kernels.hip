@@ -278,11 +278,6 @@ __device__ __forceinline__ float2 row_partial(const float (&x)[16], float c) {
 // lies at least 1/(2d) from an integer and the two fp32 roundings move it by less.
 __device__ __forceinline__ int div_small(int i, float hd) { return (int)((float)(2 * i + 1) * hd); }
 
-// Pass 1 hands out its target items from kQueues counters (workgroup g uses counter
-// g % min(kQueues, grid), items of its own residue class), kQueueStride ints apart.
-constexpr int kQueues = 8;
-constexpr int kQueueStride = 32;
-
 // ---------------------------------------------------------------------------
 // pack: one wave per 16 draft rows (lane n + 16 q: row n, quarter q of each k-step).
 // The W1 rows of the rows' previous tokens go into `btile` in MFMA lane order, so
