@@ -11,7 +11,9 @@ finds its inputs in the 256 MB Infinity Cache.
 
 Prints one JSON line.  ``value`` = verified draft blocks per second.
 ``roofline`` is for the dominant launch (row statistics, pass 1), timed with
-HIP events recorded around it by the library's stage hook on the same stream.
+HIP events recorded around it by the library's stage hook on the same stream,
+and compared both with the published HBM peak and with a plain streaming read
+measured on the same device (the package's stream-read kernel).
 ``cpu_baseline`` is the fp64 oracle on the host, on the same batch.
 """
 from __future__ import annotations
@@ -81,6 +83,43 @@ class HipEvents:
     def destroy(self, evs):
         for e in evs:
             self.h.hipEventDestroy(e)
+
+
+def read_ceiling(torch, dev, nbytes=1 << 30, nbuf=3, reps=12):
+    """Measured streaming-read rate of the device: the package's plain read kernel over
+    nbuf rotating buffers of nbytes (together well beyond the Infinity Cache), at a few
+    grid sizes; returns the best (GB/s, grid)."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    L = ctypes.CDLL(os.path.join(here, "draft_block_verification_row_amd", "libdspark_stream_read.so"))
+    L.dspark_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    L.dspark_stream_read.restype = ctypes.c_int
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    bufs = [torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=dev, generator=gen) for _ in range(nbuf)]
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+
+    def launch(i, grid):
+        if L.dspark_stream_read(bufs[i % nbuf].data_ptr(), nbytes, grid, sink.data_ptr(), stream) != 0:
+            raise RuntimeError("dspark_stream_read failed")
+
+    best = (0.0, 0)
+    for grid in (2048, 4096, 8192, 16384):
+        for i in range(nbuf):
+            launch(i, grid)
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(reps):
+            launch(i, grid)
+        t1.record()
+        torch.cuda.synchronize()
+        gbps = reps * nbytes / (t0.elapsed_time(t1) * 1e-3) / 1e9
+        best = max(best, (gbps, grid))
+    del bufs
+    return best
 
 
 def alg_bytes(B, k, V, R, e, s, gamma) -> float:
@@ -238,6 +277,16 @@ def main() -> int:
         "logits_per_s": round(2 * B * k * V / (ms_step * 1e-3), 1),
         "step_alg_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "accepted_mean": {m: round(float(np.mean(realized[m])), 4) for m in realized},
+    }
+
+    # the measured read ceiling of this device, beside the published peak
+    log("timing a plain streaming read (3 x 1 GiB buffers)")
+    ceil_gbps, ceil_grid = read_ceiling(torch, dev)
+    result["roofline"]["measured_read_GBps"] = round(ceil_gbps, 1)
+    result["roofline"]["frac_of_measured_read"] = round(achieved / ceil_gbps, 4)
+    result["stream_read_ceiling"] = {
+        "GBps": round(ceil_gbps, 1), "grid": ceil_grid, "bytes_per_launch": 1 << 30, "buffers": 3,
+        "kernel": "dspark_stream_read: grid-stride 16-B loads, 256-thread groups, random bytes",
     }
 
     # the drafter's Markov walk at the same shape (the step before verification)

@@ -1,4 +1,6 @@
-"""Build libdspark_verify.so in-tree with hipcc for gfx950.
+"""Build libdspark_verify.so in-tree with hipcc for gfx950, and beside it
+libdspark_stream_read.so (a plain streaming read: the measured read ceiling that
+the throughput measurement compares the row-statistics pass with).
 
 Usage: python -m draft_block_verification_row_amd.build
 """
@@ -10,6 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SOURCES = [os.path.join(PKG, "csrc", f) for f in ("api.hip", "kernels.hip", "schedule.hip")]
 LIB = os.path.join(PKG, "libdspark_verify.so")
+READ_SOURCES = [os.path.join(PKG, "csrc", "stream_read.hip")]
+READ_LIB = os.path.join(PKG, "libdspark_stream_read.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -19,10 +23,9 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the HIP library (always recompiles) and return its path."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + SOURCES + ["-o", tmp]
+def _compile(sources, lib, verbose):
+    tmp = lib + ".tmp"
+    cmd = [HIPCC] + FLAGS + sources + ["-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (res.stderr or "").splitlines() if noise not in l)
@@ -30,7 +33,13 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + err)
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile both HIP libraries (always recompiles) and return the sampler's path."""
+    _compile(SOURCES, LIB, verbose)
+    _compile(READ_SOURCES, READ_LIB, verbose)
     return LIB
 
 

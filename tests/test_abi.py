@@ -129,3 +129,21 @@ def test_draft_scatter_host_errors():
     assert L.dspark_draft_scatter(None, 256, 2, 4, 10, 1, 256, None) == 1
     assert L.dspark_draft_scatter(256, 256, 2, 11, 10, 1, 256, None) == 1   # K > V
     assert L.dspark_draft_scatter(256, 256, 0, 4, 10, 1, 256, None) == 0    # nothing to do
+
+
+def test_stream_read_library_loads():
+    """The measured-read-ceiling library beside the sampler builds, loads and exports
+    its one function; argument checks run on the host (no launch)."""
+    m = _built_lib()
+    path = os.path.join(os.path.dirname(m.LIB_PATH), "libdspark_stream_read.so")
+    if not os.path.exists(path):
+        from draft_block_verification_row_amd import build
+        build.build()
+    L = ctypes.CDLL(path)
+    f = L.dspark_stream_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(None, 16, 1, 16, None) == 1            # null source
+    assert f(16, 24, 1, 16, None) == 1              # size not a multiple of 16
+    assert f(16, 16, 0, 16, None) == 1              # empty grid
+    assert f(16, 0, 1, 16, None) == 0               # nothing to read: no launch
