@@ -801,6 +801,8 @@ __device__ __forceinline__ void stage_reduce(const ScanLds& sh, int w, int l, in
 // every draft is kept).  The argmax of a target row comes from its group maxima (raw
 // logits, exact): the first group that reaches the row maximum, then the first id of
 // that group holding it.  No residual pass and no sampler are involved.
+constexpr int kLoadsInFlight = 8;   // per lane, in the per-wave loops over group partials
+
 template <int DT>
 __device__ __forceinline__ void greedy_scan(const Args& a, int b, int gamma) {
   __shared__ int s_am[kMaxK + 1];
@@ -809,12 +811,35 @@ __device__ __forceinline__ void greedy_scan(const Args& a, int b, int gamma) {
   const size_t rb = (size_t)a.V * (DT == kBF16 ? 2 : 4);
   for (int r = w; r <= gamma; r += kWaves) {   // one wave per target row
     const int row = b * k1 + r;
+    // the group maxima of lane l are groups l + 64 u: loaded 8 at a time (clamped
+    // index, masked after), kept for the index search when they all fit
+    float gm[kLoadsInFlight];
+    auto load_maxima = [&](int g0) {
+#pragma unroll
+      for (int u = 0; u < kLoadsInFlight; ++u)
+        gm[u] = a.ws.tpart[(size_t)min(g0 + l + 64 * u, NG - 1) * NT + row].x;
+    };
+    load_maxima(0);
     float M = -INFINITY;
-    for (int g = l; g < NG; g += 64) M = fmaxf(M, a.ws.tpart[(size_t)g * NT + row].x);
+    for (int g0 = 0;;) {
+#pragma unroll
+      for (int u = 0; u < kLoadsInFlight; ++u)
+        if (g0 + l + 64 * u < NG) M = fmaxf(M, gm[u]);
+      g0 += 64 * kLoadsInFlight;
+      if (g0 >= NG) break;
+      load_maxima(g0);
+    }
     for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     int gs = 0x7fffffff;
-    for (int g = l; g < NG; g += 64)
-      if (a.ws.tpart[(size_t)g * NT + row].x == M) gs = min(gs, g);
+    if (NG > 64 * kLoadsInFlight) load_maxima(0);
+    for (int g0 = 0;;) {
+#pragma unroll
+      for (int u = 0; u < kLoadsInFlight; ++u)
+        if (g0 + l + 64 * u < NG && gm[u] == M) gs = min(gs, g0 + l + 64 * u);
+      g0 += 64 * kLoadsInFlight;
+      if (g0 >= NG) break;
+      load_maxima(g0);
+    }
     for (int off = 32; off >= 1; off >>= 1) gs = min(gs, __shfl_xor(gs, off));
     gs = gs < NG ? gs : 0;
     int vs = 0x7fffffff;
@@ -1263,8 +1288,18 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
       if (!((mask >> i) & 1u)) continue;
       if ((ci & (kWaves - 1)) == w) {
         const int dr = b * a.k + i;
+        // 8 loads in flight per lane (clamped index, masked after); each lane still
+        // adds its groups l, l + 64, ... in increasing order
         double v = 0.0;
-        for (int gi = l; gi < NG; gi += 64) v += (double)a.ws.wgrp[(size_t)gi * ND + dr];
+        for (int g0 = 0; g0 < NG; g0 += 64 * kLoadsInFlight) {
+          float x[kLoadsInFlight];
+#pragma unroll
+          for (int u = 0; u < kLoadsInFlight; ++u)
+            x[u] = a.ws.wgrp[(size_t)min(g0 + l + 64 * u, NG - 1) * ND + dr];
+#pragma unroll
+          for (int u = 0; u < kLoadsInFlight; ++u)
+            if (g0 + l + 64 * u < NG) v += (double)x[u];
+        }
         v = wave_sum(v);
         if (l == 0) {
           s_R[i] = v;
@@ -1491,26 +1526,38 @@ __global__ __launch_bounds__(kThreads) void walk_pick_kernel(Args a, int j, int3
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int NG = a.NG;
-  if (j >= stream_gamma(a, b)) {
+  // the stream's draft count, temperature and previous token, and a thread's first
+  // two group partials, go out together: branch-free addresses (the tokens drawn so
+  // far stand in for an absent input, whose value is then replaced)
+  const int graw = *(a.num_drafts != nullptr ? a.num_drafts + b : a.tokens);
+  const float traw = *(a.temperature != nullptr ? a.temperature + b : reinterpret_cast<const float*>(a.tokens));
+  const int praw = *(j > 0 ? a.tokens + b * a.k + j - 1 : (a.anchor != nullptr ? a.anchor + b : a.tokens));
+  const float2 p0 = a.ws.tpart[(size_t)min(tid, NG - 1) * a.B + b];
+  const float2 p1 = a.ws.tpart[(size_t)min(tid + kThreads, NG - 1) * a.B + b];
+  __builtin_amdgcn_sched_barrier(0);
+  const int gamma = a.num_drafts != nullptr ? (graw < 0 ? 0 : (graw > a.k ? a.k : graw)) : a.k;
+  if (j >= gamma) {
     if (tid == 0) {
       tokens_out[b * a.k + j] = -1;
       if (logq_out != nullptr) logq_out[b * a.k + j] = NAN;
     }
     return;
   }
-  const float Tf = stream_temp(a, b);
+  const float Tf = a.temperature != nullptr ? traw : 1.0f;
   const bool greedy = Tf == 0.f;
   const double invT = greedy ? 0.0 : 1.0 / (double)Tf;
-  const int prev = draft_prev(a, b, j);
+  const int pr = (j > 0 || a.anchor != nullptr) ? praw : -1;
+  const int prev = (pr >= 0 && pr < a.V) ? pr : -1;
   const size_t esz = DT == kBF16 ? 2 : 4;
   const char* drow = reinterpret_cast<const char*>(a.draft) + ((size_t)b * a.k + j) * a.V * esz;
   // group choice: the largest maximum (greedy) or the race over group masses
   double best = -INFINITY;
   int gbest = 0x7fffffff;
   double lmax = -INFINITY;   // for log q: max over groups of m_g / T + ln s_g
-  for (int gi = tid; gi < NG; gi += kThreads) {
-    const float2 p = a.ws.tpart[(size_t)gi * a.B + b];
-    if (p.x == -INFINITY) continue;
+  // a thread's groups in increasing order: the first two were loaded above (clamped
+  // index) and serve log q too
+  auto race_group = [&](int gi, float2 p) {
+    if (gi >= NG || p.x == -INFINITY) return;
     double sc;
     if (greedy) {
       sc = (double)p.x;
@@ -1520,7 +1567,10 @@ __global__ __launch_bounds__(kThreads) void walk_pick_kernel(Args a, int j, int3
       sc = lw - log(race_clock(a.key0, a.key1, (uint32_t)b, (uint32_t)gi, walk_purpose_group(j), a.step));
     }
     if (sc > best) { best = sc; gbest = gi; }
-  }
+  };
+  race_group(tid, p0);
+  race_group(tid + kThreads, p1);
+  for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) race_group(gi, a.ws.tpart[(size_t)gi * a.B + b]);
   block_max_index(best, gbest, rs, ri);
   const int gsel = gbest < NG ? gbest : 0;
   // inside the group: biased logits in fp64 (the Markov bias from one cooperative pass
@@ -1545,10 +1595,12 @@ __global__ __launch_bounds__(kThreads) void walk_pick_kernel(Args a, int j, int3
     m = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
     __syncthreads();
     double s = 0.0;
-    for (int gi = tid; gi < NG; gi += kThreads) {
-      const float2 p = a.ws.tpart[(size_t)gi * a.B + b];
-      if (p.x != -INFINITY) s += exp((double)p.x * invT + log((double)p.y) - m);
-    }
+    auto add_group = [&](int gi, float2 p) {
+      if (gi < NG && p.x != -INFINITY) s += exp((double)p.x * invT + log((double)p.y) - m);
+    };
+    add_group(tid, p0);
+    add_group(tid + kThreads, p1);
+    for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) add_group(gi, a.ws.tpart[(size_t)gi * a.B + b]);
     s = block_sum(s, red);
     if (tid == x - gsel * kGroup) logq_out[b * a.k + j] = xv * invT - (m + log(s));
   } else if (tid == 0 && logq_out != nullptr) {
