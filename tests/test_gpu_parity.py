@@ -165,3 +165,23 @@ def test_run_to_run_bit_identical(mod):
         assert np.array_equal(a["accepted_len"], b["accepted_len"])
         assert np.array_equal(a["out_tokens"], b["out_tokens"])
         assert np.array_equal(np.nan_to_num(a["diag"], nan=7.0), np.nan_to_num(b["diag"], nan=7.0))
+
+
+@pytest.mark.parametrize("method", ["tokenwise", "block"])
+def test_maximum_draft_count(mod, method):
+    """k = 32 (the largest block the library takes): six passes of row statistics in
+    the scan, a 32-bit candidate mask; ragged counts from 0 to 32 and a greedy stream."""
+    wl = workloads.make_zipf("maxk", seed=32, B=4, k=32, V=700, dtype="bf16", R=64, sigma=1.5,
+                             rho=(0.8, 0.995), greedy_every=4)
+    wl.num_drafts = np.array([32, 0, 17, 31], dtype=np.int32)
+    _run(mod, wl, method, range(4), "k32")
+
+
+@pytest.mark.parametrize("method", ["tokenwise", "block"])
+def test_batch_wider_than_a_workgroup(mod, method):
+    """B = 600 streams (more than the 256 threads that fill the per-workgroup stream
+    table in one step), mixed greedy and sampled, ragged counts."""
+    wl = workloads.make_zipf("wideB", seed=600, B=600, k=2, V=300, dtype="bf16", R=32, sigma=1.5,
+                             rho=(0.6, 0.99), greedy_every=5)
+    wl.num_drafts = (np.arange(600) % 3).astype(np.int32)
+    _run(mod, wl, method, range(2), "B600")
