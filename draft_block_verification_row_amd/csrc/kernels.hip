@@ -1689,7 +1689,7 @@ __global__ __launch_bounds__(kThreads) void markov_bias_kernel(BiasArgs ba) {
 // loads of all 4 slots are in flight together; the dot products accumulate in fp64.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void adaptive_kernel(AdaptArgs aa) {
-  constexpr int kSlots = 4;   // slots whose hidden states are in flight together
+  constexpr int kSlots = 8;   // slots whose hidden states are in flight together (k <= 8: one round)
   __shared__ double s_part[kWaves][kMaxK];
   __shared__ double s_c[kMaxK];
   const int b = blockIdx.x;
@@ -1697,24 +1697,37 @@ __global__ __launch_bounds__(kThreads) void adaptive_kernel(AdaptArgs aa) {
   // w . h for every slot: the whole workgroup splits H, each wave sums its share in
   // fp64 and the 4 wave sums meet in LDS
   for (int j0 = 0; j0 < aa.k; j0 += kSlots) {
-    double acc[kSlots] = {0.0, 0.0, 0.0, 0.0};
+    double acc[kSlots];
+#pragma unroll
+    for (int sl = 0; sl < kSlots; ++sl) acc[sl] = 0.0;
     const uint16_t* h[kSlots];
 #pragma unroll
     for (int sl = 0; sl < kSlots; ++sl) h[sl] = aa.hidden + ((size_t)b * aa.k + min(j0 + sl, aa.k - 1)) * aa.H;
     if (aa.vec_ok) {   // H % 8 == 0 and 16-byte aligned rows
-#pragma unroll 2
-      for (int c0 = 8 * tid; c0 < aa.H; c0 += 8 * kThreads) {
-        const uint4 wv = *reinterpret_cast<const uint4*>(aa.w + c0);
-        uint4 hv[kSlots];
+      // two steps of 8 ids per thread at a time (H = 4096: all of a slot's loads at
+      // once): clamped addresses, the past-the-end step masked after
+      constexpr int kSteps = 2;
+      for (int c00 = 8 * tid; c00 < aa.H; c00 += 8 * kThreads * kSteps) {
+        uint4 wv[kSteps], hv[kSteps][kSlots];
 #pragma unroll
-        for (int sl = 0; sl < kSlots; ++sl) hv[sl] = *reinterpret_cast<const uint4*>(h[sl] + c0);
-        const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+        for (int it = 0; it < kSteps; ++it) {
+          const int cc = min(c00 + 8 * kThreads * it, aa.H - 8);
+          wv[it] = *reinterpret_cast<const uint4*>(aa.w + cc);
 #pragma unroll
-        for (int sl = 0; sl < kSlots; ++sl) {
-          const uint32_t hh[4] = {hv[sl].x, hv[sl].y, hv[sl].z, hv[sl].w};
+          for (int sl = 0; sl < kSlots; ++sl) hv[it][sl] = *reinterpret_cast<const uint4*>(h[sl] + cc);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // every load above goes out before any use
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[sl] += (double)bf16lo(hh[i]) * (double)bf16lo(ww[i]) + (double)bf16hi(hh[i]) * (double)bf16hi(ww[i]);
+        for (int it = 0; it < kSteps; ++it) {
+          if (c00 + 8 * kThreads * it >= aa.H) continue;
+          const uint32_t ww[4] = {wv[it].x, wv[it].y, wv[it].z, wv[it].w};
+#pragma unroll
+          for (int sl = 0; sl < kSlots; ++sl) {
+            const uint32_t hh[4] = {hv[it][sl].x, hv[it][sl].y, hv[it][sl].z, hv[it][sl].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[sl] += (double)bf16lo(hh[i]) * (double)bf16lo(ww[i]) + (double)bf16hi(hh[i]) * (double)bf16hi(ww[i]);
+          }
         }
       }
     } else {
