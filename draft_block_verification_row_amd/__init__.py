@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.argtypes = [ctypes.POINTER(VerifyProblem), ctypes.POINTER(VerifyOutputs), vp, sz, vp]
             f.restype = i32
+        L.dspark_verify_noalloc.argtypes = [ctypes.POINTER(VerifyProblem), ctypes.POINTER(VerifyOutputs), i32, vp]
+        L.dspark_verify_noalloc.restype = i32
         L.dspark_draft_sample.argtypes = [ctypes.POINTER(VerifyProblem), vp, vp, vp, sz, vp]
         L.dspark_draft_sample.restype = i32
         L.dspark_draft_scatter.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
@@ -206,6 +208,31 @@ def verify_tokenwise(target, draft, draft_tokens, **kw):
 def verify_block(target, draft, draft_tokens, **kw):
     """Block verification; returns (accepted_len [B], out_tokens [B, k+1], diag or None)."""
     return _verify("dspark_verify_block", target, draft, draft_tokens, **kw)
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+_METHODS = {"tokenwise": 0, "block": 1}
+
+
+def verify_noalloc(method, target, draft, draft_tokens, num_drafts=None, temperature=None, W1=None, W2t=None,
+                   anchor=None, seed=0, step=0, diag=False, out=None):
+    """Either verifier on the library's static per-device scratch (no workspace, no
+    allocation inside the call).  ``method`` is "tokenwise" or "block".  Output
+    tensors are allocated here unless ``out`` = (accepted_len, out_tokens, diag or
+    None) is given.  Calls that overlap on one device race on the shared scratch."""
+    if method not in _METHODS:
+        raise ValueError(f"method must be one of {sorted(_METHODS)}")
+    p, (B, k, V) = _problem(target, draft, draft_tokens, num_drafts, temperature, W1, W2t, anchor, seed, step)
+    dev = target.device
+    if out is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        toks = torch.empty(B, k + 1, dtype=torch.int32, device=dev)
+        dg = torch.empty(B, k + 1, 5, dtype=torch.float64, device=dev) if diag else None
+    else:
+        acc, toks, dg = out
+    o = VerifyOutputs(accepted_len=_ptr(acc), out_tokens=_ptr(toks), diag=_ptr(dg), stage_events=None)
+    _check(lib().dspark_verify_noalloc(ctypes.byref(p), ctypes.byref(o), _METHODS[method], _stream(dev)))
+    return acc, toks, dg
 
 
 def draft_sample(draft, num_drafts=None, temperature=None, W1=None, W2t=None, anchor=None, seed=0, step=0,

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/dspark_verify.h"
 #include "common.hpp"
 
@@ -158,9 +160,48 @@ dspark_status walk_common(const dspark_verify_problem* p, int32_t* tokens_out, d
   return DSPARK_OK;
 }
 
+// Scratch of the allocation-free verify entry point: one copy per device, held until
+// the process ends.  Host code never passes `scratch` itself to a kernel (in host code
+// the name is a stand-in, not a device address); it uses the address that
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+constexpr size_t kScratchBytes = (size_t)DSPARK_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+dspark_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DSPARK_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return DSPARK_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSPARK_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+dspark_status dspark_verify_noalloc(const dspark_verify_problem* p, const dspark_verify_outputs* o, int32_t method,
+                                    void* stream) {
+  if (method != 0 && method != 1) return DSPARK_ERR_INVALID_ARG;
+  if (!problem_sizes_ok(p)) return DSPARK_ERR_INVALID_ARG;
+  if (layout(p->B, p->k, p->V).total > kScratchBytes) return DSPARK_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  const dspark_status st = scratch_for_current_device(&ws);
+  if (st != DSPARK_OK) return st;
+  return verify_common(p, o, ws, kScratchBytes, stream, method);
+}
 
 dspark_status dspark_draft_sample(const dspark_verify_problem* p, int32_t* tokens_out, double* logq_out,
                                   void* ws, size_t ws_bytes, void* stream) {
@@ -246,6 +287,7 @@ const char* dspark_status_string(dspark_status s) {
     case DSPARK_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case DSPARK_ERR_HIP: return "HIP launch failed";
     case DSPARK_ERR_NO_MEMORY: return "host allocation failed";
+    case DSPARK_ERR_TOO_LARGE: return "problem needs more scratch than the static per-device buffer holds";
   }
   return "unknown status";
 }

@@ -50,7 +50,9 @@ typedef enum {
                                  W1/W2t not 16-byte aligned, or B > 4096 */
   DSPARK_ERR_WORKSPACE = 3,   /* workspace NULL, misaligned (256 B) or smaller than required */
   DSPARK_ERR_HIP = 4,         /* a HIP launch or device query failed */
-  DSPARK_ERR_NO_MEMORY = 5    /* a host allocation of the cost table failed */
+  DSPARK_ERR_NO_MEMORY = 5,   /* a host allocation of the cost table failed */
+  DSPARK_ERR_TOO_LARGE = 6    /* dspark_verify_noalloc: the problem's scratch exceeds
+                                 DSPARK_NOALLOC_SCRATCH_BYTES */
 } dspark_status;
 
 typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
@@ -143,6 +145,26 @@ dspark_status dspark_verify_tokenwise(const dspark_verify_problem* problem,
 dspark_status dspark_verify_block(const dspark_verify_problem* problem,
                                   const dspark_verify_outputs* out,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Either verifier with no workspace argument and no allocation, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  method 0 = token-by-token (as
+ * dspark_verify_tokenwise), 1 = block (as dspark_verify_block); same problem,
+ * outputs, kernels and results.  The scratch is a static buffer of
+ * DSPARK_NOALLOC_SCRATCH_BYTES per device, set aside when the library's device
+ * code is loaded and held until the process ends; the problem must fit it
+ * (dspark_workspace_bytes(problem) <= DSPARK_NOALLOC_SCRATCH_BYTES, else
+ * DSPARK_ERR_TOO_LARGE and nothing is enqueued).  Every call on one device uses the
+ * same buffer: calls that can overlap on one device (different streams) race and
+ * give undefined results; calls in order on one stream are safe.  The buffer keeps
+ * the last call's contents; each call clears what it needs cleared with a kernel
+ * (no memset).  Calls hipMalloc, hipFree or any allocating routine: never.
+ * Errors as dspark_verify_block, plus DSPARK_ERR_INVALID_ARG for another method.
+ */
+#define DSPARK_NOALLOC_SCRATCH_BYTES (32u << 20)
+dspark_status dspark_verify_noalloc(const dspark_verify_problem* problem, const dspark_verify_outputs* out,
+                                    int32_t method, void* stream);
 
 /*
  * The drafter's walk with its Markov head [P2 §6 "Why the Markov Head Helps";
