@@ -239,14 +239,17 @@ dspark_status dspark_adaptive_k(const uint16_t* hidden, const uint16_t* w, float
  * Probability": candidates are added greedily in descending prefix survival and
  * the low-confidence tail is cut once the expected accepted tokens stop paying;
  * P3 "The controller, and the table it reads from": the cost of a verify pass is
- * a table indexed by its token count].  With a_{b,j} = c_{b,0} ... c_{b,j}
- * (fp64, multiplied left to right), the (b, j) pairs are ranked by descending a,
- * ties by j then b, so every leading part of the ranking holds slots 0..n_b-1 of
- * each stream b.  Taking the first m puts B + m tokens in the verify batch (n_b
- * drafts plus each stream's own target position) and expects E(m) = B + the sum
- * of their a, added one at a time in rank order.  The scheduler keeps the m in
- * [0, B k] with the largest E(m) / verify_ms[B + m] (the smallest m on ties) and
+ * a table indexed by its token count].  With a_{b,j} = c_{b,0} ... c_{b,j}, the
+ * (b, j) pairs are ranked by descending a, ties by j then b, so every leading part
+ * of the ranking holds slots 0..n_b-1 of each stream b.  Taking the first m puts
+ * B + m tokens in the verify batch (n_b drafts plus each stream's own target
+ * position) and expects E(m) = B + the sum of their a.  The scheduler keeps the m
+ * in [0, B k] with the largest E(m) / verify_ms[B + m] (the smallest m on ties) and
  * writes n_b, the count of stream b's slots among the first m.
+ * Arithmetic: survivals are fp64 products, then ranked and summed as integer
+ * multiples of 2^-40 (order-independent, exact sums), so the result is the fp64
+ * definition's except where two survivals at the cut differ by less than 2^-40 (the
+ * last draft may go to either stream) or two ratios differ by ~1e-12 relative.
  * c: device fp32 [B, k], values in [0, 1] (for example c_out of dspark_adaptive_k);
  * verify_ms: device fp32 [n_ms], positive, n_ms >= B (k + 1) + 1 (batch token
  * counts B .. B (k + 1) are read); n_out: device int32 [B] (usable as num_drafts

@@ -8,10 +8,11 @@ HIP library and its Python binding) never calls it and shares no code with it.
                           uniforms / exponential clocks drawn from it.
 * :mod:`oracle.dspark`    fp64 numpy reference of every step: Markov bias,
                           softmaxes, token-wise and block verification, the
-                          race sampler, confidence head and adaptive choice.
+                          exponential-race sampler (one clock per vocabulary id),
+                          confidence head and adaptive choice.
 * :mod:`oracle.schedule`  batch-level draft scheduler (greedy over prefix
-                          survival against a token-count cost table) and the
-                          online cost table rebuilt from live medians.
+                          survival against a token-count cost table, plain fp64)
+                          and the online cost table rebuilt from live medians.
 * :mod:`oracle.enumerate` exact enumeration of emitted-sequence distributions
                           on tiny vocabularies (no randomness).
 
@@ -19,7 +20,9 @@ Pins (tests marked ``not gpu``): Random123 known-answer vectors for Philox;
 exact enumeration showing both verifiers reproduce target-only sampling;
 closed forms (two-point softmax, one-hot Markov rows, 1 - TV acceptance,
 k = 1 equivalence, q = p); the pages' worked numbers; Monte Carlo of the full
-sampler against the enumeration; brute force over every draft-count vector
+sampler against the enumeration; Monte Carlo of the Markov path (drafts from
+the Markov drafter, verified, continued by the target) against target-only
+sampling, with planted slips caught; brute force over every draft-count vector
 for the batch scheduler and hand-computed medians for the online table.  Parity unpinned: which token the sampler
 emits at a given seed is fixed only by this package's sampling convention
 (any exact sampler is equally correct in distribution).

@@ -24,7 +24,6 @@ import numpy as np
 
 from . import philox
 
-RACE_GROUP_SIZE = 256   # READING: vocabulary groups of the two-level race sampler
 NEAR_MARGIN = 1e-6      # decisions closer than this to their threshold are "near"
 
 
@@ -69,6 +68,15 @@ def markov_bias(W1: np.ndarray, W2t: np.ndarray, prev) -> np.ndarray:
 def draft_prev_tokens(anchor: int, x: np.ndarray, gamma: int) -> np.ndarray:
     """prev_0 = anchor (the last accepted token), prev_j = x_{j-1}: the Markov walk's conditioning."""
     return np.concatenate([[int(anchor)], np.asarray(x[: max(gamma - 1, 0)], dtype=np.int64)])[:gamma]
+
+
+def draft_scaled_logits(d: np.ndarray, W1, W2t, prev, T: float) -> np.ndarray:
+    """(d + W1[prev] . W2) / T: the drafter's logits with the Markov bias of their previous
+    tokens, then divided by the temperature (READING: the bias belongs to the drafter's
+    logits, the temperature to the sampler).  d [rows, V], prev [rows]; W1 None: no bias."""
+    if W1 is not None:
+        d = d + markov_bias(W1, W2t, prev)
+    return d / T
 
 
 # ----------------------------------------------------------------------------
@@ -154,50 +162,37 @@ def block_stop(h: np.ndarray, u: np.ndarray):
 
 
 # ----------------------------------------------------------------------------
-# sampler: two-level exponential race
+# sampler: exponential race over the vocabulary
 # ----------------------------------------------------------------------------
-def _race(scores_w: np.ndarray, clocks: np.ndarray):
-    """argmax of w / E among w > 0 (lowest index on ties) and margin 1 - second/first."""
-    cand = scores_w > 0
+def race_sample(w: np.ndarray, seed: int, b: int, step: int, purpose: int = philox.PURPOSE_SAMPLE):
+    """Draw Y with P(Y = v) = w_v / sum(w) by an exponential race.
+
+    READING (the pages only say "sample from the normalized residual"): every id v
+    with w_v > 0 gets an Exp(1) clock E_v (``philox.race_clocks``, one per id, keyed by
+    stream b, ``purpose`` and ``step``) and Y is the id with the largest w_v / E_v,
+    the lowest id on ties.  The first of independent exponential clocks of rates w_v
+    to ring is v with probability w_v / sum(w), which is the normalised law.
+    Returns (Y, margin) with margin = 1 - second best / best score (1 if only one
+    id has weight), or (-1, 0) if no id has weight.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    cand = w > 0
     if not np.any(cand):
         return -1, 0.0
-    s = np.where(cand, scores_w / clocks, -np.inf)
-    best = int(np.argmax(s))
+    E = philox.race_clocks(seed, b, np.arange(w.shape[0]), purpose, step)
+    score = np.where(cand, w / E, -np.inf)
+    best = int(np.argmax(score))           # np.argmax: the first (lowest) id of equal maxima
     if np.count_nonzero(cand) == 1:
         return best, 1.0
-    second = np.max(np.delete(s, best))
-    return best, float(1.0 - second / s[best])
-
-
-def race_sample(w: np.ndarray, seed: int, b: int, step: int, group: int = RACE_GROUP_SIZE,
-                purposes=(philox.PURPOSE_RACE_GROUP, philox.PURPOSE_RACE_ITEM)):
-    """Draw Y with P(Y = v) = w_v / sum(w) by a two-level exponential race.
-
-    READING (the pages only say "sample from the normalized residual"): the
-    vocabulary is cut into consecutive groups of ``group`` ids.  Group g wins
-    the race with score W_g / E_g, W_g = sum of its weights, E_g an Exp(1) clock
-    (Philox purpose RACE_GROUP, index g); inside the winning group the id with
-    the largest w_v / E_v wins (purpose RACE_ITEM, index v).  An exponential
-    race picks each contestant with probability proportional to its weight, so
-    P(Y = v) = (W_g / W)(w_v / W_g) = w_v / W.  Returns (Y, margin).
-    """
-    V = w.shape[0]
-    ng = (V + group - 1) // group
-    W = np.array([np.sum(w[g * group: min(V, (g + 1) * group)]) for g in range(ng)])
-    Eg = philox.race_clocks(seed, b, np.arange(ng), purposes[0], step)
-    g, mg = _race(W, Eg)
-    lo, hi = g * group, min(V, (g + 1) * group)
-    Ev = philox.race_clocks(seed, b, np.arange(lo, hi), purposes[1], step)
-    v, mv = _race(w[lo:hi], Ev)
-    return lo + v, min(mg, mv)
+    second = float(np.max(np.delete(score, best)))
+    return best, float(1.0 - second / score[best])
 
 
 # ----------------------------------------------------------------------------
 # one stream, one call
 # ----------------------------------------------------------------------------
 def verify_stream(tl: np.ndarray, dl: np.ndarray, x: np.ndarray, gamma: int, T: float,
-                  anchor: int, W1, W2t, seed: int, b: int, step: int, method: str,
-                  group: int = RACE_GROUP_SIZE) -> dict:
+                  anchor: int, W1, W2t, seed: int, b: int, step: int, method: str) -> dict:
     """Verify one stream's block.
 
     tl [gamma+1, V] and dl [gamma, V] are raw fp64 logits (target rows 0..gamma,
@@ -209,10 +204,7 @@ def verify_stream(tl: np.ndarray, dl: np.ndarray, x: np.ndarray, gamma: int, T: 
     """
     logp = log_softmax(tl[: gamma + 1] / T)
     if gamma > 0:
-        d = dl[:gamma].copy()
-        if W1 is not None:
-            d = d + markov_bias(W1, W2t, draft_prev_tokens(anchor, x, gamma))
-        logq = log_softmax(d / T)
+        logq = log_softmax(draft_scaled_logits(dl[:gamma], W1, W2t, draft_prev_tokens(anchor, x, gamma), T))
     else:
         logq = np.zeros((0, tl.shape[1]))
     p = np.exp(logp)
@@ -248,7 +240,7 @@ def verify_stream(tl: np.ndarray, dl: np.ndarray, x: np.ndarray, gamma: int, T: 
             # the path that reaches it; should rounding produce one, draw from p_s.
             w = p[s]
             degenerate = True
-    Y, m_smp = race_sample(w, seed, b, step, group)
+    Y, m_smp = race_sample(w, seed, b, step)
     return dict(s=s, Y=Y, diag=diag, margin_accept=m_acc, margin_sample=m_smp,
                 degenerate=degenerate, logr=logr, u=u)
 
@@ -273,7 +265,7 @@ def greedy_stream(tl: np.ndarray, x: np.ndarray, gamma: int) -> dict:
 
 def verify(target, draft, dtype: str, draft_tokens, temperature=None, anchor=None,
            W1=None, W2t=None, num_drafts=None, seed: int = 0, step: int = 0,
-           method: str = "block", group: int = RACE_GROUP_SIZE) -> dict:
+           method: str = "block") -> dict:
     """Both verifiers over B streams.
 
     target [B, k+1, V], draft [B, k, V] (fp32 or bf16 bits), draft_tokens [B, k],
@@ -307,7 +299,7 @@ def verify(target, draft, dtype: str, draft_tokens, temperature=None, anchor=Non
             r = greedy_stream(tl, x_all[b], gamma)
         else:
             r = verify_stream(tl, dl, x_all[b], gamma, float(T_all[b]), int(a_all[b]), W1, W2t,
-                              seed, b, step, method, group)
+                              seed, b, step, method)
         s = r["s"]
         acc[b] = s
         out[b, :s] = x_all[b, :s]
@@ -324,21 +316,16 @@ def verify(target, draft, dtype: str, draft_tokens, temperature=None, anchor=Non
 # the drafter's Markov walk  [P2 §6 "Why the Markov Head Helps"; P1 §3 "The Markov
 # fix-up" and Figure 2]
 # ----------------------------------------------------------------------------
-def draft_purposes(j: int):
-    """READING: the walk's race clocks for slot j use Philox purpose words 16 + 2j
-    (groups) and 17 + 2j (ids), apart from the verifier's (1, 2, 3)."""
-    return 16 + 2 * j, 17 + 2 * j
-
-
 def draft_walk(draft, dtype: str, temperature=None, anchor=None, W1=None, W2t=None, num_drafts=None,
-               seed: int = 0, step: int = 0, group: int = RACE_GROUP_SIZE) -> dict:
+               seed: int = 0, step: int = 0) -> dict:
     """Draw the drafts slot by slot from the drafter with its Markov head:
     x_j ~ softmax((d_j + W1[x_{j-1}] . W2) / T), x_{-1} = the anchor token.
 
     The drafter's logits d_j [B, k, V] come from its parallel pass; the Markov head
     is what makes slot j depend on the token drawn at slot j-1.  T = 0 takes the
-    largest biased logit (first id on ties).  Draws use the two-level race with the
-    slot's own clocks (``draft_purposes``).  Returns tokens [B, k] (-1 past
+    largest biased logit (first id on ties).  Draws use the exponential race with the
+    slot's own clocks (READING: Philox purpose ``philox.walk_purpose(j)`` = 16 + j, apart
+    from the verifiers' words).  Returns tokens [B, k] (-1 past
     gamma_b), log q_j(x_j) [B, k] and the smallest decision margin per stream:
     the race margin, or for T = 0 (x_1 - x_2) / (|x_1| + 1) over the two largest
     biased logits.
@@ -359,7 +346,7 @@ def draft_walk(draft, dtype: str, temperature=None, anchor=None, W1=None, W2t=No
         for j in range(int(g_all[b])):
             d = widen(draft[b, j], dtype)
             if W1 is not None:
-                d = d + markov_bias(W1, W2t, prev)[0]
+                d = d + markov_bias(W1, W2t, [prev])[0]
             T = float(T_all[b])
             if T == 0.0:
                 order = np.argsort(-d, kind="stable")
@@ -367,7 +354,7 @@ def draft_walk(draft, dtype: str, temperature=None, anchor=None, W1=None, W2t=No
                 m = (d[order[0]] - d[order[1]]) / (abs(d[order[0]]) + 1.0) if V > 1 else np.inf
             else:
                 ls = log_softmax(d / T)
-                x, m = race_sample(np.exp(ls), seed, b, step, group, draft_purposes(j))
+                x, m = race_sample(np.exp(ls), seed, b, step, philox.walk_purpose(j))
                 logq[b, j] = ls[x]
             toks[b, j] = x
             margin[b] = min(margin[b], m)

@@ -21,8 +21,13 @@ step), so calls are replayable and independent of how streams are sharded.
     counter = (b, idx, purpose, step & 0xffffffff), output word 0 is used
 
 purposes: ACCEPT (idx = draft slot j) gives the uniform of the accept tests;
-RACE_GROUP (idx = vocab group g) and RACE_ITEM (idx = vocab id v) give the
-exponential clocks of the sampler; DRAFT is reserved for drafting harnesses.
+SAMPLE gives the exponential clocks of the verifiers' sampler and 16 + j those
+of slot j of the drafter's walk; DRAFT is reserved for drafting harnesses.
+
+The sampler needs one clock per vocabulary id.  Those are read off the
+generator's output stream for (b, purpose, step): counter (b, i, purpose, step)
+yields the 128-bit block of words 4i .. 4i+3, so id v takes word v mod 4 of the
+block at i = v div 4 (the four output words of one counter, in order).
 """
 from __future__ import annotations
 
@@ -35,8 +40,13 @@ W1 = 0xBB67AE85
 
 PURPOSE_DRAFT = 0
 PURPOSE_ACCEPT = 1
-PURPOSE_RACE_GROUP = 2
-PURPOSE_RACE_ITEM = 3
+PURPOSE_SAMPLE = 3
+WALK_PURPOSE_BASE = 16
+
+
+def walk_purpose(j: int) -> int:
+    """Purpose word of the clocks of slot j of the drafter's walk (apart from the verifiers')."""
+    return WALK_PURPOSE_BASE + int(j)
 
 _MASK = np.uint64(0xFFFFFFFF)
 _S32 = np.uint64(32)
@@ -88,8 +98,23 @@ def accept_uniforms(seed: int, b: int, n: int, step: int) -> np.ndarray:
     return (np.floor(x / 256.0) + 1.0) * 2.0 ** -24
 
 
-def race_clocks(seed: int, b: int, idx, purpose: int, step: int) -> np.ndarray:
-    """Exponential clocks E = -ln(U), U = ((x >> 8) + 1/2) * 2^-24 in (0, 1) (fp64)."""
-    x = words(seed, b, idx, purpose, step).astype(np.float64)
+def stream_words(seed: int, b: int, ids, purpose: int, step: int) -> np.ndarray:
+    """Word v of the output stream of (b, purpose, step) for every id v: word (v mod 4) of
+    the block at counter (b, v div 4, purpose, step)."""
+    ids = np.asarray(ids, dtype=np.int64).reshape(-1)
+    n = ids.size
+    ctr = np.empty((n, 4), dtype=np.uint64)
+    ctr[:, 0] = np.uint64(int(b) & 0xFFFFFFFF)
+    ctr[:, 1] = (ids // 4).astype(np.uint64)
+    ctr[:, 2] = np.uint64(purpose)
+    ctr[:, 3] = np.uint64(int(step) & 0xFFFFFFFF)
+    blocks = philox4x32_10(ctr, key_from_seed(seed))
+    return blocks[np.arange(n), ids % 4]
+
+
+def race_clocks(seed: int, b: int, ids, purpose: int, step: int) -> np.ndarray:
+    """Exponential clocks E_v = -ln(U_v), U_v = ((x_v >> 8) + 1/2) * 2^-24 in (0, 1) (fp64),
+    x_v = word v of the stream of (b, purpose, step)."""
+    x = stream_words(seed, b, ids, purpose, step).astype(np.float64)
     U = (np.floor(x / 256.0) + 0.5) * 2.0 ** -24
     return -np.log(U)

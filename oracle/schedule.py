@@ -15,19 +15,15 @@ Sources (page titles; sections as headed on each page):
        samples, rebuilt every 32 observations).
 
 READING (batch scheduler).  Candidates are the (stream b, slot j) pairs with
-prefix survival a[b, j] = c[b, 0] * ... * c[b, j] (fp64, left to right).  The
-pages leave the arithmetic of the expected-token sums open; here each survival
-is clipped to [0, 1] and rounded to the nearest multiple of 2^-40 (ties to
-even), and E is accumulated in those units as an exact integer, so neither the
-ranking nor any sum depends on the order of additions (the resolution, 2^-40
-tokens, is far below anything the ratio can resolve).  Candidates are taken in
-descending rounded survival, ties by slot j then stream b; since a never grows
-along a stream, every prefix of that order holds, for each stream, a prefix of
-its slots.  Taking the first m candidates puts B + m tokens in the verify batch
-(each stream's n_b drafts plus its own target position) and expects
-E(m) = B + (sum of those m survivals) accepted tokens.  The scheduler keeps the
-m with the largest E(m) / verify_ms[B + m] (fp64 division, E exact in fp64),
-the smallest m on ties.  With B = 1 this is the per-stream adaptive choice.
+prefix survival a[b, j] = c[b, 0] * ... * c[b, j] (fp64, multiplied left to
+right).  They are taken in descending survival, ties by slot j then stream b;
+since a never grows along a stream (c <= 1), every leading part of that order
+holds, for each stream, a prefix of its slots.  Taking the first m candidates
+puts B + m tokens in the verify batch (each stream's n_b drafts plus its own
+target position) and expects E(m) = B + the sum of those m survivals accepted
+tokens, added one at a time in rank order in fp64.  The scheduler keeps the m
+with the largest E(m) / verify_ms[B + m] (fp64), the smallest m on ties.  With
+B = 1 this is the per-stream adaptive choice.
 
 READING (online table).  Observations (token count t, milliseconds) are filed
 in arrival order.  The table in force is the boot table until the first
@@ -55,28 +51,22 @@ def prefix_survival_rows(c: np.ndarray) -> np.ndarray:
     return a
 
 
-FIXED_BITS = 40   # survivals are counted in units of 2^-40 tokens
-
-
-def fixed_survival(a: np.ndarray) -> np.ndarray:
-    """round(clip(a, 0, 1) * 2^40) as exact integers (NaN counts as 0)."""
-    a = np.where(np.isnan(a), 0.0, np.clip(a, 0.0, 1.0))
-    return np.rint(a * float(1 << FIXED_BITS)).astype(np.int64)
-
-
-def greedy_order(a_fixed: np.ndarray):
-    """All (b, j) pairs by descending rounded survival, ties by j then b."""
-    B, k = a_fixed.shape
+def greedy_order(a: np.ndarray):
+    """All (b, j) pairs by descending survival, ties by slot j then stream b."""
+    B, k = a.shape
     pairs = [(b, j) for b in range(B) for j in range(k)]
-    return sorted(pairs, key=lambda bj: (-int(a_fixed[bj[0], bj[1]]), bj[1], bj[0]))
+    return sorted(pairs, key=lambda bj: (-float(a[bj[0], bj[1]]), bj[1], bj[0]))
 
 
 def batch_schedule(c: np.ndarray, verify_ms) -> dict:
     """Per-stream draft counts n[B] chosen jointly for one verify batch.
 
     verify_ms[t] is the cost of a verify batch of t tokens; it must cover
-    t = B .. B (k + 1).  Returns n, the chosen m = sum n, E(m), every ratio,
-    the survivals (fp64 and rounded) and the margin (best - runner-up) / best.
+    t = B .. B (k + 1).  Returns n, the chosen m = sum n, E(m), every ratio, the
+    survivals, the margin (best - runner-up) / best of the ratio, and cut_gap, the
+    survival of the last candidate taken minus that of the first one left out
+    (inf when m is 0 or B k): how finely the ranking must resolve survivals for the
+    same streams to receive the m drafts.
     """
     c = np.asarray(c, dtype=np.float32)
     B, k = c.shape
@@ -84,12 +74,10 @@ def batch_schedule(c: np.ndarray, verify_ms) -> dict:
     if len(ms) < B * (k + 1) + 1:
         raise ValueError("verify_ms must cover B (k + 1) tokens")
     a = prefix_survival_rows(c)
-    aq = fixed_survival(a)
-    order = greedy_order(aq)
-    units = [B << FIXED_BITS]                    # exact integers
+    order = greedy_order(a)
+    E = [float(B)]
     for (b, j) in order:
-        units.append(units[-1] + int(aq[b, j]))
-    E = [u / float(1 << FIXED_BITS) for u in units]   # exact: below 2^53 units
+        E.append(E[-1] + float(a[b, j]))
     ratio = [E[m] / ms[B + m] for m in range(len(E))]
     m_best = 0
     for m in range(1, len(ratio)):
@@ -100,8 +88,9 @@ def batch_schedule(c: np.ndarray, verify_ms) -> dict:
         n[b] += 1
     others = [r for m, r in enumerate(ratio) if m != m_best]
     margin = (ratio[m_best] - max(others)) / ratio[m_best] if others else 1.0
-    return dict(n=n, m=m_best, expected=E[m_best], ratio=np.array(ratio), a=a, a_fixed=aq,
-                margin=float(margin))
+    cut_gap = (float(a[order[m_best - 1]]) - float(a[order[m_best]])) if 0 < m_best < len(order) else np.inf
+    return dict(n=n, m=m_best, expected=E[m_best], ratio=np.array(ratio), a=a, margin=float(margin),
+                cut_gap=cut_gap)
 
 
 def _median(values) -> float:

@@ -1,10 +1,16 @@
 """Batch-level scheduler and online cost table on the HIP path vs the oracle.
 
-The scheduler's survivals, its order and its running sums are computed in the
-same fp64 operations, in the same order, on both sides, so the draft counts,
-the total and the expected token count must match bit for bit.  The cost
-table is fed by HIP event pairs around real verify calls; its served table must
-equal the oracle's table rebuilt from the same filed observations.
+The oracle computes the scheduler's definition in fp64 (survivals multiplied left
+to right, E(m) summed in rank order); the kernel ranks survivals rounded to
+multiples of 2^-40 and sums them exactly as integers.  Comparison rule: the
+draft counts n and the total B + m are bit-exact, except where the oracle's
+ratio margin (best - runner-up) / best is below 1e-12 (then nothing is compared)
+or where the survivals on either side of the cut differ by less than 2^-40 (then
+only the total is compared: which stream takes the last draft is below the
+kernel's resolution); those cases are counted and printed.  E(m) is within 1e-12
+relative.  The cost table is fed by HIP event pairs around real verify calls;
+its served table must equal the oracle's table rebuilt from the same filed
+observations.
 """
 import numpy as np
 import pytest
@@ -32,15 +38,29 @@ def _table(kind, B, k, rng):
     return ms.astype(np.float32)
 
 
+RATIO_NEAR = 1e-12          # the oracle's ratio margin below which no count is compared
+KERNEL_RESOLUTION = 2.0 ** -40   # the kernel ranks survivals in these units
+
+
 def _check(mod, c, ms, label):
     n, total, expected = mod.schedule_batch(torch.from_numpy(c).cuda(), torch.from_numpy(ms).cuda())
     torch.cuda.synchronize()
     ref = osch.batch_schedule(c, ms)
     n_g = n.cpu().numpy()
-    print(f"[{label}] B={c.shape[0]} k={c.shape[1]} m={ref['m']} gpu_total={int(total.item())}", flush=True)
-    assert np.array_equal(n_g, ref["n"]), label
-    assert int(total.item()) == c.shape[0] + ref["m"]
-    assert float(expected.item()) == ref["expected"]
+    B = c.shape[0]
+    near_ratio = ref["margin"] < RATIO_NEAR
+    near_cut = 0.0 < ref["cut_gap"] <= KERNEL_RESOLUTION
+    print(f"[{label}] B={B} k={c.shape[1]} m={ref['m']} gpu_total={int(total.item())} "
+          f"ratio_margin={ref['margin']:.3g} cut_gap={ref['cut_gap']:.3g} "
+          f"near_ratio={near_ratio} near_cut={near_cut}", flush=True)
+    if near_ratio:
+        return ref
+    assert int(total.item()) == B + ref["m"], label
+    assert abs(float(expected.item()) - ref["expected"]) <= 1e-12 * ref["expected"], label
+    if near_cut:
+        assert int(n_g.sum()) == ref["m"], label
+    else:
+        assert np.array_equal(n_g, ref["n"]), label
     return ref
 
 
@@ -68,7 +88,7 @@ def test_schedule_ties_and_extremes(mod, B, k):
         _check(mod, c, _table(kind, B, k, rng), f"sched-ties-{kind}")
     flat = np.full(B * (k + 1) + 1, 5.0, dtype=np.float32)
     ref = _check(mod, c, flat, "sched-flat")
-    assert np.array_equal(ref["n"], (ref["a_fixed"] > 0).sum(axis=1))   # a flat cost takes every positive survival
+    assert np.array_equal(ref["n"], (ref["a"] > 0).sum(axis=1))   # a flat cost takes every positive survival
 
 
 def test_confidence_schedule_then_ragged_verify(mod):
@@ -86,7 +106,8 @@ def test_confidence_schedule_then_ragged_verify(mod):
     c_h = c.cpu().numpy()
     ref = osch.batch_schedule(c_h, ms)
     n_g = n.cpu().numpy()
-    assert np.array_equal(n_g, ref["n"])
+    if ref["margin"] >= RATIO_NEAR and not 0.0 < ref["cut_gap"] <= KERNEL_RESOLUTION:
+        assert np.array_equal(n_g, ref["n"])
     wl.num_drafts = n_g
     o = H.run_oracle(wl, "block", 0)
     t = H.Tally()

@@ -51,14 +51,28 @@ def test_uniformity_chi2():
 
 
 def test_race_clocks_are_exponential():
-    E = philox.race_clocks(seed=17, b=2, idx=np.arange(200000), purpose=philox.PURPOSE_RACE_ITEM, step=3)
+    E = philox.race_clocks(seed=17, b=2, ids=np.arange(200000), purpose=philox.PURPOSE_SAMPLE, step=3)
     assert np.all(E > 0)
     assert abs(E.mean() - 1.0) < 0.01
     assert abs(np.mean(E > 1.0) - np.exp(-1.0)) < 0.005
+    for w in range(4):   # each of the four words of a block on its own
+        Ew = E[w::4]
+        assert abs(Ew.mean() - 1.0) < 0.02 and abs(np.mean(Ew > 1.0) - np.exp(-1.0)) < 0.01
+
+
+def test_stream_words_read_blocks_in_order():
+    """Id v reads word v mod 4 of the block at counter (b, v div 4, purpose, step)."""
+    ids = np.arange(12)
+    got = philox.stream_words(5, 7, ids, philox.PURPOSE_SAMPLE, 9)
+    ctr = np.array([[7, i, philox.PURPOSE_SAMPLE, 9] for i in range(3)], dtype=np.uint64)
+    blocks = philox.philox4x32_10(ctr, philox.key_from_seed(5))
+    assert np.array_equal(got, blocks.reshape(-1))
+    # word 0 of each block is the same word the accept uniforms take
+    assert np.array_equal(got[::4], philox.words(5, 7, np.arange(3), philox.PURPOSE_SAMPLE, 9))
 
 
 def test_purposes_and_steps_are_distinct_streams():
     a = philox.words(1, 0, np.arange(64), philox.PURPOSE_ACCEPT, 0)
-    b = philox.words(1, 0, np.arange(64), philox.PURPOSE_RACE_ITEM, 0)
+    b = philox.words(1, 0, np.arange(64), philox.PURPOSE_SAMPLE, 0)
     c = philox.words(1, 0, np.arange(64), philox.PURPOSE_ACCEPT, 1)
     assert not np.array_equal(a, b) and not np.array_equal(a, c)

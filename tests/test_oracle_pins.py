@@ -245,7 +245,7 @@ def test_race_two_point_closed_form():
     wins = 0
     n = 4000
     for step in range(n):
-        Y, _ = dspark.race_sample(w, seed=9, b=0, step=step, group=2)
+        Y, _ = dspark.race_sample(w, seed=9, b=0, step=step)
         assert Y in (0, 3)
         wins += Y == 0
     # binomial sd = sqrt(n * .21) ~ 29

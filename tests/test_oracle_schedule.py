@@ -1,7 +1,7 @@
 """Pins of the batch-level scheduler and the online cost table in the oracle.
 
 Scheduler: brute force over every per-stream draft count vector on small
-batches (any positive cost table), the single-stream case against the
+batches (any positive cost table, unrounded fp64 survivals, 1e-12 relative), the single-stream case against the
 per-stream adaptive choice and the pages' worked example, and closed-form
 special cases (flat cost, zero confidence, a linear cost whose marginal price
 exceeds every survival).  Online table: hand-computed medians, windows and
@@ -20,10 +20,8 @@ def _rng(seed):
 
 
 def _brute_force(a, ms):
-    """max over all n in [0, k]^B of (B + sum_b sum_{j<n_b} a[b, j]) / ms[B + sum n].
-
-    Called with the rounded survivals (multiples of 2^-40): every such sum is exact
-    in fp64, so the optimum is compared for equality."""
+    """max over all n in [0, k]^B of (B + sum_b sum_{j<n_b} a[b, j]) / ms[B + sum n],
+    with the survivals a as the oracle computes them (fp64, unrounded)."""
     B, k = a.shape
     best = -1.0
     for n in itertools.product(range(k + 1), repeat=B):
@@ -49,13 +47,14 @@ def test_batch_schedule_matches_brute_force(B, k, seed):
             ms = g.uniform(1.0, 20.0, size=t.shape)                 # arbitrary positive table
         ms = ms.astype(np.float32)
         r = schedule.batch_schedule(c, ms)
-        aq = r["a_fixed"] / float(1 << schedule.FIXED_BITS)
-        assert np.all(np.abs(aq - r["a"]) <= 2.0 ** -41)
-        bf = _brute_force(aq, ms)
-        assert r["ratio"][r["m"]] == bf
+        a = r["a"]
+        # survivals: running products of the confidences (independent of the oracle's loop)
+        assert np.allclose(a, np.cumprod(c.astype(np.float64), axis=1), rtol=1e-15, atol=0)
+        bf = _brute_force(a, ms)
+        assert abs(r["ratio"][r["m"]] - bf) <= 1e-12 * bf
         # the returned counts realise that optimum
-        E = B + sum(float(np.sum(aq[b, :r["n"][b]])) for b in range(B))
-        assert E / float(ms[B + int(r["n"].sum())]) == bf
+        E = B + sum(float(np.sum(a[b, :r["n"][b]])) for b in range(B))
+        assert abs(E / float(ms[B + int(r["n"].sum())]) - bf) <= 1e-12 * bf
         assert int(r["n"].sum()) == r["m"]
 
 
@@ -64,7 +63,7 @@ def test_greedy_order_takes_prefixes_of_each_stream():
     c = g.uniform(0.0, 1.0, size=(6, 5)).astype(np.float32)
     c[1, 2:] = 1.0
     c[2, 1] = 0.0
-    order = schedule.greedy_order(schedule.fixed_survival(schedule.prefix_survival_rows(c)))
+    order = schedule.greedy_order(schedule.prefix_survival_rows(c))
     for m in range(len(order) + 1):
         taken = {}
         for (b, j) in order[:m]:
@@ -130,8 +129,8 @@ def test_marginal_price_threshold():
         alpha, beta = float(g.uniform(5, 40)), float(g.uniform(0.1, 1.5))
         ms = (alpha + beta * np.arange(B * (k + 1) + 1)).astype(np.float32).astype(np.float64)
         r = schedule.batch_schedule(c, ms)
-        a = r["a_fixed"] / float(1 << schedule.FIXED_BITS)
-        order = schedule.greedy_order(r["a_fixed"])
+        a = r["a"]
+        order = schedule.greedy_order(a)
         m = r["m"]
         if m > 0:
             b, j = order[m - 1]
@@ -141,11 +140,16 @@ def test_marginal_price_threshold():
             assert a[b, j] <= (ms[B + m + 1] - ms[B + m]) * r["ratio"][m] * (1 + 1e-12)
 
 
-def test_fixed_survival_rounding():
-    """Multiples of 2^-40 stay put, half-units round to even, the range clips."""
-    u = 2.0 ** -40
-    a = np.array([0.0, 1.0, 3 * u, 2.5 * u, 3.5 * u, 1.5, -0.25, np.nan, 0.5])
-    assert schedule.fixed_survival(a).tolist() == [0, 1 << 40, 3, 2, 4, 1 << 40, 0, 0, 1 << 39]
+def test_cut_gap_is_the_ranking_resolution_needed():
+    """Two streams whose first survivals differ by one fp32 step, a table that pays for
+    exactly one draft: the draft goes to the larger survival, and cut_gap is the gap."""
+    hi = np.float32(0.9)
+    lo = np.nextafter(hi, np.float32(0))
+    c = np.array([[lo, 0.5], [hi, 0.5]], dtype=np.float32)
+    ms = np.array([1.0, 1.0, 1.0, 1.2, 10.0, 100.0, 100.0], dtype=np.float32)   # B = 2: t = 2..6
+    r = schedule.batch_schedule(c, ms)
+    assert r["m"] == 1 and r["n"].tolist() == [0, 1]
+    assert r["cut_gap"] == float(hi) - float(lo)
 
 
 def test_schedule_rejects_short_table():

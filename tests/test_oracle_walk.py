@@ -5,7 +5,8 @@ joint law is the chain-rule product of those conditionals; the test builds it fr
 the separately pinned pieces (``markov_bias``, ``log_softmax``) over every sequence
 of a tiny vocabulary and checks the walk's draws against it with a chi-square test.
 Plausible slips (conditioning on the wrong token, no bias at slot 0, one set of
-clocks for every slot) each change the law by far more than the test's tolerance.
+clocks for every slot) each change the law by far more than the test's tolerance;
+``test_walk_same_clocks_every_slot_is_caught`` plants the last one.
 """
 import itertools
 
@@ -55,7 +56,7 @@ def test_walk_follows_the_chain_rule(anchor):
     counts = dict.fromkeys(law, 0)
     for step in range(n):
         r = dspark.draft_walk(draft, "f32", np.array([T], np.float32), np.array([anchor]), W1, W2t,
-                              seed=11, step=step, group=2)
+                              seed=11, step=step)
         counts[tuple(int(t) for t in r["tokens"][0])] += 1
     keys = sorted(law)
     exp = np.array([law[s] * n for s in keys])
@@ -106,3 +107,26 @@ def test_walk_ragged_and_seed_dependence():
     draws = {tuple(dspark.draft_walk(draft[:1], "f32", np.ones(1, np.float32), np.array([1]), W1, W2t,
                                      seed=s, step=0)["tokens"][0]) for s in range(40)}
     assert len(draws) > 10   # different seeds give different walks
+
+
+def test_walk_same_clocks_every_slot_is_caught(monkeypatch):
+    """Reusing slot 0's clocks at every slot correlates the slots' draws: the chain-rule
+    test's statistic blows far past its band."""
+    from oracle import philox
+    draft, W1, W2t = _tiny(7)
+    T, anchor = 0.8, 2
+    law = _exact_law(draft, W1, W2t, anchor, T)
+    monkeypatch.setattr(philox, "walk_purpose", lambda j: philox.WALK_PURPOSE_BASE)
+    n = 3000
+    counts = dict.fromkeys(law, 0)
+    for step in range(n):
+        r = dspark.draft_walk(draft, "f32", np.array([T], np.float32), np.array([anchor]), W1, W2t,
+                              seed=11, step=step)
+        counts[tuple(int(t) for t in r["tokens"][0])] += 1
+    keys = sorted(law)
+    exp = np.array([law[s] * n for s in keys])
+    obs = np.array([counts[s] for s in keys])
+    big = exp >= 5
+    chi2 = float(np.sum((obs[big] - exp[big]) ** 2 / exp[big]))
+    dof = int(big.sum()) - 1
+    assert chi2 > dof + 10 * np.sqrt(2 * dof), (chi2, dof)
