@@ -21,7 +21,6 @@ LIB_PATH = os.path.join(_PKG, "libdspark_verify.so")
 
 DSPARK_F32 = 0
 DSPARK_BF16 = 1
-RACE_GROUP = 256
 MAX_K = 32
 STAGES = 5   # launches per verify call
 

@@ -23,7 +23,7 @@ bool rank_ok(int R) { return R == 32 || R == 64 || R == 128 || R == 256; }
 
 // Offsets of every workspace region, in the order of dspark::Workspace.
 struct Layout {
-  size_t off[15];
+  size_t off[17];
   size_t total;
 };
 
@@ -31,7 +31,7 @@ Layout layout(int B, int k, int V) {
   const size_t NG = (size_t)(V + kGroup - 1) / kGroup;
   const size_t BT = (size_t)B * (k + 1), BD = (size_t)B * k;
   const size_t tiles = (BD + kChunk - 1) / kChunk;
-  const size_t sizes[15] = {
+  const size_t sizes[17] = {
       BT * NG * sizeof(float2),           // tpart
       BD * NG * sizeof(float2),           // dpart
       BD * NG * sizeof(float),            // wgrp
@@ -43,14 +43,16 @@ Layout layout(int B, int k, int V) {
       BD * sizeof(double),       // lpx
       BD * sizeof(double),       // lqx
       (size_t)B * 4 * sizeof(int32_t),  // info
+      (size_t)B * 4 * sizeof(int32_t),  // info2
       (size_t)B * sizeof(uint32_t),     // rowmask
       BD * sizeof(Item),                // items
       kCounterInts * sizeof(int32_t),   // nitems: list counts and pass-1 item counters
       tiles * 8 * 64 * sizeof(uint4),   // btile (sized for the largest rank, R = 256)
+      BD * NG * sizeof(Top2),           // race candidates
   };
   Layout L;
   size_t o = 0;
-  for (int i = 0; i < 15; ++i) {
+  for (int i = 0; i < 17; ++i) {
     L.off[i] = o;
     o += align_up(sizes[i] > 0 ? sizes[i] : 1);
   }
@@ -115,10 +117,12 @@ dspark_status verify_common(const dspark_verify_problem* p, const dspark_verify_
   a.ws.lpx = reinterpret_cast<double*>(base + L.off[8]);
   a.ws.lqx = reinterpret_cast<double*>(base + L.off[9]);
   a.ws.info = reinterpret_cast<int32_t*>(base + L.off[10]);
-  a.ws.rowmask = reinterpret_cast<uint32_t*>(base + L.off[11]);
-  a.ws.items = reinterpret_cast<Item*>(base + L.off[12]);
-  a.ws.nitems = reinterpret_cast<int32_t*>(base + L.off[13]);
-  a.ws.btile = reinterpret_cast<uint4*>(base + L.off[14]);
+  a.ws.info2 = reinterpret_cast<int32_t*>(base + L.off[11]);
+  a.ws.rowmask = reinterpret_cast<uint32_t*>(base + L.off[12]);
+  a.ws.items = reinterpret_cast<Item*>(base + L.off[13]);
+  a.ws.nitems = reinterpret_cast<int32_t*>(base + L.off[14]);
+  a.ws.btile = reinterpret_cast<uint4*>(base + L.off[15]);
+  a.ws.race = reinterpret_cast<Top2*>(base + L.off[16]);
   if (launch_verify(a, reinterpret_cast<hipStream_t>(stream), o->stage_events) != hipSuccess)
     return DSPARK_ERR_HIP;
   return DSPARK_OK;
@@ -155,6 +159,7 @@ dspark_status walk_common(const dspark_verify_problem* p, int32_t* tokens_out, d
   a.key1 = (uint32_t)(p->seed >> 32);
   a.step = p->step;
   a.ws.tpart = reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) + L.off[0]);   // [NG][B] partials
+  a.ws.race = reinterpret_cast<Top2*>(reinterpret_cast<char*>(ws) + L.off[16]);    // [NG][B] candidates
   if (launch_walk(a, tokens_out, logq_out, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return DSPARK_ERR_HIP;
   return DSPARK_OK;

@@ -25,10 +25,9 @@ constexpr int kCounterInts = kQueueStride * (1 + kQueues);
 constexpr double kLog2e = 1.4426950408889634074;
 constexpr double kLn2 = 0.69314718055994530942;
 
-enum Purpose : uint32_t { kPurposeDraft = 0, kPurposeAccept = 1, kPurposeRaceGroup = 2, kPurposeRaceItem = 3 };
-// The drafter walk's race clocks for slot j: purpose 16 + 2j (groups), 17 + 2j (ids).
-__host__ __device__ constexpr uint32_t walk_purpose_group(int j) { return 16u + 2u * (uint32_t)j; }
-__host__ __device__ constexpr uint32_t walk_purpose_item(int j) { return 17u + 2u * (uint32_t)j; }
+enum Purpose : uint32_t { kPurposeDraft = 0, kPurposeAccept = 1, kPurposeSample = 3 };
+// The drafter walk's race clocks for slot j: purpose 16 + j.
+__host__ __device__ constexpr uint32_t walk_purpose(int j) { return 16u + (uint32_t)j; }
 enum Dtype : int { kF32 = 0, kBF16 = 1 };
 
 // ---------------------------------------------------------------------------
@@ -49,19 +48,56 @@ __device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint3
   return c0;
 }
 
+// All four output words of one counter.
+__device__ __forceinline__ uint4 philox4(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                         uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+    k0 += 0x9E3779B9u; k1 += 0xBB67AE85u;
+  }
+  return make_uint4(c0, c1, c2, c3);
+}
+
+// The sampler's clocks: one per vocabulary id, from the generator's output stream for
+// (stream b, purpose, step): id v reads word v mod 4 of counter (b, v div 4, purpose,
+// step), E_v = -ln U_v with U_v = ((x >> 8) + 1/2) 2^-24.
+__device__ __forceinline__ uint32_t stream_word(uint32_t k0, uint32_t k1, uint32_t b, uint32_t v, uint32_t purpose,
+                                                uint32_t step) {
+  const uint4 w = philox4(b, v >> 2, purpose, step, k0, k1);
+  const uint32_t i = v & 3u;
+  return i == 0 ? w.x : (i == 1 ? w.y : (i == 2 ? w.z : w.w));
+}
+
+// log2 E in fp64 (the exact comparison of candidates).
+__device__ __forceinline__ double clock_log2_f64(uint32_t x) {
+  const double U = ((double)(x >> 8) + 0.5) * 0x1.0p-24;
+  return log2(-log(U));
+}
+
+// log2 E in fp32, within ~2e-5 absolute: U <= 1/2 is exact in fp32 and -ln U >= ln 2;
+// for U > 1/2, d = 1 - U is exact, -ln(1 - d) is a three-term series below 2^-8 and
+// -ln of the rounded 1 - d above (relative error <= 2^-24 / d <= 2^-16 in E).
+__device__ __forceinline__ float clock_log2_f32(uint32_t x) {
+  const uint32_t m = x >> 8;
+  const float U = ((float)m + 0.5f) * 0x1.0p-24f;
+  const float d = ((float)((1u << 24) - 1u - m) + 0.5f) * 0x1.0p-24f;
+  const float ln2 = 0.69314718055994530942f;
+  const float e_lo = -__builtin_amdgcn_logf(U) * ln2;                      // v_log_f32 is log2
+  const float e_series = d * (1.0f + d * (0.5f + d * (1.0f / 3.0f)));
+  const float e_hi = d < 0x1.0p-8f ? e_series : -__builtin_amdgcn_logf(1.0f - d) * ln2;
+  return __builtin_amdgcn_logf(m < (1u << 23) ? e_lo : e_hi);
+}
+
 // Accept uniform u = ((x >> 8) + 1) * 2^-24, in (0, 1], exact in fp32 and fp64.
 __device__ __forceinline__ double accept_uniform(uint32_t k0, uint32_t k1, uint32_t b, uint32_t j, uint32_t step) {
   const uint32_t x = philox_word0(b, j, kPurposeAccept, step, k0, k1);
   return (double)((x >> 8) + 1u) * 0x1.0p-24;
 }
 
-// Exponential clock E = -ln(U), U = ((x >> 8) + 1/2) * 2^-24 in (0, 1), fp64.
-__device__ __forceinline__ double race_clock(uint32_t k0, uint32_t k1, uint32_t b, uint32_t idx,
-                                             uint32_t purpose, uint32_t step) {
-  const uint32_t x = philox_word0(b, idx, purpose, step, k0, k1);
-  const double U = ((double)(x >> 8) + 0.5) * 0x1.0p-24;
-  return -log(U);
-}
 
 // ---------------------------------------------------------------------------
 // Loads.  bf16 -> fp32 is a 16-bit shift.
@@ -127,12 +163,22 @@ __device__ __forceinline__ float sum4lanes(float v) {
 }
 
 // One row of the residual pass, prepared by the scan: the target/draft rows, the
-// Markov previous token, the row maxima, the temperature constant (hi + lo) and the
-// exponent constants of P p and q in log2 units (hi + lo).
+// Markov previous token, the stream, the row maxima, the temperature constant
+// (hi + lo) and the exponent constants of P p and q in log2 units (hi + lo).
 struct Item {
-  int32_t dr, tr, prev, pad;
+  int32_t dr, tr, prev, b;
   float Mt, Md, chi, clo;
   float kph, kpl, kqh, kql;
+};
+
+// The two best race candidates of one listed row within one 256-id group: log2
+// scores (log2 w - log2 E, fp32) and ids; larger score first, the smaller id among
+// equal scores.  Empty slots hold (-inf, INT_MAX).
+struct Top2 {
+  float s1;
+  int32_t v1;
+  float s2;
+  int32_t v2;
 };
 
 // ---------------------------------------------------------------------------
@@ -150,10 +196,12 @@ struct Workspace {
   double* lpx;        // [B*k]         log p_j(x_j)
   double* lqx;        // [B*k]         log q_j(x_j)
   int32_t* info;      // [B*4]         gamma, stop (token-wise t / block provisional), f, flags
+  int32_t* info2;     // [B*4]         first list index of the stream's residual rows, list index of its bonus row
   uint32_t* rowmask;  // [B]           pass-2 rows of each stream (bit i = slot i)
   Item* items;        // [B*k]         pass-2 list: residual rows from the front, bonus rows from the back
   int32_t* nitems;    // [kCounterInts] list counts and work counters (see kQueues)
   uint4* btile;       // [ceil(B*k/16)][R/32][64] W1 tiles of pass 2's rows in MFMA lane order
+  Top2* race;         // [NG][B*k]       race candidates of the pass-2 rows (by list index); the walk: [NG][B]
 };
 
 struct Args {

@@ -1003,15 +1003,20 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
     a.ws.rowmask[b] = mask;
     s_mask = mask;
     s_base = mask ? atomicAdd(a.ws.nitems, __popc(mask)) : 0;
-    if (stop == gamma) {   // the bonus row is sampled: pass 2 takes its group statistics
+    int bonus_item = -1;
+    if (stop == gamma) {   // the bonus row is sampled: pass 2 races over it
       const int ib = atomicAdd(a.ws.nitems + 1, 1);
       Item it{};
       it.dr = -1;
       it.tr = b * k1 + gamma;
       it.prev = -1;
-      it.chi = (float)(kLog2e / T);   // pass 1's fp32 constant for this stream
-      a.ws.items[a.B * a.k - 1 - ib] = it;
+      it.b = b;
+      temp_split((float)T, it.chi, it.clo);
+      bonus_item = a.B * a.k - 1 - ib;
+      a.ws.items[bonus_item] = it;
     }
+    a.ws.info2[4 * b + 0] = s_base;
+    a.ws.info2[4 * b + 1] = bonus_item;
   }
   __syncthreads();
   if (tid <= gamma) a.ws.logP[b * k1 + tid] = s_lp[tid];
@@ -1022,7 +1027,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
     it.dr = b * a.k + i;
     it.tr = b * k1 + i;
     it.prev = a.W1 != nullptr ? draft_prev(a, b, i) : -1;
-    it.pad = 0;
+    it.b = b;
     it.Mt = s_M[i];
     it.Md = s_M[gamma + 1 + i];
     temp_split((float)T, it.chi, it.clo);
@@ -1053,15 +1058,85 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// pass2: residual group masses sum max(0, P_i p_i - q_i) of the listed rows.
+// Race candidates.  The sampler draws Y = argmax_v w_v / E_v over the whole
+// vocabulary, one Exp(1) clock per id (an exponential race picks v with probability
+// w_v / sum w).  The kernels rank log2 w - log2 E in fp32 and keep, per listed row
+// and 256-id group, the two best (score, id); the per-stream kernels then take the
+// best group and re-evaluate every candidate within kRaceWindow of it in fp64.
+// ---------------------------------------------------------------------------
+constexpr float kRaceWindow = 0x1.0p-6f;   // log2 units: far above the fp32 ranking error (~1e-5)
+
+__device__ __forceinline__ Top2 top2_empty() { return Top2{-INFINITY, INT_MAX, -INFINITY, INT_MAX}; }
+__device__ __forceinline__ bool top_better(float s, int v, float t, int u) { return s > t || (s == t && v < u); }
+// Branch-free (selects only): (-inf, INT_MAX) is never inserted.
+__device__ __forceinline__ void top2_add(Top2& a, float s, int v) {
+  const bool b1 = top_better(s, v, a.s1, a.v1);
+  const bool b2 = top_better(s, v, a.s2, a.v2);
+  const float s2 = b1 ? a.s1 : (b2 ? s : a.s2);
+  const int v2 = b1 ? a.v1 : (b2 ? v : a.v2);
+  a.s1 = b1 ? s : a.s1;
+  a.v1 = b1 ? v : a.v1;
+  a.s2 = s2;
+  a.v2 = v2;
+}
+__device__ __forceinline__ void top2_merge(Top2& a, const Top2& o) {
+  top2_add(a, o.s1, o.v1);
+  top2_add(a, o.s2, o.v2);
+}
+// The best two of the 4 lanes {n, n+16, n+32, n+48} (row swaps as in max4lanes); every
+// lane of the four ends with the same result.
+__device__ __forceinline__ Top2 top2_4lanes(Top2 t) {
+  auto swap_merge16 = [](Top2 x) {
+    const auto s1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x.s1), __float_as_uint(x.s1), false, false);
+    const auto v1 = __builtin_amdgcn_permlane16_swap((uint32_t)x.v1, (uint32_t)x.v1, false, false);
+    const auto s2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x.s2), __float_as_uint(x.s2), false, false);
+    const auto v2 = __builtin_amdgcn_permlane16_swap((uint32_t)x.v2, (uint32_t)x.v2, false, false);
+    Top2 r{__uint_as_float(s1[0]), (int)v1[0], __uint_as_float(s2[0]), (int)v2[0]};
+    top2_merge(r, Top2{__uint_as_float(s1[1]), (int)v1[1], __uint_as_float(s2[1]), (int)v2[1]});
+    return r;
+  };
+  auto swap_merge32 = [](Top2 x) {
+    const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x.s1), __float_as_uint(x.s1), false, false);
+    const auto v1 = __builtin_amdgcn_permlane32_swap((uint32_t)x.v1, (uint32_t)x.v1, false, false);
+    const auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x.s2), __float_as_uint(x.s2), false, false);
+    const auto v2 = __builtin_amdgcn_permlane32_swap((uint32_t)x.v2, (uint32_t)x.v2, false, false);
+    Top2 r{__uint_as_float(s1[0]), (int)v1[0], __uint_as_float(s2[0]), (int)v2[0]};
+    top2_merge(r, Top2{__uint_as_float(s1[1]), (int)v1[1], __uint_as_float(s2[1]), (int)v2[1]});
+    return r;
+  };
+  return swap_merge32(swap_merge16(t));
+}
+
+// This lane's best two of ids c0 .. c0 + 15 (c0 a multiple of 4), lw = log2 of the
+// weights (-inf: no weight); clocks of stream b from 4 generator blocks.
+__device__ __forceinline__ Top2 race16(const float (&lw)[16], int c0, uint32_t b, uint32_t purpose, const Args& a) {
+  Top2 t = top2_empty();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 x = philox4(b, (uint32_t)(c0 >> 2) + i, purpose, a.step, a.key0, a.key1);
+    const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const bool has = lw[4 * i + w] != -INFINITY;
+      const float sc = lw[4 * i + w] - clock_log2_f32(xs[w]);
+      top2_add(t, has ? sc : -INFINITY, has ? c0 + 4 * i + w : INT_MAX);
+    }
+  }
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// pass2: per listed row and group, the residual mass sum max(0, P_i p_i - q_i) and
+// the race candidates of w = max(0, P_i p_i - q_i); then, for the bonus rows the
+// verifiers stop at (listed from the back), the race candidates of w = p_gamma.
 // The scan prepared one Item per listed row (row indices and exponent constants)
-// and its packed W1 tile.  Waves reduce 64 ids each; the 4 wave sums of a row meet
-// in LDS and are flushed every 256 rows.
+// and its packed W1 tile.  Waves reduce 64 ids each; the 4 wave results of a row
+// meet in LDS and are flushed every 256 rows.
 // ---------------------------------------------------------------------------
 template <int DT, int KS, bool MARKOV, bool VEC>
 __global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
   __shared__ float part[kFlush * kChunk][kWaves];
-  __shared__ float2 bpart[kChunk][kWaves];
+  __shared__ Top2 rpart[kFlush * kChunk][kWaves];
   const int g = blockIdx.x;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, q = l >> 4;
   const int cb = (g * kWaves + w) * kWaveCols;
@@ -1100,8 +1175,10 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
   if (MARKOV && NI > 0) load_btile<KS>(a, 0, l, Bc);
   for (int c = 0; c < nch; ++c) {
     const int2 hnn = rows_of(c + 2);
-    const float4* kc = reinterpret_cast<const float4*>(&a.ws.items[item_at(c)].Mt);
+    const Item& itc = a.ws.items[item_at(c)];
+    const float4* kc = reinterpret_cast<const float4*>(&itc.Mt);
     const float4 k0 = kc[0], k1 = kc[1];   // (Mt, Md, chi, clo), (kph, kpl, kqh, kql)
+    const uint32_t sb = (uint32_t)min(max(itc.b, 0), a.B - 1);
     float bias[16];   // the bias alone (not folded into the draft logits: the residual
                       // compares P p with q and keeps their rounding apart)
     if (MARKOV) {
@@ -1116,51 +1193,74 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
     fetch(hn, tb, db);
     hn = hnn;
     if (rag) mask_shift(xt, shift);
+    // residual weights, their sum and the race, four ids (one generator block) at a time
     float s = 0.f;
+    Top2 rt = top2_empty();
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float tp = xt[e] - k0.x;
-      const float d = MARKOV ? xd[e] + bias[e] : xd[e];
-      const float tq = d - k0.y;
-      const float ep = fmaf(tp, k0.z, k1.x) + fmaf(tp, k0.w, k1.y);
-      const float eq = fmaf(tq, k0.z, k1.z) + fmaf(tq, k0.w, k1.w);
-      const float wv = __builtin_amdgcn_exp2f(ep) - __builtin_amdgcn_exp2f(eq);
-      s += ((VEC || c0 + e < a.V) && wv > 0.f) ? wv : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const uint4 xr = philox4(sb, (uint32_t)(c0 >> 2) + i, kPurposeSample, a.step, a.key0, a.key1);
+      const uint32_t xs[4] = {xr.x, xr.y, xr.z, xr.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = 4 * i + u;
+        const float tp = xt[e] - k0.x;
+        const float d = MARKOV ? xd[e] + bias[e] : xd[e];
+        const float tq = d - k0.y;
+        const float ep = fmaf(tp, k0.z, k1.x) + fmaf(tp, k0.w, k1.y);
+        const float eq = fmaf(tq, k0.z, k1.z) + fmaf(tq, k0.w, k1.w);
+        const float wv = __builtin_amdgcn_exp2f(ep) - __builtin_amdgcn_exp2f(eq);
+        const bool pos = (VEC || c0 + e < a.V) && wv > 0.f;
+        s += pos ? wv : 0.f;
+        const float sc = __builtin_amdgcn_logf(wv) - clock_log2_f32(xs[u]);
+        top2_add(rt, pos ? sc : -INFINITY, pos ? c0 + e : INT_MAX);
+      }
     }
     s = sum4lanes(s);
-    if (q == 0) part[(c % kFlush) * kChunk + n][w] = s;
+    rt = top2_4lanes(rt);
+    if (q == 0) {
+      part[(c % kFlush) * kChunk + n][w] = s;
+      rpart[(c % kFlush) * kChunk + n][w] = rt;
+    }
     if (c % kFlush == kFlush - 1 || c == nch - 1) {
       __syncthreads();
       const int it = (c - c % kFlush) * kChunk + tid;
       if (tid < (c % kFlush + 1) * kChunk && it < NI) {
         const int dr = a.ws.items[it].dr;
         a.ws.wgrp[(size_t)g * ND + dr] = (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]);
+        Top2 r = rpart[tid][0];
+#pragma unroll
+        for (int ww = 1; ww < kWaves; ++ww) top2_merge(r, rpart[tid][ww]);
+        a.ws.race[(size_t)g * ND + it] = r;
       }
       __syncthreads();
     }
   }
-  // bonus rows the verifier stops at (listed from the back of the list): their group
-  // statistics (max, sum 2^((x - max) c)) with pass 1's constant, as pass 1 does for
-  // every other target row
-  const int NT2 = a.B * (a.k + 1);
+  // bonus rows the verifiers stop at (listed from the back of the list): race
+  // candidates of p_gamma, log2 w = x c (unnormalised: every group of the row uses the
+  // same scale, which is all the race needs)
   for (int c = 0; c < (NB + kChunk - 1) / kChunk; ++c) {
-    const Item& it = a.ws.items[ND - 1 - min(c * kChunk + n, NB - 1)];
-    const int tr = min(max(it.tr, 0), NT2 - 1);
-    const float cb_ = it.chi;
+    const int ib = ND - 1 - min(c * kChunk + n, NB - 1);
+    const Item& it = a.ws.items[ib];
+    const int tr = min(max(it.tr, 0), NT - 1);
+    const uint32_t sb = (uint32_t)min(max(it.b, 0), a.B - 1);
+    const float chi = it.chi, clo = it.clo;
     Raw16<DT> t;
     raw_load<DT, VEC>(t, reinterpret_cast<const char*>(a.target) + (size_t)tr * rb, c0, a.V);
     float x[16];
     raw_to_f32<DT>(t, x);
     if (rag) mask_shift(x, shift);
-    const float2 pw = row_partial<0>(x, cb_);
-    if (q == 0) bpart[n][w] = pw;
+    float lw[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      lw[e] = ((VEC || c0 + e < a.V) && x[e] != -INFINITY) ? fmaf(x[e], chi, x[e] * clo) : -INFINITY;
+    const Top2 rt = top2_4lanes(race16(lw, c0, sb, kPurposeSample, a));
+    if (q == 0) rpart[n][w] = rt;
     __syncthreads();
     if (tid < kChunk && c * kChunk + tid < NB) {
-      const Item& ib = a.ws.items[ND - 1 - (c * kChunk + tid)];
-      float2 p[kWaves];
+      Top2 r = rpart[tid][0];
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) p[ww] = bpart[tid][ww];
-      a.ws.tpart[(size_t)g * NT2 + ib.tr] = combine_waves(p, ib.chi);
+      for (int ww = 1; ww < kWaves; ++ww) top2_merge(r, rpart[tid][ww]);
+      a.ws.race[(size_t)g * ND + (ND - 1 - (c * kChunk + tid))] = r;
     }
     __syncthreads();
   }
@@ -1237,10 +1337,99 @@ __device__ __forceinline__ float group_bias(const Args& a, int prev, int gsel, G
   return acc;
 }
 
+// The Markov bias of one id in fp64, by a whole wave: sum_r W1[prev, r] W2t[v, r]
+// (prev < 0: 0); every lane gets the result.
+__device__ __forceinline__ double bias_f64_wave(const Args& a, int prev, int v) {
+  double acc = 0.0;
+  if (prev >= 0) {
+    const int l = threadIdx.x & 63;
+    for (int r = l; r < a.R; r += 64)
+      acc += (double)bf16_to_f32(a.W1[(size_t)prev * a.R + r]) * (double)bf16_to_f32(a.W2t[(size_t)v * a.R + r]);
+  }
+  return wave_sum(acc);
+}
+
+// Race winner of one row from the per-group candidates race[g][it] (g < NG): the best
+// fp32 score, then every candidate within kRaceWindow of it scored again in fp64 by
+// `score64(v)` (called by a whole wave, result in every lane; -inf for no weight).
+// Returns the id with the largest fp64 score (the smallest id among equal ones), or
+// -1 if no group has a candidate.  Every thread of the workgroup must call it.
+constexpr int kMaxCand = 256;
+struct RaceLds {
+  int cand[kMaxCand];
+  double sc[kMaxCand];
+  int n;
+  float best[kWaves];
+};
+
+template <class Score64>
+__device__ int race_pick(const Args& a, int it, int ND, RaceLds& sh, double* rs, int* ri, Score64 score64) {
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int NG = a.NG;
+  // every thread's first two groups are loaded at once (clamped, masked after)
+  Top2 t0 = a.ws.race[(size_t)min(tid, NG - 1) * ND + it];
+  Top2 t1 = a.ws.race[(size_t)min(tid + kThreads, NG - 1) * ND + it];
+  if (tid >= NG) t0 = top2_empty();
+  if (tid + kThreads >= NG) t1 = top2_empty();
+  float best = fmaxf(t0.s1, t1.s1);
+  for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) best = fmaxf(best, a.ws.race[(size_t)gi * ND + it].s1);
+  best = wave_max_dpp(best);
+  if (tid == 0) sh.n = 0;
+  if (l == 0) sh.best[w] = best;
+  __syncthreads();
+  best = fmaxf(fmaxf(sh.best[0], sh.best[1]), fmaxf(sh.best[2], sh.best[3]));
+  if (best == -INFINITY) return -1;   // uniform
+  const float floor_ = best - kRaceWindow;
+  auto offer = [&](float sc, int v) {
+    if (sc >= floor_ && v >= 0 && v < a.V) {
+      const int k = atomicAdd(&sh.n, 1);
+      if (k < kMaxCand) sh.cand[k] = v;
+    }
+  };
+  offer(t0.s1, t0.v1); offer(t0.s2, t0.v2);
+  offer(t1.s1, t1.v1); offer(t1.s2, t1.v2);
+  for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) {
+    const Top2 t = a.ws.race[(size_t)gi * ND + it];
+    offer(t.s1, t.v1); offer(t.s2, t.v2);
+  }
+  __syncthreads();
+  const int nc = min(sh.n, kMaxCand);
+  for (int c = w; c < nc; c += kWaves) {
+    const double sc = score64(sh.cand[c]);
+    if (l == 0) sh.sc[c] = sc;
+  }
+  __syncthreads();
+  double bs = -INFINITY;
+  int bv = 0x7fffffff;
+  for (int c = tid; c < nc; c += kThreads) take_better(bs, bv, sh.sc[c], sh.cand[c]);
+  block_argmax(bs, bv, rs, ri);
+  return bv < a.V ? bv : -1;
+}
+
+// The race over a whole target row in fp64 (w = exp2(x c) up to a common factor):
+// only when a residual has no mass anywhere (rounding; the verifiers then draw from p_s).
+template <int DT>
+__device__ int full_row_race(const Args& a, const char* row, uint32_t b, double c, double* rs, int* ri) {
+  double bs = -INFINITY;
+  int bv = 0x7fffffff;
+  for (int v0 = 4 * threadIdx.x; v0 < a.V; v0 += 4 * kThreads) {
+    const uint4 x = philox4(b, (uint32_t)(v0 >> 2), kPurposeSample, a.step, a.key0, a.key1);
+    const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (v0 + i >= a.V) break;
+      const double lt = load1<DT>(row, v0 + i);
+      if (lt == -INFINITY) continue;
+      take_better(bs, bv, lt * c - clock_log2_f64(xs[i]), v0 + i);
+    }
+  }
+  block_argmax(bs, bv, rs, ri);
+  return bv < a.V ? bv : 0;
+}
+
 template <int DT, int KS>
 __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
-  __shared__ GroupBiasLds<KS> gb;
-  __shared__ double red[kWaves];
+  __shared__ RaceLds rl;
   __shared__ double rs[kWaves];
   __shared__ int ri[kWaves];
   __shared__ double s_R[kMaxK], s_h[kMaxK + 1];
@@ -1248,7 +1437,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int k1 = a.k + 1;
   const int NG = a.NG;
-  const int NT = a.B * k1, ND = a.B * a.k;
+  const int ND = a.B * a.k;
   const int4 info = *reinterpret_cast<const int4*>(a.ws.info + 4 * b);
   const int gamma = info.x, f = info.z;
   int stop = info.y;
@@ -1266,17 +1455,10 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
     if (tid == 0) a.accepted_len[b] = stop;
     return;
   }
+  const int2 info2 = *reinterpret_cast<const int2*>(a.ws.info2 + 4 * b);
   const double T = (double)Tf;
   const double c = kLog2e / T;
   const size_t esz = DT == kBF16 ? 2 : 4;
-
-  // group clocks do not depend on the data: computed while the loads below are in flight
-  double Eg[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int gi = tid + kThreads * t;
-    Eg[t] = gi < NG ? race_clock(a.key0, a.key1, (uint32_t)b, (uint32_t)gi, kPurposeRaceGroup, a.step) : 1.0;
-  }
   if (tid <= kMaxK) s_h[tid] = NAN;
   if (tid < kMaxK) s_R[tid] = NAN;
   __syncthreads();
@@ -1319,85 +1501,37 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
   const int s = stop;
   const int tr = b * k1 + s;
   const int dr = b * a.k + (s < gamma ? s : 0);
-
-  // group masses of the sampled row: the residual (pass 2) or, for the bonus row
-  // and an all-zero residual, the target's own partials.  A thread's first two
-  // groups load both kinds at once; groups past 512 (V > 131072) are re-read.
   const bool resid = s < gamma;
-  float Wr[2];
-  float2 Tp[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {   // unconditional loads (clamped group), masked after
-    const int gi = tid + kThreads * t;
-    const int gc = gi < NG ? gi : NG - 1;
-    Wr[t] = a.ws.wgrp[(size_t)gc * ND + dr];
-    Tp[t] = a.ws.tpart[(size_t)gc * NT + tr];
-    if (gi >= NG || !resid) Wr[t] = 0.f;
-    if (gi >= NG) Tp[t] = make_float2(-INFINITY, 0.f);
-  }
-  double rsum = (double)Wr[0] + (double)Wr[1];
-  if (resid)
-    for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) rsum += (double)a.ws.wgrp[(size_t)gi * ND + dr];
-  const bool use_p = !resid || !(block_sum(rsum, red) > 0.0);
-  // sampling from p_s: the target row's maximum over its group maxima (pass 2 took the
-  // bonus row's group statistics; any common reference works for the race, this one
-  // keeps every weight <= 1)
-  double Mt = resid ? (double)a.ws.tm[tr] : 0.0;   // the residual's weights use the scan's row maximum
-  if (use_p) {
-    float m = fmaxf(Tp[0].x, Tp[1].x);
-    for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) m = fmaxf(m, a.ws.tpart[(size_t)gi * NT + tr].x);
-    m = wave_max_dpp(m);
-    if (l == 0) red[w] = (double)m;
-    __syncthreads();
-    Mt = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
-    __syncthreads();
-  }
-  auto target_mass = [&](float2 p) {
-    return p.x == -INFINITY ? 0.0 : (double)p.y * exp2(((double)p.x - Mt) * c);
-  };
-  double best = -1.0;
-  int gbest = 0x7fffffff;
-  for (int gi = tid, t = 0; gi < NG; gi += kThreads, ++t) {
-    double W;
-    if (t < 2) W = use_p ? target_mass(Tp[t < 2 ? t : 0]) : (double)Wr[t < 2 ? t : 0];
-    else W = use_p ? target_mass(a.ws.tpart[(size_t)gi * NT + tr]) : (double)a.ws.wgrp[(size_t)gi * ND + dr];
-    if (W > 0.0) {
-      const double E = t < 2 ? Eg[t < 2 ? t : 0]
-                             : race_clock(a.key0, a.key1, (uint32_t)b, (uint32_t)gi, kPurposeRaceGroup, a.step);
-      const double sc = W / E;
-      if (sc > best) { best = sc; gbest = gi; }
-    }
-  }
-  block_argmax(best, gbest, rs, ri);
-  const int gsel = gbest < NG ? gbest : 0;
-
-  // race inside the winning group, weights recomputed in fp64 (the Markov bias of the
-  // group's ids from one cooperative pass over their W2t rows).  The logits, the
-  // row constants and the clock do not wait for the bias pass and its barrier.
-  const int v = gsel * kGroup + tid;
-  const int vc = v < a.V ? v : a.V - 1;
-  const double lt = load1<DT>(reinterpret_cast<const char*>(a.target) + (size_t)tr * a.V * esz, vc);
-  const double dl = load1<DT>(reinterpret_cast<const char*>(a.draft) + (size_t)dr * a.V * esz, vc);
-  const double lpP = a.method == 1 ? a.ws.logP[tr] * kLog2e : 0.0;
-  const double tl2s = a.ws.tl2s[tr], dm = (double)a.ws.dm[dr], dl2s = a.ws.dl2s[dr];
-  const double E = race_clock(a.key0, a.key1, (uint32_t)b, (uint32_t)v, kPurposeRaceItem, a.step);
-  const int prev = (!use_p && a.W1 != nullptr) ? draft_prev(a, b, s) : -1;
-  const float bias = prev >= 0 ? group_bias<KS>(a, prev, gsel, gb) : 0.f;
-  double sc = -1.0;
-  if (v < a.V) {
-    double wv;
-    if (use_p) {
-      wv = exp2((lt - Mt) * c);
-    } else {
+  // the sampled row's place in the pass-2 list
+  const int it = min(max(resid ? info2.x + __popc(mask & ((1u << s) - 1u)) : info2.y, 0), ND - 1);
+  const char* trow = reinterpret_cast<const char*>(a.target) + (size_t)tr * a.V * esz;
+  const char* drow = reinterpret_cast<const char*>(a.draft) + (size_t)dr * a.V * esz;
+  int Y;
+  if (resid) {
+    // w(v) = max(0, P_s p_s(v) - q_s(v)) in fp64 from the exact logits, the fp64 row
+    // normalisers and the fp64 Markov bias at v
+    const double Mt = (double)a.ws.tm[tr], tl2s = a.ws.tl2s[tr];
+    const double Md = (double)a.ws.dm[dr], dl2s = a.ws.dl2s[dr];
+    const double lpP = a.method == 1 ? a.ws.logP[tr] * kLog2e : 0.0;
+    const int prev = a.W1 != nullptr ? draft_prev(a, b, s) : -1;
+    Y = race_pick(a, it, ND, rl, rs, ri, [&](int v) {
+      const double bias = a.W1 != nullptr ? bias_f64_wave(a, prev, v) : 0.0;
+      const double lt = load1<DT>(trow, v), ld = load1<DT>(drow, v);
       const double pv = exp2((lt - Mt) * c - tl2s + lpP);
-      const double qv = exp2((dl + (double)bias - dm) * c - dl2s);
-      wv = pv - qv;
-    }
-    if (wv > 0.0) sc = wv / E;
+      const double qv = exp2((ld + bias - Md) * c - dl2s);
+      const double wv = pv - qv;
+      const uint32_t x = stream_word(a.key0, a.key1, (uint32_t)b, (uint32_t)v, kPurposeSample, a.step);
+      return wv > 0.0 ? log2(wv) - clock_log2_f64(x) : -INFINITY;
+    });
+    if (Y < 0) Y = full_row_race<DT>(a, trow, (uint32_t)b, c, rs, ri);   // no residual mass: draw from p_s
+  } else {
+    Y = race_pick(a, it, ND, rl, rs, ri, [&](int v) {
+      const double lt = load1<DT>(trow, v);
+      const uint32_t x = stream_word(a.key0, a.key1, (uint32_t)b, (uint32_t)v, kPurposeSample, a.step);
+      return lt != -INFINITY ? lt * c - clock_log2_f64(x) : -INFINITY;
+    });
+    if (Y < 0) Y = full_row_race<DT>(a, trow, (uint32_t)b, c, rs, ri);
   }
-  int vbest = sc >= 0.0 ? v : 0x7fffffff;
-  block_argmax(sc, vbest, rs, ri);
-  const int Y = vbest < a.V ? vbest : gsel * kGroup;
 
   // outputs
   if (tid <= a.k) {
@@ -1433,6 +1567,7 @@ constexpr int kWalkRows = 64;   // streams per LDS block in the partial pass
 template <int DT, int KS, bool MARKOV, bool VEC>
 __global__ __launch_bounds__(kThreads, 2) void walk_partials_kernel(Args a, int j) {
   __shared__ float2 part[kWalkRows][kWaves];
+  __shared__ Top2 rpart[kWalkRows][kWaves];
   __shared__ int s_prev[kWalkRows];
   __shared__ float s_c[kWalkRows];
   __shared__ uint4 w1s[MARKOV ? kWalkRows * (4 * KS + 1) : 1];   // W1 rows, padded stride
@@ -1500,7 +1635,16 @@ __global__ __launch_bounds__(kThreads, 2) void walk_partials_kernel(Args a, int 
       }
       if (rag) mask_shift(x, shift);
       const float2 pw = row_partial<0>(x, s_c[rr]);
-      if (q == 0) part[rr][w] = pw;
+      // race candidates of q_j: log2 w = x log2(e) / T, a common scale for the row
+      float lw[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) lw[e] = ((VEC || c0 + e < a.V) && x[e] != -INFINITY) ? x[e] * s_c[rr] : -INFINITY;
+      const uint32_t sb = (uint32_t)min(r0 + rr, a.B - 1);
+      const Top2 rt = top2_4lanes(race16(lw, c0, sb, walk_purpose(j), a));
+      if (q == 0) {
+        part[rr][w] = pw;
+        rpart[rr][w] = rt;
+      }
     }
     __syncthreads();
     if (tid < kWalkRows && r0 + tid < a.B) {
@@ -1508,6 +1652,10 @@ __global__ __launch_bounds__(kThreads, 2) void walk_partials_kernel(Args a, int 
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) p[ww] = part[tid][ww];
       a.ws.tpart[(size_t)g * a.B + r0 + tid] = combine_waves(p, s_c[tid]);
+      Top2 r = rpart[tid][0];
+#pragma unroll
+      for (int ww = 1; ww < kWaves; ++ww) top2_merge(r, rpart[tid][ww]);
+      a.ws.race[(size_t)g * a.B + r0 + tid] = r;
     }
     if (r0 + kWalkRows < a.B) load_block(r0 + kWalkRows);   // uniform
     __syncthreads();
@@ -1520,9 +1668,11 @@ __device__ void block_max_index(double& val, int& idx, double* rs, int* ri) { bl
 template <int DT, int KS>
 __global__ __launch_bounds__(kThreads) void walk_pick_kernel(Args a, int j, int32_t* tokens_out, double* logq_out) {
   __shared__ GroupBiasLds<KS> gb;
+  __shared__ RaceLds rl;
   __shared__ double rs[kWaves];
   __shared__ int ri[kWaves];
   __shared__ double red[kWaves];
+  __shared__ double s_xv;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int NG = a.NG;
@@ -1545,66 +1695,76 @@ __global__ __launch_bounds__(kThreads) void walk_pick_kernel(Args a, int j, int3
   }
   const float Tf = a.temperature != nullptr ? traw : 1.0f;
   const bool greedy = Tf == 0.f;
-  const double invT = greedy ? 0.0 : 1.0 / (double)Tf;
   const int pr = (j > 0 || a.anchor != nullptr) ? praw : -1;
-  const int prev = (pr >= 0 && pr < a.V) ? pr : -1;
+  const int prev = (a.W1 != nullptr && pr >= 0 && pr < a.V) ? pr : -1;
   const size_t esz = DT == kBF16 ? 2 : 4;
   const char* drow = reinterpret_cast<const char*>(a.draft) + ((size_t)b * a.k + j) * a.V * esz;
-  // group choice: the largest maximum (greedy) or the race over group masses
-  double best = -INFINITY;
-  int gbest = 0x7fffffff;
-  double lmax = -INFINITY;   // for log q: max over groups of m_g / T + ln s_g
-  // a thread's groups in increasing order: the first two were loaded above (clamped
-  // index) and serve log q too
-  auto race_group = [&](int gi, float2 p) {
-    if (gi >= NG || p.x == -INFINITY) return;
-    double sc;
-    if (greedy) {
-      sc = (double)p.x;
-    } else {
-      const double lw = (double)p.x * invT + log((double)p.y);   // ln W_g (unnormalised)
-      lmax = fmax(lmax, lw);
-      sc = lw - log(race_clock(a.key0, a.key1, (uint32_t)b, (uint32_t)gi, walk_purpose_group(j), a.step));
-    }
-    if (sc > best) { best = sc; gbest = gi; }
-  };
-  race_group(tid, p0);
-  race_group(tid + kThreads, p1);
-  for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) race_group(gi, a.ws.tpart[(size_t)gi * a.B + b]);
-  block_max_index(best, gbest, rs, ri);
-  const int gsel = gbest < NG ? gbest : 0;
-  // inside the group: biased logits in fp64 (the Markov bias from one cooperative pass
-  // over the group's W2t rows)
-  const int v = gsel * kGroup + tid;
-  const float bias = (a.W1 != nullptr && prev >= 0) ? group_bias<KS>(a, prev, gsel, gb) : 0.f;
-  double xv = -INFINITY, sc = -INFINITY;
-  if (v < a.V) {
-    xv = (double)load1<DT>(drow, v) + (double)bias;
-    sc = greedy ? xv
-                : xv * invT - log(race_clock(a.key0, a.key1, (uint32_t)b, (uint32_t)v, walk_purpose_item(j), a.step));
-  }
-  int vbest = v < a.V ? v : 0x7fffffff;
-  block_max_index(sc, vbest, rs, ri);
-  const int x = vbest < a.V ? vbest : gsel * kGroup;
-  if (logq_out != nullptr && !greedy) {
-    // log q_j(x) = x_v / T - ln sum_g W_g, the sum from the fp32 group partials
-    double m = lmax;
-    for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off));
-    if ((tid & 63) == 0) red[tid >> 6] = m;
-    __syncthreads();
-    m = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
-    __syncthreads();
-    double s = 0.0;
-    auto add_group = [&](int gi, float2 p) {
-      if (gi < NG && p.x != -INFINITY) s += exp((double)p.x * invT + log((double)p.y) - m);
+  int x;
+  if (greedy) {
+    // the largest biased logit: the group with the largest maximum, then inside it the
+    // biased logits in fp64 (the group's Markov bias from one cooperative pass over its
+    // W2t rows), the first id among equal values
+    double best = -INFINITY;
+    int gbest = 0x7fffffff;
+    auto max_group = [&](int gi, float2 p) {
+      if (gi < NG && p.x != -INFINITY && (double)p.x > best) { best = (double)p.x; gbest = gi; }
     };
-    add_group(tid, p0);
-    add_group(tid + kThreads, p1);
-    for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) add_group(gi, a.ws.tpart[(size_t)gi * a.B + b]);
-    s = block_sum(s, red);
-    if (tid == x - gsel * kGroup) logq_out[b * a.k + j] = xv * invT - (m + log(s));
-  } else if (tid == 0 && logq_out != nullptr) {
-    logq_out[b * a.k + j] = NAN;
+    max_group(tid, p0);
+    max_group(tid + kThreads, p1);
+    for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) max_group(gi, a.ws.tpart[(size_t)gi * a.B + b]);
+    block_max_index(best, gbest, rs, ri);
+    const int gsel = gbest < NG ? gbest : 0;
+    const int v = gsel * kGroup + tid;
+    const float bias = prev >= 0 ? group_bias<KS>(a, prev, gsel, gb) : 0.f;
+    double xv = v < a.V ? (double)load1<DT>(drow, v) + (double)bias : -INFINITY;
+    int vbest = v < a.V ? v : 0x7fffffff;
+    block_max_index(xv, vbest, rs, ri);
+    x = vbest < a.V ? vbest : gsel * kGroup;
+    if (tid == 0 && logq_out != nullptr) logq_out[b * a.k + j] = NAN;
+  } else {
+    // the race over q_j from the per-group candidates, re-scored in fp64:
+    // log2 w - log2 E with log2 w = (d_j(v) + bias(v)) log2(e) / T
+    const double invT = 1.0 / (double)Tf;
+    const double c = kLog2e * invT;
+    auto biased = [&](int v) {   // whole wave
+      const double bias = prev >= 0 ? bias_f64_wave(a, prev, v) : 0.0;
+      return (double)load1<DT>(drow, v) + bias;
+    };
+    x = race_pick(a, b, a.B, rl, rs, ri, [&](int v) {
+      const double y = biased(v);
+      const uint32_t xw = stream_word(a.key0, a.key1, (uint32_t)b, (uint32_t)v, walk_purpose(j), a.step);
+      return y != -INFINITY ? y * c - clock_log2_f64(xw) : -INFINITY;
+    });
+    if (x < 0) x = 0;   // a row with no finite logit (excluded by the caller's contract)
+    if (logq_out != nullptr) {
+      // log q_j(x) = y_x / T - ln sum_g W_g, the sum from the fp32 group partials
+      if (tid < 64) {
+        const double y = biased(x);
+        if (tid == 0) s_xv = y;
+      }
+      double lmax = -INFINITY;
+      auto lw_group = [&](int gi, float2 p) {
+        return (gi < NG && p.x != -INFINITY) ? (double)p.x * invT + log((double)p.y) : -INFINITY;
+      };
+      lmax = fmax(lw_group(tid, p0), lw_group(tid + kThreads, p1));
+      for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads)
+        lmax = fmax(lmax, lw_group(gi, a.ws.tpart[(size_t)gi * a.B + b]));
+      double m = lmax;
+      for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off));
+      if ((tid & 63) == 0) red[tid >> 6] = m;
+      __syncthreads();
+      m = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+      __syncthreads();
+      double sum = 0.0;
+      auto add_group = [&](int gi, float2 p) {
+        if (gi < NG && p.x != -INFINITY) sum += exp((double)p.x * invT + log((double)p.y) - m);
+      };
+      add_group(tid, p0);
+      add_group(tid + kThreads, p1);
+      for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) add_group(gi, a.ws.tpart[(size_t)gi * a.B + b]);
+      sum = block_sum(sum, red);
+      if (tid == 0) logq_out[b * a.k + j] = s_xv * invT - (m + log(sum));
+    }
   }
   if (tid == 0) tokens_out[b * a.k + j] = x;
 }

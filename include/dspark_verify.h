@@ -29,9 +29,12 @@
  *     reduction uses floating-point atomics.
  *   - Random numbers are Philox4x32-10 (Salmon et al., SC'11) with key = seed
  *     and counter = (global stream index, index, purpose, step): purpose 1 gives
- *     the accept uniforms u_{b,j} = ((x >> 8) + 1) 2^-24, purposes 2 and 3 the
- *     exponential clocks of the sampler.  Outputs do not depend on how streams
- *     are batched or sharded.
+ *     the accept uniforms u_{b,j} = ((x >> 8) + 1) 2^-24 (word 0 of counter
+ *     (b, j, 1, step)).  The emitted token is drawn by an exponential race over
+ *     the vocabulary: Y = argmax_v w_v / E_v with one clock E_v = -ln U_v,
+ *     U_v = ((x_v >> 8) + 1/2) 2^-24, per id, x_v = word v mod 4 of counter
+ *     (b, v div 4, 3, step); the lowest id wins ties.  Outputs do not depend on
+ *     how streams are batched or sharded.
  */
 #ifndef DSPARK_VERIFY_H
 #define DSPARK_VERIFY_H
@@ -57,8 +60,6 @@ typedef enum {
 
 typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
 
-/* Vocabulary group size of the two-level race sampler (ids [256g, 256g+256)). */
-#define DSPARK_RACE_GROUP 256
 /* Largest draft block the verify entry points accept. */
 #define DSPARK_MAX_K 32
 
@@ -170,9 +171,9 @@ dspark_status dspark_verify_noalloc(const dspark_verify_problem* problem, const 
  * The drafter's walk with its Markov head [P2 §6 "Why the Markov Head Helps";
  * P1 §3 "The Markov fix-up", Figure 2]: for each stream b and slot j < gamma_b,
  *   x_j ~ softmax((d_j + W1[x_{j-1}] . W2) / T_b),   x_{-1} = anchor_tokens[b]
- * (anchor < 0 or W1 NULL: no bias at that slot), drawn with the two-level race on
- * Philox purposes 16 + 2j (groups) and 17 + 2j (ids); T_b = 0 takes the largest
- * biased logit (first id among equal ones).  Uses from `problem`: B, k, V, dtype,
+ * (anchor < 0 or W1 NULL: no bias at that slot), drawn with the exponential race
+ * of the verifiers on Philox purpose 16 + j; T_b = 0 takes the largest biased
+ * logit (first id among equal ones).  Uses from `problem`: B, k, V, dtype,
  * draft_logits [B, k, V], num_drafts (NULL = k), temperature, W1, W2t, R,
  * anchor_tokens, seed, step; target_logits and draft_tokens are ignored and may be
  * NULL.  tokens_out: device int32 [B, k], -1 past gamma_b; it may be passed as the
