@@ -78,18 +78,18 @@ __device__ __forceinline__ double clock_log2_f64(uint32_t x) {
   return log2(-log(U));
 }
 
-// log2 E in fp32, within ~2e-5 absolute: U <= 1/2 is exact in fp32 and -ln U >= ln 2;
-// for U > 1/2, d = 1 - U is exact, -ln(1 - d) is a three-term series below 2^-8 and
-// -ln of the rounded 1 - d above (relative error <= 2^-24 / d <= 2^-16 in E).
-__device__ __forceinline__ float clock_log2_f32(uint32_t x) {
+// E = -ln U in fp32 with one logarithm, relative error <= ~2^-16: U <= 1/2 is exact in
+// fp32; for U > 1/2, d = 1 - U is exact, and -ln(1 - d) is a three-term series below
+// 2^-8 (where the rounded 1 - d would lose E) and -ln of the rounded 1 - d above.
+__device__ __forceinline__ float clock_f32(uint32_t x) {
   const uint32_t m = x >> 8;
   const float U = ((float)m + 0.5f) * 0x1.0p-24f;
   const float d = ((float)((1u << 24) - 1u - m) + 0.5f) * 0x1.0p-24f;
-  const float ln2 = 0.69314718055994530942f;
-  const float e_lo = -__builtin_amdgcn_logf(U) * ln2;                      // v_log_f32 is log2
-  const float e_series = d * (1.0f + d * (0.5f + d * (1.0f / 3.0f)));
-  const float e_hi = d < 0x1.0p-8f ? e_series : -__builtin_amdgcn_logf(1.0f - d) * ln2;
-  return __builtin_amdgcn_logf(m < (1u << 23) ? e_lo : e_hi);
+  const bool upper = m >= (1u << 23);
+  const float t = upper ? 1.0f - d : U;
+  const float e = -__builtin_amdgcn_logf(t) * 0.69314718055994530942f;   // v_log_f32 is log2
+  const float series = d * (1.0f + d * (0.5f + d * (1.0f / 3.0f)));
+  return (upper && d < 0x1.0p-8f) ? series : e;
 }
 
 // Accept uniform u = ((x >> 8) + 1) * 2^-24, in (0, 1], exact in fp32 and fp64.
@@ -98,6 +98,56 @@ __device__ __forceinline__ double accept_uniform(uint32_t k0, uint32_t k1, uint3
   return (double)((x >> 8) + 1u) * 0x1.0p-24;
 }
 
+
+// ---------------------------------------------------------------------------
+// Workspace data that one launch phase writes and another reads -- in the fused
+// verify launch, a workgroup possibly on another XCD -- goes through agent-coherent
+// accesses (relaxed atomics at agent scope, the sc1 bit): stores write through to
+// the device's coherence point and loads do not take stale L2 lines, so no cache
+// write-back or invalidate is needed between phases.  Types of 4 or 8k bytes.
+// ---------------------------------------------------------------------------
+template <class T>
+__device__ __forceinline__ T ld_c(const T* p) {
+  static_assert(sizeof(T) % 4 == 0, "coherent accesses move whole 32-bit words");
+  T v;
+  if constexpr (sizeof(T) % 8 == 0) {
+    uint64_t w[sizeof(T) / 8];
+    uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<T*>(p));
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 8); ++i)
+      w[i] = __hip_atomic_load(q + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_memcpy(&v, w, sizeof(T));
+  } else {
+    uint32_t w[sizeof(T) / 4];
+    uint32_t* q = reinterpret_cast<uint32_t*>(const_cast<T*>(p));
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 4); ++i)
+      w[i] = __hip_atomic_load(q + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_memcpy(&v, w, sizeof(T));
+  }
+  return v;
+}
+
+template <class T>
+__device__ __forceinline__ void st_c(T* p, const T& v) {
+  static_assert(sizeof(T) % 4 == 0, "coherent accesses move whole 32-bit words");
+  if constexpr (sizeof(T) % 8 == 0) {
+    uint64_t w[sizeof(T) / 8];
+    __builtin_memcpy(w, &v, sizeof(T));
+    uint64_t* q = reinterpret_cast<uint64_t*>(p);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 8); ++i) __hip_atomic_store(q + i, w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    uint32_t w[sizeof(T) / 4];
+    __builtin_memcpy(w, &v, sizeof(T));
+    uint32_t* q = reinterpret_cast<uint32_t*>(p);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 4); ++i) __hip_atomic_store(q + i, w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Wait until this wave's memory operations have completed (s_waitcnt vmcnt(0)).
+__device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ---------------------------------------------------------------------------
 // Loads.  bf16 -> fp32 is a 16-bit shift.
@@ -202,7 +252,14 @@ struct Workspace {
   int32_t* nitems;    // [kCounterInts] list counts and work counters (see kQueues)
   uint4* btile;       // [ceil(B*k/16)][R/32][64] W1 tiles of pass 2's rows in MFMA lane order
   Top2* race;         // [NG][B*k]       race candidates of the pass-2 rows (by list index); the walk: [NG][B]
+  int32_t* sync;      // [kSyncInts]     fused launch: go word at [0], error word at [1], workgroup g's
+                      //                 arrival word at [kSyncStride (1 + g)]; cleared by pack
 };
+
+// The fused verify launch's barrier words (one 64-byte line each).
+constexpr int kSyncStride = 16;
+constexpr int kMaxFusedGrid = 2048;
+constexpr int kSyncInts = kSyncStride * (1 + kMaxFusedGrid);
 
 struct Args {
   int B, k, V, R, NG, dtype;
@@ -217,6 +274,7 @@ struct Args {
   const int32_t* anchor;
   uint32_t key0, key1, step;
   int method;                     // 0 token-wise, 1 block
+  int fused_grid;                 // > 0: workgroups of the fused launch (0: separate launches)
   int32_t* accepted_len;
   int32_t* out_tokens;
   double* diag;

@@ -34,6 +34,10 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
 
 #include "common.hpp"
 
@@ -288,8 +292,12 @@ __device__ __forceinline__ int div_small(int i, float hd) { return (int)((float)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void pack_kernel(Args a) {
   const int c = blockIdx.x, l = threadIdx.x, n = l & 15, q = l >> 4;
-  if (c == 0 && l < 2) a.ws.nitems[l] = 0;
-  if (c == 0 && l < kQueues) a.ws.nitems[kQueueStride * (1 + l)] = 0;
+  if (c == 0 && l < 2) st_c(&a.ws.nitems[l], 0);
+  if (c == 0 && l < kQueues) st_c(&a.ws.nitems[kQueueStride * (1 + l)], 0);
+  if (a.fused_grid > 0) {   // the fused launch's go and error words, and every arrival word
+    if (c == 0 && l == 0) st_c(&a.ws.sync[1], 0);
+    for (int i = c * 64 + l; i <= a.fused_grid; i += gridDim.x * 64) st_c(&a.ws.sync[kSyncStride * i], 0);
+  }
   if (a.W1 == nullptr) return;
   const int ND = a.B * a.k;
   const int drc = min(c * kChunk + n, ND - 1);
@@ -308,55 +316,13 @@ __global__ __launch_bounds__(64) void pack_kernel(Args a) {
     if (kk < ks) dst[kk * 64] = pv >= 0 ? v[kk] : make_uint4(0, 0, 0, 0);
 }
 
-// The logits at the token x_j of draft slot j of stream b, for log p_j(x_j) and
-// log q_j(x_j): the target's t_j(x_j), and the drafter's d_j(x_j) plus the Markov bias
-// W1[prev] . W2t[x_j], summed in fp64: lane (n, q) of the wave takes quarter q of
-// every 32-wide k-step (four running sums, one per 32-bit word), then the 4 lanes of
-// the row add up (xor 16, then xor 32).  The whole wave calls it; every lane gets its
-// row's (t, d + bias).  Loads are unconditional (clamped rows).
-// The caller reads pv = draft_prev(b, j) (or -1 without W1) and x = x_j beforehand,
-// so that their loads go out ahead of its other loads.
-template <int DT>
-__device__ __forceinline__ double2 token_logits(const Args& a, int b, int j, int pv, int x, int q) {
-  const int dr = b * a.k + j;
-  const size_t esz = DT == kBF16 ? 2 : 4;
-  const double lt = load1<DT>(reinterpret_cast<const char*>(a.target) + (size_t)(b * (a.k + 1) + j) * a.V * esz, x);
-  const double ld = load1<DT>(reinterpret_cast<const char*>(a.draft) + (size_t)dr * a.V * esz, x);
-  double bias = 0.0;
-  if (a.W1 != nullptr) {
-    const int ks = a.R / 32;   // <= 8
-    uint4 v[8], y[8];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {   // unconditional loads (clamped row), masked after
-      const int kc = kk < ks ? kk : 0;
-      v[kk] = *reinterpret_cast<const uint4*>(a.W1 + (size_t)max(pv, 0) * a.R + kc * 32 + 8 * q);
-      y[kk] = *reinterpret_cast<const uint4*>(a.W2t + (size_t)x * a.R + kc * 32 + 8 * q);
-    }
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      if (pv < 0 || kk >= ks) v[kk] = make_uint4(0, 0, 0, 0);
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const uint32_t wa[4] = {v[kk].x, v[kk].y, v[kk].z, v[kk].w};
-      const uint32_t wb[4] = {y[kk].x, y[kk].y, y[kk].z, y[kk].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[i] += (double)bf16lo(wa[i]) * (double)bf16lo(wb[i]) + (double)bf16hi(wa[i]) * (double)bf16hi(wb[i]);
-    }
-    bias = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    bias += __shfl_xor(bias, 16);
-    bias += __shfl_xor(bias, 32);
-  }
-  return make_double2(lt, ld + bias);
-}
-
-// One k-step slice of a packed tile per lane: the B operand of 16 rows.
+// One k-step slice of a packed tile per lane: the B operand of 16 rows (tiles the scan
+// wrote for pass 2: coherent loads).
 template <int KS>
 __device__ __forceinline__ void load_btile(const Args& a, int c, int l, bf16x8 (&B)[KS]) {
   const uint4* t = a.ws.btile + (size_t)c * KS * 64 + l;
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) B[kk] = __builtin_bit_cast(bf16x8, t[kk * 64]);
+  for (int kk = 0; kk < KS; ++kk) B[kk] = __builtin_bit_cast(bf16x8, ld_c(&t[kk * 64]));
 }
 
 // x + bias at the lane's row and 16 columns: A = this wave's W2 slab, B = a packed
@@ -531,7 +497,7 @@ __device__ __forceinline__ void pass1_draft(const Args& a, const StreamTable& st
         float2 p[kWaves];
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) p[ww] = part[tid][ww];
-        a.ws.dpart[(size_t)g * ND + dr] = combine_waves(p, st.tc[bb]);
+        st_c(&a.ws.dpart[(size_t)g * ND + dr], combine_waves(p, st.tc[bb]));
       }
       __syncthreads();
     }
@@ -595,7 +561,8 @@ struct TargetQueue {
 };
 
 template <int DT, bool VEC>
-__device__ __forceinline__ void pass1_target(const Args& a, const StreamTable& st, TargetQueue<DT>& tq) {
+__device__ __forceinline__ void pass1_target(const Args& a, const StreamTable& st, TargetQueue<DT>& tq, int g,
+                                             int ng1) {
   using Q = TargetQueue<DT>;
   constexpr int U = Q::U, RS = Q::kRS, IR = Q::kItemRows;
   const int tid = threadIdx.x, rq = tid >> 4, l16 = tid & 15;
@@ -618,7 +585,7 @@ __device__ __forceinline__ void pass1_target(const Args& a, const StreamTable& s
     tr = b * k1 + st.gam[b];
     return p < NR && st.tc[b] < kGreedyTc;
   };
-  const int nq = min(kQueues, (int)gridDim.x), qx = blockIdx.x % nq;
+  const int nq = min(kQueues, ng1), qx = g % nq;
   auto claim = [&]() {
     if (tid == 0) {
       tq.slot[tq.par] = tq.pend;
@@ -657,7 +624,7 @@ __device__ __forceinline__ void pass1_target(const Args& a, const StreamTable& s
       raw_to_f32<DT>(raw[u], x);
       if (rag) mask_shift(x, shift);
       const float2 pw = row_partial<1>(x, act ? st.tc[b] : 0.f);
-      if (l16 == 0 && act) a.ws.tpart[(size_t)gi * NT + tr] = pw;
+      if (l16 == 0 && act) st_c(&a.ws.tpart[(size_t)gi * NT + tr], pw);
     }
   };
   int cur = claim();
@@ -678,14 +645,22 @@ __device__ __forceinline__ void pass1_target(const Args& a, const StreamTable& s
 }
 
 
-// VEC (rows 16-byte aligned, V >= 16) is a whole-kernel choice made on the host.
+// LDS of pass 1: the wave partials of a flush, the staged W1 tiles (64 KB at R = 256)
+// and the item claim slots; the per-stream table (8 bytes a stream) lives in the
+// launch's dynamic LDS.
+template <int KS, bool MARKOV>
+struct Pass1Lds {
+  float2 part[kFlush * kChunk][kWaves];
+  uint4 bst[MARKOV ? 2 * TileStage<KS>::kUnits : 1];
+  int qslot[2];
+};
+
+// Pass 1 for vocabulary group g of a pass of ng1 workgroups (one per group).  A
+// receives this workgroup's W2 slab (the fused launch keeps it for pass 2).
+// VEC (rows 16-byte aligned, V >= 16) is a whole-launch choice made on the host.
 template <int DT, int KS, bool MARKOV, bool VEC>
-__global__ __launch_bounds__(kThreads, 2) void pass1_kernel(Args a) {
-  extern __shared__ char smem[];
-  __shared__ float2 part[kFlush * kChunk][kWaves];
-  __shared__ uint4 bst[MARKOV ? 2 * TileStage<KS>::kUnits : 1];   // 64 KB at R = 256
-  __shared__ int qslot[2];
-  const int g = blockIdx.x;
+__device__ __forceinline__ void pass1_body(const Args& a, int g, int ng1, Pass1Lds<KS, MARKOV>& sh, char* table,
+                                           bf16x8 (&A)[4][KS]) {
   // Issue order: this thread's stream's temperature and draft count, then the W2 slab
   // and the first W1 tile block (which do not depend on the stream table), so that
   // building the table waits only for its own two loads and the slab, the launch's
@@ -693,7 +668,6 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_kernel(Args a) {
   const int tb = min((int)threadIdx.x, a.B - 1);
   const float T0 = a.temperature != nullptr ? a.temperature[tb] : 1.0f;    // raw: used after the
   const int n0 = a.num_drafts != nullptr ? a.num_drafts[tb] : a.k;          // slab loads below
-  bf16x8 A[4][KS];
   TileStage<KS> stage;
   if (MARKOV) {
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
@@ -701,12 +675,20 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_kernel(Args a) {
     tile_stage_load<KS>(a, 0, (a.B * a.k + kChunk - 1) / kChunk, stage);
   }
   __builtin_amdgcn_sched_barrier(0);   // keep the uses of T0 and n0 after the loads above
-  const StreamTable st = build_stream_table(a, smem, (int)threadIdx.x < a.B ? T0 : NAN,
+  const StreamTable st = build_stream_table(a, table, (int)threadIdx.x < a.B ? T0 : NAN,
                                             n0 < 0 ? 0 : (n0 > a.k ? a.k : n0));
-  TargetQueue<DT> tq{qslot, 0, 0};
-  if (threadIdx.x == 0) tq.pend = claim_add(a.ws.nitems + kQueueStride * (1 + g % min(kQueues, (int)gridDim.x)));
-  pass1_draft<DT, KS, MARKOV, VEC>(a, st, g, part, bst, A, stage);
-  pass1_target<DT, VEC>(a, st, tq);
+  TargetQueue<DT> tq{sh.qslot, 0, 0};
+  if (threadIdx.x == 0) tq.pend = claim_add(a.ws.nitems + kQueueStride * (1 + g % min(kQueues, ng1)));
+  pass1_draft<DT, KS, MARKOV, VEC>(a, st, g, sh.part, sh.bst, A, stage);
+  pass1_target<DT, VEC>(a, st, tq, g, ng1);
+}
+
+template <int DT, int KS, bool MARKOV, bool VEC>
+__global__ __launch_bounds__(kThreads, 2) void pass1_kernel(Args a) {
+  extern __shared__ __align__(16) char table[];
+  __shared__ Pass1Lds<KS, MARKOV> sh;
+  bf16x8 A[4][KS];
+  pass1_body<DT, KS, MARKOV, VEC>(a, blockIdx.x, gridDim.x, sh, table, A);
 }
 
 // Row normalisers from the group partials (m_g, s_g) of pass 1: M = max_g m_g and
@@ -719,7 +701,7 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_kernel(Args a) {
 // exponent (M c split into hi + lo exactly), so each moves by a relative
 // (m_g - M) c 2^-24 at most and S is within ~2e-7 relative, summed in fp64.
 constexpr int kScanRows = 6;                               // target (and draft) rows per pass
-constexpr int kScanGroups = 512;                           // groups per pass
+constexpr int kScanGroups = 256;                           // groups per pass
 constexpr int kStageIter = kScanRows * kScanGroups / kThreads;
 struct ScanLds {
   float2 t[kScanRows][kScanGroups + 1];   // +1: stores of one instruction spread over banks
@@ -740,8 +722,8 @@ __device__ __forceinline__ void stage_load(StageRegs& sr, const Args& a, int b, 
     const int e = tid + kThreads * i;
     const int gl = min(e / kScanRows, ng - 1), r = e % kScanRows;
     const size_t gg = (size_t)(g0 + gl);
-    sr.t[i] = a.ws.tpart[gg * NT + b * k1 + r0 + (r < nt ? r : 0)];
-    sr.d[i] = a.ws.dpart[gg * ND + b * a.k + min(r0 + (r < nd ? r : 0), a.k - 1)];
+    sr.t[i] = ld_c(&a.ws.tpart[gg * NT + b * k1 + r0 + (r < nt ? r : 0)]);
+    sr.d[i] = ld_c(&a.ws.dpart[gg * ND + b * a.k + min(r0 + (r < nd ? r : 0), a.k - 1)]);
   }
 }
 
@@ -755,43 +737,46 @@ __device__ __forceinline__ void stage_store(const StageRegs& sr, ScanLds& sh, in
   }
 }
 
-// One pass of groups [g0, g0 + ng) over the 3 LDS rows of this wave (slot q: row
-// w + 4q of the 12, target rows first), folded into the running (M, S) of each.  The
-// three rows go through each step together so that their latencies overlap.
+// One pass of groups [g0, g0 + ng) over one LDS row, folded into its running (M, S).
+// Every term, and the rescaling of S when the pass raises M, is 2^((m - M) cf) in
+// the three-operation form 2^(fma(m, cf, -mh)) 2^(-ml) with M cf = mh + ml exactly
+// (cf = log2(e) / T in fp32, as pass 1 used inside each group); an empty group
+// (m_g = -inf, s_g = 0) adds 0.
+__device__ __forceinline__ void stage_reduce_row(const float2* row, int l, int ng, float cf, float& M, double& S) {
+  float2 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int g = l + 64 * i;
+    v[i] = g < ng ? row[g] : make_float2(-INFINITY, 0.f);
+  }
+  float m = v[0].x;
+#pragma unroll
+  for (int i = 1; i < 8; ++i) m = fmaxf(m, v[i].x);
+  m = wave_max_dpp(m);
+  if (m > M) {
+    if (M != -INFINITY) {
+      const float mh = m * cf, ml = fmaf(m, cf, -mh);
+      S *= (double)__builtin_amdgcn_exp2f(fmaf(M, cf, -mh)) * (double)__builtin_amdgcn_exp2f(-ml);
+    }
+    M = m;
+  }
+  const float mh = M * cf, ml = fmaf(M, cf, -mh);
+  double part = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) part += (double)v[i].y * (double)__builtin_amdgcn_exp2f(fmaf(v[i].x, cf, -mh));
+  S += part * (double)__builtin_amdgcn_exp2f(-ml);
+}
+
+// The 3 LDS rows of this wave (slot q: row w + 4q of the 12, target rows first), one
+// after the other (a scheduling barrier keeps their registers apart).
 __device__ __forceinline__ void stage_reduce(const ScanLds& sh, int w, int l, int ng, double c, float (&M)[3],
                                              double (&S)[3]) {
-  float2 v[3][8];
-  float m[3];
+  const float cf = (float)c;
 #pragma unroll
   for (int q = 0; q < 3; ++q) {
     const int slot = w + kWaves * q;
-    const float2* row = slot < kScanRows ? sh.t[slot] : sh.d[slot - kScanRows];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int g = l + 64 * i;
-      v[q][i] = g < ng ? row[g] : make_float2(-INFINITY, 0.f);
-    }
-    m[q] = v[q][0].x;
-#pragma unroll
-    for (int i = 1; i < 8; ++i) m[q] = fmaxf(m[q], v[q][i].x);
-  }
-#pragma unroll
-  for (int q = 0; q < 3; ++q) m[q] = wave_max_dpp(m[q]);
-  const float cf = (float)c;   // log2(e) / T in fp32, as pass 1 used inside each group
-#pragma unroll
-  for (int q = 0; q < 3; ++q) {
-    if (m[q] > M[q]) {
-      if (M[q] != -INFINITY) S[q] *= exp2(((double)M[q] - (double)m[q]) * c);
-      M[q] = m[q];
-    }
-    // 2^((m_g - M) cf) as 2^(fma(m_g, cf, -mh)) 2^(-ml) with M cf = mh + ml exactly;
-    // an empty group (m_g = -inf, s_g = 0) adds 0
-    const float mh = M[q] * cf, ml = fmaf(M[q], cf, -mh);
-    double part = 0.0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      part += (double)v[q][i].y * (double)__builtin_amdgcn_exp2f(fmaf(v[q][i].x, cf, -mh));
-    S[q] += part * (double)__builtin_amdgcn_exp2f(-ml);
+    stage_reduce_row(slot < kScanRows ? sh.t[slot] : sh.d[slot - kScanRows], l, ng, cf, M[q], S[q]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -804,8 +789,7 @@ __device__ __forceinline__ void stage_reduce(const ScanLds& sh, int w, int l, in
 constexpr int kLoadsInFlight = 8;   // per lane, in the per-wave loops over group partials
 
 template <int DT>
-__device__ __forceinline__ void greedy_scan(const Args& a, int b, int gamma) {
-  __shared__ int s_am[kMaxK + 1];
+__device__ __forceinline__ void greedy_scan(const Args& a, int b, int gamma, int* s_am) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int k1 = a.k + 1, NT = a.B * k1, NG = a.NG;
   const size_t rb = (size_t)a.V * (DT == kBF16 ? 2 : 4);
@@ -817,7 +801,7 @@ __device__ __forceinline__ void greedy_scan(const Args& a, int b, int gamma) {
     auto load_maxima = [&](int g0) {
 #pragma unroll
       for (int u = 0; u < kLoadsInFlight; ++u)
-        gm[u] = a.ws.tpart[(size_t)min(g0 + l + 64 * u, NG - 1) * NT + row].x;
+        gm[u] = ld_c(&a.ws.tpart[(size_t)min(g0 + l + 64 * u, NG - 1) * NT + row]).x;
     };
     load_maxima(0);
     float M = -INFINITY;
@@ -857,34 +841,44 @@ __device__ __forceinline__ void greedy_scan(const Args& a, int b, int gamma) {
     int t = gamma;
     for (int j = 0; j < gamma; ++j)
       if (s_am[j] != a.tokens[b * a.k + j]) { t = j; break; }
-    a.ws.info[4 * b + 0] = gamma;
-    a.ws.info[4 * b + 1] = t;      // the stop: no residual mass is needed
-    a.ws.info[4 * b + 2] = 0;
-    a.ws.info[4 * b + 3] = s_am[t];   // the emitted token
-    a.ws.rowmask[b] = 0u;
+    // gamma, the stop (no residual mass is needed), 0, the emitted token
+    st_c(reinterpret_cast<int4*>(a.ws.info + 4 * b), make_int4(gamma, t, 0, s_am[t]));
+    st_c(&a.ws.rowmask[b], 0u);
   }
-  if (tid <= gamma) a.ws.logP[b * k1 + tid] = NAN;
+  if (tid <= gamma) st_c(&a.ws.logP[b * k1 + tid], (double)NAN);
   if (tid < gamma) {
-    a.ws.lpx[b * a.k + tid] = NAN;
-    a.ws.lqx[b * a.k + tid] = NAN;
+    st_c(&a.ws.lpx[b * a.k + tid], (double)NAN);
+    st_c(&a.ws.lqx[b * a.k + tid], (double)NAN);
   }
 }
 
+// LDS of the scan of one stream.
+struct ScanPhaseLds {
+  ScanLds sh;
+  float s_M[2 * kMaxK + 1];
+  double s_l2s[2 * kMaxK + 1];
+  double s_lt[kMaxK], s_ld[kMaxK], s_u[kMaxK], s_lr[kMaxK], s_lp[kMaxK + 1];
+  double s_thr[kMaxK], s_eP[kMaxK + 1];
+  int s_am[kMaxK + 1];
+  int s_base;
+  uint32_t s_mask;
+};
+
+// The scan of stream b.  Every thread of the workgroup calls it.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
-  __shared__ ScanLds sh;
-  __shared__ float s_M[2 * kMaxK + 1];
-  __shared__ double s_l2s[2 * kMaxK + 1];
-  __shared__ double s_lt[kMaxK], s_ld[kMaxK], s_u[kMaxK], s_lr[kMaxK], s_lp[kMaxK + 1];
-  __shared__ double s_thr[kMaxK], s_eP[kMaxK + 1];
-  __shared__ int s_base;
-  __shared__ uint32_t s_mask;
-  const int b = blockIdx.x;
+__device__ __forceinline__ void scan_body(const Args& a, int b, ScanPhaseLds& L) {
+  ScanLds& sh = L.sh;
+  float* s_M = L.s_M;
+  double* s_l2s = L.s_l2s;
+  double *s_lt = L.s_lt, *s_ld = L.s_ld, *s_u = L.s_u, *s_lr = L.s_lr, *s_lp = L.s_lp;
+  double *s_thr = L.s_thr, *s_eP = L.s_eP;
+  int& s_base = L.s_base;
+  uint32_t& s_mask = L.s_mask;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int gamma = stream_gamma(a, b);
   const float Tf = stream_temp(a, b);
   if (Tf == 0.f) {   // the whole workgroup takes the greedy branch
-    greedy_scan<DT>(a, b, gamma);
+    greedy_scan<DT>(a, b, gamma, L.s_am);
     return;
   }
   const double T = (double)Tf;
@@ -893,27 +887,49 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
   const int NT = a.B * k1, ND = a.B * a.k;
   const size_t esz = DT == kBF16 ? 2 : 4;
 
-  // the draft tokens and their previous tokens first, then the first row-statistics
-  // loads, then the gathers at the tokens: each wait covers only what it needs
-  const bool gath = w < 2 && 16 * w < gamma;   // waves 0 and 1: slots 16 w + n (lane n + 16 q)
-  const int jg = min(16 * w + (l & 15), max(gamma - 1, 0));
-  int pv = -1, xg = 0;
-  if (gath) {
-    pv = a.W1 != nullptr ? draft_prev(a, b, jg) : -1;
-    xg = clamp_tok(a.tokens[b * a.k + jg], a.V);
-  }
+  // the first row-statistics loads, then the logits at the drafts
   const int ngp = min(a.NG, kScanGroups);
   StageRegs sreg;
   stage_load(sreg, a, b, 0, min(kScanRows, gamma), min(kScanRows, gamma), 0, ngp, tid);
 
   if (tid < gamma) s_u[tid] = accept_uniform(a.key0, a.key1, (uint32_t)b, (uint32_t)tid, a.step);
 
-  // the logits at the drafts
-  if (gath) {
-    const double2 tl = token_logits<DT>(a, b, jg, pv, xg, l >> 4);
-    if ((l >> 4) == 0 && 16 * w + (l & 15) < gamma) {
-      s_lt[jg] = tl.x;
-      s_ld[jg] = tl.y;
+  // the logits at the drafts, t_j(x_j) and d_j(x_j) + W1[prev_j] . W2t[x_j] (the bias in
+  // fp64): wave w takes slots w and w + 4 at a time, lane l ranks 4l .. 4l + 3
+  for (int j0 = w; j0 < gamma; j0 += 2 * kWaves) {
+    int x[2], pv[2];
+    uint2 p1[2], p2[2];
+    float lt[2], ld[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = min(j0 + kWaves * u, gamma - 1);
+      x[u] = clamp_tok(a.tokens[b * a.k + j], a.V);
+      pv[u] = a.W1 != nullptr ? draft_prev(a, b, j) : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = min(j0 + kWaves * u, gamma - 1);
+      lt[u] = load1<DT>(reinterpret_cast<const char*>(a.target) + (size_t)(b * k1 + j) * a.V * esz, x[u]);
+      ld[u] = load1<DT>(reinterpret_cast<const char*>(a.draft) + (size_t)(b * a.k + j) * a.V * esz, x[u]);
+      const int r = min(4 * l, max(a.R - 4, 0));   // lanes past R / 4 re-read a valid piece, unused
+      p1[u] = p2[u] = make_uint2(0, 0);
+      if (a.W1 != nullptr) {
+        p1[u] = *reinterpret_cast<const uint2*>(a.W1 + (size_t)max(pv[u], 0) * a.R + r);
+        p2[u] = *reinterpret_cast<const uint2*>(a.W2t + (size_t)x[u] * a.R + r);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      double acc = 0.0;
+      if (pv[u] >= 0 && 4 * l < a.R)
+        acc = (double)bf16lo(p1[u].x) * (double)bf16lo(p2[u].x) + (double)bf16hi(p1[u].x) * (double)bf16hi(p2[u].x) +
+              (double)bf16lo(p1[u].y) * (double)bf16lo(p2[u].y) + (double)bf16hi(p1[u].y) * (double)bf16hi(p2[u].y);
+      acc = wave_sum(acc);
+      const int j = j0 + kWaves * u;
+      if (l == 0 && j < gamma) {
+        s_lt[j] = lt[u];
+        s_ld[j] = (double)ld[u] + acc;
+      }
     }
   }
 
@@ -946,8 +962,8 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
         const int r = is_t ? j : gamma + 1 + j;                 // index into s_M / s_l2s
         s_M[r] = M[q];
         s_l2s[r] = l2s;
-        if (is_t) { a.ws.tm[b * k1 + j] = M[q]; a.ws.tl2s[b * k1 + j] = l2s; }
-        else { a.ws.dm[b * a.k + j] = M[q]; a.ws.dl2s[b * a.k + j] = l2s; }
+        if (is_t) { st_c(&a.ws.tm[b * k1 + j], M[q]); st_c(&a.ws.tl2s[b * k1 + j], l2s); }
+        else { st_c(&a.ws.dm[b * a.k + j], M[q]); st_c(&a.ws.dl2s[b * a.k + j], l2s); }
       }
     }
   }
@@ -958,8 +974,8 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
     const int j = tid;
     const double lpx = (s_lt[j] - (double)s_M[j]) / T - s_l2s[j] * kLn2;
     const double lqx = (s_ld[j] - (double)s_M[gamma + 1 + j]) / T - s_l2s[gamma + 1 + j] * kLn2;
-    a.ws.lpx[b * a.k + j] = lpx;
-    a.ws.lqx[b * a.k + j] = lqx;
+    st_c(&a.ws.lpx[b * a.k + j], lpx);
+    st_c(&a.ws.lqx[b * a.k + j], lqx);
     s_lr[j] = lpx - lqx;
     s_thr[j] = s_lr[j] >= 0.0 ? 1.0 : exp(s_lr[j]);   // token-wise threshold min(1, r_j)
   }
@@ -996,11 +1012,8 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
         stop = -1;
       }
     }
-    a.ws.info[4 * b + 0] = gamma;
-    a.ws.info[4 * b + 1] = stop;
-    a.ws.info[4 * b + 2] = f;
-    a.ws.info[4 * b + 3] = t;
-    a.ws.rowmask[b] = mask;
+    st_c(reinterpret_cast<int4*>(a.ws.info + 4 * b), make_int4(gamma, stop, f, t));
+    st_c(&a.ws.rowmask[b], mask);
     s_mask = mask;
     s_base = mask ? atomicAdd(a.ws.nitems, __popc(mask)) : 0;
     int bonus_item = -1;
@@ -1013,13 +1026,12 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
       it.b = b;
       temp_split((float)T, it.chi, it.clo);
       bonus_item = a.B * a.k - 1 - ib;
-      a.ws.items[bonus_item] = it;
+      st_c(&a.ws.items[bonus_item], it);
     }
-    a.ws.info2[4 * b + 0] = s_base;
-    a.ws.info2[4 * b + 1] = bonus_item;
+    st_c(reinterpret_cast<int2*>(a.ws.info2 + 4 * b), make_int2(s_base, bonus_item));
   }
   __syncthreads();
-  if (tid <= gamma) a.ws.logP[b * k1 + tid] = s_lp[tid];
+  if (tid <= gamma) st_c(&a.ws.logP[b * k1 + tid], s_lp[tid]);
   const uint32_t mask = s_mask;
   if (tid < gamma && ((mask >> tid) & 1u)) {
     const int i = tid;
@@ -1037,7 +1049,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
     it.kpl = (float)(kp - (double)it.kph);
     it.kqh = (float)kq;
     it.kql = (float)(kq - (double)it.kqh);
-    a.ws.items[s_base + __popc(mask & ((1u << i) - 1u))] = it;
+    st_c(&a.ws.items[s_base + __popc(mask & ((1u << i) - 1u))], it);
   }
   // W1 tiles of the listed rows for pass 2 (pass 1, the only other reader, is done)
   if (a.W1 != nullptr && mask != 0u) {
@@ -1048,13 +1060,19 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
       if (tid < 4 * ks) {
         const int kk = tid >> 2, q = tid & 3;
         const int prev = draft_prev(a, b, i);
-        a.ws.btile[((size_t)(it >> 4) * ks + kk) * 64 + (it & 15) + 16 * q] =
-            prev >= 0 ? *reinterpret_cast<const uint4*>(a.W1 + (size_t)prev * a.R + kk * 32 + 8 * q)
-                      : make_uint4(0, 0, 0, 0);
+        st_c(&a.ws.btile[((size_t)(it >> 4) * ks + kk) * 64 + (it & 15) + 16 * q],
+             prev >= 0 ? *reinterpret_cast<const uint4*>(a.W1 + (size_t)prev * a.R + kk * 32 + 8 * q)
+                       : make_uint4(0, 0, 0, 0));
       }
       ++it;
     }
   }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
+  __shared__ ScanPhaseLds L;
+  scan_body<DT>(a, blockIdx.x, L);
 }
 
 // ---------------------------------------------------------------------------
@@ -1107,22 +1125,68 @@ __device__ __forceinline__ Top2 top2_4lanes(Top2 t) {
   return swap_merge32(swap_merge16(t));
 }
 
-// This lane's best two of ids c0 .. c0 + 15 (c0 a multiple of 4), lw = log2 of the
-// weights (-inf: no weight); clocks of stream b from 4 generator blocks.
-__device__ __forceinline__ Top2 race16(const float (&lw)[16], int c0, uint32_t b, uint32_t purpose, const Args& a) {
-  Top2 t = top2_empty();
-#pragma unroll
+// A lane's best two race candidates while its ids arrive in increasing order, as
+// ratios w / E (0: none): a later id replaces an earlier one only with a strictly
+// larger ratio, so the smaller id wins ties without comparing ids.
+struct LaneTop {
+  float s1, s2;
+  int32_t v1, v2;
+};
+__device__ __forceinline__ LaneTop lane_top_empty() { return LaneTop{0.f, 0.f, INT_MAX, INT_MAX}; }
+__device__ __forceinline__ void lane_top_add(LaneTop& t, float r, int v) {
+  const bool b1 = r > t.s1, b2 = r > t.s2;
+  t.s2 = b1 ? t.s1 : (b2 ? r : t.s2);
+  t.v2 = b1 ? t.v1 : (b2 ? v : t.v2);
+  t.s1 = b1 ? r : t.s1;
+  t.v1 = b1 ? v : t.v1;
+}
+// As log2 scores on the row's common scale: log2(w / E) + off, where the lane's
+// weights were w_v = 2^(log2 w_v - off).
+__device__ __forceinline__ Top2 lane_top_log2(const LaneTop& t, float off) {
+  Top2 r;
+  r.s1 = t.s1 > 0.f ? __builtin_amdgcn_logf(t.s1) + off : -INFINITY;
+  r.v1 = t.s1 > 0.f ? t.v1 : INT_MAX;
+  r.s2 = t.s2 > 0.f ? __builtin_amdgcn_logf(t.s2) + off : -INFINITY;
+  r.v2 = t.s2 > 0.f ? t.v2 : INT_MAX;
+  return r;
+}
+
+// The race over this lane's ids c0 .. c0 + 15 (c0 a multiple of 4), one generator
+// block of four ids per step, from the lane's values parked in LDS (a private slot of
+// 4 float4: the race then needs none of the registers that produced them).
+// Ratios (EXP = false): the slot holds weights w >= 0 on the row's common scale.
+// Exponents (EXP = true): it holds y with weights 2^(y c) (y = -inf: none); they are
+// taken relative to the lane's largest y, m (so each lies in (0, 1]), and the result
+// is put back on the common scale, log2 w = y c.
+template <bool EXP>
+__device__ __forceinline__ Top2 race16(const float4* slot, float m, float c, int c0, uint32_t b, uint32_t purpose,
+                                       const Args& a) {
+  LaneTop t = lane_top_empty();
+#pragma unroll 1
   for (int i = 0; i < 4; ++i) {
+    const float4 y4 = slot[i];
+    const float ys[4] = {y4.x, y4.y, y4.z, y4.w};
     const uint4 x = philox4(b, (uint32_t)(c0 >> 2) + i, purpose, a.step, a.key0, a.key1);
     const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const bool has = lw[4 * i + w] != -INFINITY;
-      const float sc = lw[4 * i + w] - clock_log2_f32(xs[w]);
-      top2_add(t, has ? sc : -INFINITY, has ? c0 + 4 * i + w : INT_MAX);
+    for (int u = 0; u < 4; ++u) {
+      const float w = EXP ? __builtin_amdgcn_exp2f((ys[u] - m) * c) : ys[u];
+      lane_top_add(t, w * __builtin_amdgcn_rcpf(clock_f32(xs[u])), c0 + 4 * i + u);
     }
   }
-  return t;
+  return lane_top_log2(t, EXP ? m * c : 0.f);
+}
+
+__device__ __forceinline__ void park16(float4* slot, const float (&v)[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) slot[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+}
+
+__device__ __forceinline__ float max16(const float (&v)[16]) {
+  float m = v[0];
+#pragma unroll
+  for (int e = 1; e < 16; ++e) m = fmaxf(m, v[e]);
+  return m == -INFINITY ? 0.f : m;   // no weight in the lane: every ratio is 0
 }
 
 // ---------------------------------------------------------------------------
@@ -1133,11 +1197,19 @@ __device__ __forceinline__ Top2 race16(const float (&lw)[16], int c0, uint32_t b
 // and its packed W1 tile.  Waves reduce 64 ids each; the 4 wave results of a row
 // meet in LDS and are flushed every 256 rows.
 // ---------------------------------------------------------------------------
+struct Pass2Lds {
+  float part[kFlush * kChunk][kWaves];
+  Top2 rpart[kFlush * kChunk][kWaves];
+  float4 park[kThreads][4];   // a lane's 16 race weights
+};
+
+// Pass 2 for vocabulary group g.  slab_loaded: A already holds this workgroup's W2
+// slab (the fused launch's pass 1 left it there).
 template <int DT, int KS, bool MARKOV, bool VEC>
-__global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
-  __shared__ float part[kFlush * kChunk][kWaves];
-  __shared__ Top2 rpart[kFlush * kChunk][kWaves];
-  const int g = blockIdx.x;
+__device__ __forceinline__ void pass2_body(const Args& a, int g, Pass2Lds& L, bf16x8 (&A)[4][KS], bool slab_loaded) {
+  auto& part = L.part;
+  auto& rpart = L.rpart;
+  auto& park = L.park;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, q = l >> 4;
   const int cb = (g * kWaves + w) * kWaveCols;
   const int cw = cb + 16 * q;
@@ -1148,15 +1220,14 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
   const int ND = a.B * a.k;
 
   // the W2 slab does not depend on the list: its loads go out before the count is read
-  bf16x8 A[4][KS];
-  if (MARKOV) load_w2_slab<KS, VEC>(a, cb, n, q, A);
+  if (MARKOV && !slab_loaded) load_w2_slab<KS, VEC>(a, cb, n, q, A);
   // The first chunks' rows do not wait for the list count either: row indices are
   // read speculatively (entries past the count are stale, clamped to valid rows and
   // never written back), so the first logits loads follow one dependent load.
   const int NT = a.B * (a.k + 1);
   auto item_at = [&](int c) { return min(c * kChunk + n, ND - 1); };
   auto rows_of = [&](int c) {   // (dr, tr) of this lane's row in chunk c, clamped
-    int2 h = *reinterpret_cast<const int2*>(&a.ws.items[item_at(c)].dr);
+    int2 h = ld_c(reinterpret_cast<const int2*>(&a.ws.items[item_at(c)].dr));
     h.x = min(max(h.x, 0), ND - 1);
     h.y = min(max(h.y, 0), NT - 1);
     return h;
@@ -1169,7 +1240,7 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
   Raw16<DT> tb, db;
   fetch(rows_of(0), tb, db);
   int2 hn = rows_of(1);
-  const int NI = a.ws.nitems[0], NB = a.ws.nitems[1];
+  const int NI = ld_c(&a.ws.nitems[0]), NB = ld_c(&a.ws.nitems[1]);
   const int nch = (NI + kChunk - 1) / kChunk;
   bf16x8 Bc[KS];
   if (MARKOV && NI > 0) load_btile<KS>(a, 0, l, Bc);
@@ -1177,8 +1248,8 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
     const int2 hnn = rows_of(c + 2);
     const Item& itc = a.ws.items[item_at(c)];
     const float4* kc = reinterpret_cast<const float4*>(&itc.Mt);
-    const float4 k0 = kc[0], k1 = kc[1];   // (Mt, Md, chi, clo), (kph, kpl, kqh, kql)
-    const uint32_t sb = (uint32_t)min(max(itc.b, 0), a.B - 1);
+    const float4 k0 = ld_c(&kc[0]), k1 = ld_c(&kc[1]);   // (Mt, Md, chi, clo), (kph, kpl, kqh, kql)
+    const uint32_t sb = (uint32_t)min(max(ld_c(&itc.b), 0), a.B - 1);
     float bias[16];   // the bias alone (not folded into the draft logits: the residual
                       // compares P p with q and keeps their rounding apart)
     if (MARKOV) {
@@ -1193,30 +1264,23 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
     fetch(hn, tb, db);
     hn = hnn;
     if (rag) mask_shift(xt, shift);
-    // residual weights, their sum and the race, four ids (one generator block) at a time
+    // residual weights (normalised) and their sum; then the race over them
     float s = 0.f;
-    Top2 rt = top2_empty();
+    float wr[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 xr = philox4(sb, (uint32_t)(c0 >> 2) + i, kPurposeSample, a.step, a.key0, a.key1);
-      const uint32_t xs[4] = {xr.x, xr.y, xr.z, xr.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = 4 * i + u;
-        const float tp = xt[e] - k0.x;
-        const float d = MARKOV ? xd[e] + bias[e] : xd[e];
-        const float tq = d - k0.y;
-        const float ep = fmaf(tp, k0.z, k1.x) + fmaf(tp, k0.w, k1.y);
-        const float eq = fmaf(tq, k0.z, k1.z) + fmaf(tq, k0.w, k1.w);
-        const float wv = __builtin_amdgcn_exp2f(ep) - __builtin_amdgcn_exp2f(eq);
-        const bool pos = (VEC || c0 + e < a.V) && wv > 0.f;
-        s += pos ? wv : 0.f;
-        const float sc = __builtin_amdgcn_logf(wv) - clock_log2_f32(xs[u]);
-        top2_add(rt, pos ? sc : -INFINITY, pos ? c0 + e : INT_MAX);
-      }
+    for (int e = 0; e < 16; ++e) {
+      const float tp = xt[e] - k0.x;
+      const float d = MARKOV ? xd[e] + bias[e] : xd[e];
+      const float tq = d - k0.y;
+      const float ep = fmaf(tp, k0.z, k1.x) + fmaf(tp, k0.w, k1.y);
+      const float eq = fmaf(tq, k0.z, k1.z) + fmaf(tq, k0.w, k1.w);
+      const float wv = __builtin_amdgcn_exp2f(ep) - __builtin_amdgcn_exp2f(eq);
+      wr[e] = ((VEC || c0 + e < a.V) && wv > 0.f) ? wv : 0.f;
+      s += wr[e];
     }
     s = sum4lanes(s);
-    rt = top2_4lanes(rt);
+    park16(park[tid], wr);
+    const Top2 rt = top2_4lanes(race16<false>(park[tid], 0.f, 1.f, c0, sb, kPurposeSample, a));
     if (q == 0) {
       part[(c % kFlush) * kChunk + n][w] = s;
       rpart[(c % kFlush) * kChunk + n][w] = rt;
@@ -1225,45 +1289,51 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
       __syncthreads();
       const int it = (c - c % kFlush) * kChunk + tid;
       if (tid < (c % kFlush + 1) * kChunk && it < NI) {
-        const int dr = a.ws.items[it].dr;
-        a.ws.wgrp[(size_t)g * ND + dr] = (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]);
+        const int dr = min(max(ld_c(&a.ws.items[it].dr), 0), ND - 1);
+        st_c(&a.ws.wgrp[(size_t)g * ND + dr], (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]));
         Top2 r = rpart[tid][0];
 #pragma unroll
         for (int ww = 1; ww < kWaves; ++ww) top2_merge(r, rpart[tid][ww]);
-        a.ws.race[(size_t)g * ND + it] = r;
+        st_c(&a.ws.race[(size_t)g * ND + it], r);
       }
       __syncthreads();
     }
   }
   // bonus rows the verifiers stop at (listed from the back of the list): race
-  // candidates of p_gamma, log2 w = x c (unnormalised: every group of the row uses the
-  // same scale, which is all the race needs)
+  // candidates of p_gamma, log2 w = x log2(e) / T (unnormalised: every group of the
+  // row uses the same scale, which is all the race needs)
   for (int c = 0; c < (NB + kChunk - 1) / kChunk; ++c) {
     const int ib = ND - 1 - min(c * kChunk + n, NB - 1);
-    const Item& it = a.ws.items[ib];
+    const Item it = ld_c(&a.ws.items[ib]);
     const int tr = min(max(it.tr, 0), NT - 1);
     const uint32_t sb = (uint32_t)min(max(it.b, 0), a.B - 1);
-    const float chi = it.chi, clo = it.clo;
+    const float chi = it.chi, clo = it.clo;   // log2(e) / T as hi + lo
     Raw16<DT> t;
     raw_load<DT, VEC>(t, reinterpret_cast<const char*>(a.target) + (size_t)tr * rb, c0, a.V);
     float x[16];
     raw_to_f32<DT>(t, x);
     if (rag) mask_shift(x, shift);
-    float lw[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      lw[e] = ((VEC || c0 + e < a.V) && x[e] != -INFINITY) ? fmaf(x[e], chi, x[e] * clo) : -INFINITY;
-    const Top2 rt = top2_4lanes(race16(lw, c0, sb, kPurposeSample, a));
+    for (int e = 0; e < 16; ++e) x[e] = (VEC || c0 + e < a.V) ? x[e] : -INFINITY;
+    park16(park[tid], x);
+    const Top2 rt = top2_4lanes(race16<true>(park[tid], max16(x), chi + clo, c0, sb, kPurposeSample, a));
     if (q == 0) rpart[n][w] = rt;
     __syncthreads();
     if (tid < kChunk && c * kChunk + tid < NB) {
       Top2 r = rpart[tid][0];
 #pragma unroll
       for (int ww = 1; ww < kWaves; ++ww) top2_merge(r, rpart[tid][ww]);
-      a.ws.race[(size_t)g * ND + (ND - 1 - (c * kChunk + tid))] = r;
+      st_c(&a.ws.race[(size_t)g * ND + (ND - 1 - (c * kChunk + tid))], r);
     }
     __syncthreads();
   }
+}
+
+template <int DT, int KS, bool MARKOV, bool VEC>
+__global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
+  __shared__ Pass2Lds L;
+  bf16x8 A[4][KS];
+  pass2_body<DT, KS, MARKOV, VEC>(a, blockIdx.x, L, A, false);
 }
 
 // ---------------------------------------------------------------------------
@@ -1367,12 +1437,12 @@ __device__ int race_pick(const Args& a, int it, int ND, RaceLds& sh, double* rs,
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int NG = a.NG;
   // every thread's first two groups are loaded at once (clamped, masked after)
-  Top2 t0 = a.ws.race[(size_t)min(tid, NG - 1) * ND + it];
-  Top2 t1 = a.ws.race[(size_t)min(tid + kThreads, NG - 1) * ND + it];
+  Top2 t0 = ld_c(&a.ws.race[(size_t)min(tid, NG - 1) * ND + it]);
+  Top2 t1 = ld_c(&a.ws.race[(size_t)min(tid + kThreads, NG - 1) * ND + it]);
   if (tid >= NG) t0 = top2_empty();
   if (tid + kThreads >= NG) t1 = top2_empty();
   float best = fmaxf(t0.s1, t1.s1);
-  for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) best = fmaxf(best, a.ws.race[(size_t)gi * ND + it].s1);
+  for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) best = fmaxf(best, ld_c(&a.ws.race[(size_t)gi * ND + it]).s1);
   best = wave_max_dpp(best);
   if (tid == 0) sh.n = 0;
   if (l == 0) sh.best[w] = best;
@@ -1389,7 +1459,7 @@ __device__ int race_pick(const Args& a, int it, int ND, RaceLds& sh, double* rs,
   offer(t0.s1, t0.v1); offer(t0.s2, t0.v2);
   offer(t1.s1, t1.v1); offer(t1.s2, t1.v2);
   for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) {
-    const Top2 t = a.ws.race[(size_t)gi * ND + it];
+    const Top2 t = ld_c(&a.ws.race[(size_t)gi * ND + it]);
     offer(t.s1, t.v1); offer(t.s2, t.v2);
   }
   __syncthreads();
@@ -1427,21 +1497,28 @@ __device__ int full_row_race(const Args& a, const char* row, uint32_t b, double 
   return bv < a.V ? bv : 0;
 }
 
+struct FinalLds {
+  RaceLds rl;
+  double rs[kWaves];
+  int ri[kWaves];
+  double s_R[kMaxK], s_h[kMaxK + 1];
+};
+
+// Finalize of stream b.  Every thread of the workgroup calls it.
 template <int DT, int KS>
-__global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
-  __shared__ RaceLds rl;
-  __shared__ double rs[kWaves];
-  __shared__ int ri[kWaves];
-  __shared__ double s_R[kMaxK], s_h[kMaxK + 1];
-  const int b = blockIdx.x;
+__device__ __forceinline__ void finalize_body(const Args& a, int b, FinalLds& L) {
+  RaceLds& rl = L.rl;
+  double* rs = L.rs;
+  int* ri = L.ri;
+  double *s_R = L.s_R, *s_h = L.s_h;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int k1 = a.k + 1;
   const int NG = a.NG;
   const int ND = a.B * a.k;
-  const int4 info = *reinterpret_cast<const int4*>(a.ws.info + 4 * b);
+  const int4 info = ld_c(reinterpret_cast<const int4*>(a.ws.info + 4 * b));
   const int gamma = info.x, f = info.z;
   int stop = info.y;
-  const uint32_t mask = a.ws.rowmask[b];
+  const uint32_t mask = ld_c(&a.ws.rowmask[b]);
   const float Tf = stream_temp(a, b);
   if (Tf == 0.f) {   // greedy: the scan decided the stop and the token
     if (tid <= a.k) {
@@ -1455,7 +1532,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
     if (tid == 0) a.accepted_len[b] = stop;
     return;
   }
-  const int2 info2 = *reinterpret_cast<const int2*>(a.ws.info2 + 4 * b);
+  const int2 info2 = ld_c(reinterpret_cast<const int2*>(a.ws.info2 + 4 * b));
   const double T = (double)Tf;
   const double c = kLog2e / T;
   const size_t esz = DT == kBF16 ? 2 : 4;
@@ -1477,7 +1554,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
           float x[kLoadsInFlight];
 #pragma unroll
           for (int u = 0; u < kLoadsInFlight; ++u)
-            x[u] = a.ws.wgrp[(size_t)min(g0 + l + 64 * u, NG - 1) * ND + dr];
+            x[u] = ld_c(&a.ws.wgrp[(size_t)min(g0 + l + 64 * u, NG - 1) * ND + dr]);
 #pragma unroll
           for (int u = 0; u < kLoadsInFlight; ++u)
             if (g0 + l + 64 * u < NG) v += (double)x[u];
@@ -1485,7 +1562,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
         v = wave_sum(v);
         if (l == 0) {
           s_R[i] = v;
-          s_h[i] = v / (v - expm1(a.ws.logP[b * k1 + i]));
+          s_h[i] = v / (v - expm1(ld_c(&a.ws.logP[b * k1 + i])));
         }
       }
       ++ci;
@@ -1510,9 +1587,9 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
   if (resid) {
     // w(v) = max(0, P_s p_s(v) - q_s(v)) in fp64 from the exact logits, the fp64 row
     // normalisers and the fp64 Markov bias at v
-    const double Mt = (double)a.ws.tm[tr], tl2s = a.ws.tl2s[tr];
-    const double Md = (double)a.ws.dm[dr], dl2s = a.ws.dl2s[dr];
-    const double lpP = a.method == 1 ? a.ws.logP[tr] * kLog2e : 0.0;
+    const double Mt = (double)ld_c(&a.ws.tm[tr]), tl2s = ld_c(&a.ws.tl2s[tr]);
+    const double Md = (double)ld_c(&a.ws.dm[dr]), dl2s = ld_c(&a.ws.dl2s[dr]);
+    const double lpP = a.method == 1 ? ld_c(&a.ws.logP[tr]) * kLog2e : 0.0;
     const int prev = a.W1 != nullptr ? draft_prev(a, b, s) : -1;
     Y = race_pick(a, it, ND, rl, rs, ri, [&](int v) {
       const double bias = a.W1 != nullptr ? bias_f64_wave(a, prev, v) : 0.0;
@@ -1542,17 +1619,125 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
     if (a.diag != nullptr) {
       double* dg = a.diag + ((size_t)b * k1 + tid) * 5;
       const bool slot = tid < gamma;
-      dg[0] = slot ? a.ws.lpx[b * a.k + tid] : NAN;
-      dg[1] = slot ? a.ws.lqx[b * a.k + tid] : NAN;
-      dg[2] = tid <= gamma ? exp(a.ws.logP[b * k1 + tid]) : NAN;
+      const double lP = tid <= gamma ? ld_c(&a.ws.logP[b * k1 + tid]) : 0.0;
+      dg[0] = slot ? ld_c(&a.ws.lpx[b * a.k + tid]) : NAN;
+      dg[1] = slot ? ld_c(&a.ws.lqx[b * a.k + tid]) : NAN;
+      dg[2] = tid <= gamma ? exp(lP) : NAN;
       dg[3] = (a.method == 1 && tid < kMaxK) ? s_R[tid] : NAN;
       double h = (a.method == 1 && tid <= kMaxK) ? s_h[tid] : NAN;
-      if (a.method == 1 && tid == gamma && gamma >= 1) h = exp(a.ws.logP[b * k1 + gamma]);
-      if (a.method == 1 && tid >= 1 && tid < gamma && a.ws.logP[b * k1 + tid] == 0.0) h = 1.0;
+      if (a.method == 1 && tid == gamma && gamma >= 1) h = exp(lP);
+      if (a.method == 1 && tid >= 1 && tid < gamma && lP == 0.0) h = 1.0;
       dg[4] = h;
     }
   }
   if (tid == 0) a.accepted_len[b] = s;
+}
+
+template <int DT, int KS>
+__global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
+  __shared__ FinalLds L;
+  finalize_body<DT, KS>(a, blockIdx.x, L);
+}
+
+// ---------------------------------------------------------------------------
+// The fused verify launch: pass 1, scan, pass 2 and finalize as phases of one
+// launch of G >= NG workgroups, all resident at once (the host checks occupancy):
+//   phase 1  pass 1 for group g (g < NG); the workgroup keeps its W2 slab
+//   phase 2  the scan of streams g, g + G, ... (workgroups g < B, which load their
+//            slab again afterwards: the scan needs the registers)
+//   phase 3  pass 2 for group g, on the slab still in registers (W2 is read once
+//            but for the scanning workgroups' slabs)
+//   phase 4  finalize of streams g, g + G, ...
+// with a grid barrier between phases.  Data one phase leaves for another goes
+// through agent-coherent accesses (ld_c / st_c), so the barrier needs no cache
+// maintenance: each wave waits for its own memory operations, workgroup g then
+// writes its arrival word, workgroup 0 waits for all of them and writes the go word.
+// A wait gives up after ~0.2 s (s_memrealtime counts at 100 MHz), sets the error
+// word and goes on; finalize then marks its streams' outputs invalid (accepted
+// length -1).  That can only happen if the workgroups are not all resident (for
+// example another kernel on the device holding compute units), never as part of a
+// normal call.
+// ---------------------------------------------------------------------------
+constexpr uint64_t kBarrierTicks = 20000000ull;
+
+__device__ __forceinline__ void spin_until_ge(int* p, int v, int* err) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (ld_c(p) < v) {
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kBarrierTicks) {
+      st_c(err, 1);
+      break;
+    }
+  }
+}
+
+__device__ __forceinline__ void grid_barrier(const Args& a, int phase) {
+  wait_memory();
+  __syncthreads();
+  int* sync = a.ws.sync;
+  const int g = blockIdx.x, G = gridDim.x;
+  if (threadIdx.x == 0) st_c(&sync[kSyncStride * (1 + g)], phase);
+  if (g == 0) {
+    for (int i = threadIdx.x; i < G; i += kThreads) spin_until_ge(&sync[kSyncStride * (1 + i)], phase, &sync[1]);
+    __syncthreads();
+    if (threadIdx.x == 0) st_c(&sync[0], phase);
+  } else if (threadIdx.x == 0) {
+    spin_until_ge(&sync[0], phase, &sync[1]);
+  }
+  __syncthreads();
+}
+
+template <int KS, bool MARKOV>
+__host__ __device__ constexpr size_t fused_lds_bytes() {
+  size_t m = sizeof(Pass1Lds<KS, MARKOV>);
+  m = m > sizeof(ScanPhaseLds) ? m : sizeof(ScanPhaseLds);
+  m = m > sizeof(Pass2Lds) ? m : sizeof(Pass2Lds);
+  m = m > sizeof(FinalLds) ? m : sizeof(FinalLds);
+  return (m + 15) / 16 * 16;
+}
+
+template <int DT, int KS, bool MARKOV, bool VEC>
+__global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(Args a) {
+  extern __shared__ __align__(16) char table[];   // pass 1's stream table
+  __shared__ __align__(16) char lds[fused_lds_bytes<KS, MARKOV>()];
+  const int g = blockIdx.x, G = gridDim.x;
+  bf16x8 A[4][KS];
+  if (g < a.NG) pass1_body<DT, KS, MARKOV, VEC>(a, g, a.NG, *reinterpret_cast<Pass1Lds<KS, MARKOV>*>(lds), table, A);
+  grid_barrier(a, 1);
+  if (g < a.B) {
+    // a workgroup with streams to scan gives its slab's registers to the scan and loads
+    // the slab again afterwards (at B = 64 of 505 groups: 8 MB of W2); the others keep
+    // theirs through phase 2
+    for (int b = g; b < a.B; b += G) {
+      scan_body<DT>(a, b, *reinterpret_cast<ScanPhaseLds*>(lds));
+      __syncthreads();
+    }
+    grid_barrier(a, 2);
+    if (MARKOV) {   // A is defined on every path here, so the old slab is dead during the scan
+      if (g < a.NG) {
+        const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+        load_w2_slab<KS, VEC>(a, g * kGroup + w * kWaveCols, l & 15, l >> 4, A);
+      } else {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) A[s4][kk] = zero_bf16x8();
+      }
+    }
+  } else {
+    grid_barrier(a, 2);
+  }
+  if (g < a.NG) pass2_body<DT, KS, MARKOV, VEC>(a, g, *reinterpret_cast<Pass2Lds*>(lds), A, true);
+  grid_barrier(a, 3);
+  const bool failed = ld_c(&a.ws.sync[1]) != 0;
+  for (int b = g; b < a.B; b += G) {
+    if (failed) {
+      if (threadIdx.x <= a.k) a.out_tokens[b * (a.k + 1) + threadIdx.x] = -1;
+      if (threadIdx.x == 0) a.accepted_len[b] = -1;
+      continue;
+    }
+    finalize_body<DT, KS>(a, b, *reinterpret_cast<FinalLds*>(lds));
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1568,6 +1753,7 @@ template <int DT, int KS, bool MARKOV, bool VEC>
 __global__ __launch_bounds__(kThreads, 2) void walk_partials_kernel(Args a, int j) {
   __shared__ float2 part[kWalkRows][kWaves];
   __shared__ Top2 rpart[kWalkRows][kWaves];
+  __shared__ float4 park[kThreads][4];   // a lane's 16 biased logits for the race
   __shared__ int s_prev[kWalkRows];
   __shared__ float s_c[kWalkRows];
   __shared__ uint4 w1s[MARKOV ? kWalkRows * (4 * KS + 1) : 1];   // W1 rows, padded stride
@@ -1636,11 +1822,11 @@ __global__ __launch_bounds__(kThreads, 2) void walk_partials_kernel(Args a, int 
       if (rag) mask_shift(x, shift);
       const float2 pw = row_partial<0>(x, s_c[rr]);
       // race candidates of q_j: log2 w = x log2(e) / T, a common scale for the row
-      float lw[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) lw[e] = ((VEC || c0 + e < a.V) && x[e] != -INFINITY) ? x[e] * s_c[rr] : -INFINITY;
+      for (int e = 0; e < 16; ++e) x[e] = (VEC || c0 + e < a.V) ? x[e] : -INFINITY;
       const uint32_t sb = (uint32_t)min(r0 + rr, a.B - 1);
-      const Top2 rt = top2_4lanes(race16(lw, c0, sb, walk_purpose(j), a));
+      park16(park[tid], x);
+      const Top2 rt = top2_4lanes(race16<true>(park[tid], max16(x), s_c[rr], c0, sb, walk_purpose(j), a));
       if (q == 0) {
         part[rr][w] = pw;
         rpart[rr][w] = rt;
@@ -1930,15 +2116,60 @@ __global__ __launch_bounds__(kThreads) void adaptive_kernel(AdaptArgs aa) {
 // ---------------------------------------------------------------------------
 // launch wrappers (host side of this translation unit)
 // ---------------------------------------------------------------------------
+// Workgroups of the fused launch for this problem on the current device, or 0 when
+// they could not all be resident at once (then the call uses separate launches).
+// The resident count per CU comes from the runtime's occupancy calculator and is
+// cached per device for each kernel instance.  DSPARK_VERIFY_LAUNCH=separate in the
+// environment forces separate launches.
 template <int DT, int KS, bool MARKOV, bool VEC>
-static hipError_t launch_passes(const Args& a, hipStream_t st, void* const* ev) {
+static int fused_grid_for(const Args& a) {
+  const char* env = getenv("DSPARK_VERIFY_LAUNCH");
+  if (env != nullptr && strcmp(env, "separate") == 0) return 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  static int cus[64], occ[64][2];   // occ[dev][0]: table bytes it was computed for (+1)
+  static std::mutex mu;
+  const size_t table = stream_table_bytes(a.B);
+  int resident;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0 && hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    if (occ[dev][0] != (int)table + 1) {
+      int o = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, verify_fused_kernel<DT, KS, MARKOV, VEC>, kThreads,
+                                                       table) != hipSuccess)
+        return 0;
+      occ[dev][0] = (int)table + 1;
+      occ[dev][1] = o;
+    }
+    resident = occ[dev][1] * cus[dev];
+  }
+  if (a.NG > resident) return 0;
+  const int G = a.NG > a.B ? a.NG : (a.B < resident ? a.B : resident);
+  return G <= kMaxFusedGrid ? G : 0;
+}
+
+template <int DT, int KS, bool MARKOV, bool VEC>
+static hipError_t launch_passes(const Args& a0, hipStream_t st, void* const* ev) {
   auto mark = [&](int i) {
     if (ev != nullptr && ev[i] != nullptr) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[i]), st);
   };
+  Args a = a0;
+  a.fused_grid = 0;
+  if constexpr (VEC) a.fused_grid = fused_grid_for<DT, KS, MARKOV, VEC>(a);   // aligned rows only
   const int nchd = (a.B * a.k + kChunk - 1) / kChunk;
   mark(0);
   hipLaunchKernelGGL(pack_kernel, dim3(nchd), dim3(64), 0, st, a);
   mark(1);
+  if constexpr (VEC) {
+    if (a.fused_grid > 0) {   // the four other stages in one launch: their events coincide
+      hipLaunchKernelGGL((verify_fused_kernel<DT, KS, MARKOV, VEC>), dim3(a.fused_grid), dim3(kThreads),
+                         stream_table_bytes(a.B), st, a);
+      for (int i = 2; i <= 5; ++i) mark(i);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((pass1_kernel<DT, KS, MARKOV, VEC>), dim3(a.NG), dim3(kThreads), stream_table_bytes(a.B), st, a);
   mark(2);
   hipLaunchKernelGGL((scan_kernel<DT>), dim3(a.B), dim3(kThreads), 0, st, a);
