@@ -92,9 +92,10 @@ def lib() -> ctypes.CDLL:
         L.dspark_cost_table_stats.restype = i32
         L.dspark_cost_table_log.argtypes = [vp, vp, vp, i32]
         L.dspark_cost_table_log.restype = i32
+        L.dspark_random_words.argtypes = [ctypes.c_uint64, u32, u32, u32, u32, i32, i32, vp, vp]
+        L.dspark_random_words.restype = i32
         L.dspark_status_string.argtypes = [i32]
         L.dspark_status_string.restype = ctypes.c_char_p
-        del u32
         _lib = L
     return _lib
 
@@ -207,6 +208,17 @@ def verify_tokenwise(target, draft, draft_tokens, **kw):
 def verify_block(target, draft, draft_tokens, **kw):
     """Block verification; returns (accepted_len [B], out_tokens [B, k+1], diag or None)."""
     return _verify("dspark_verify_block", target, draft, draft_tokens, **kw)
+
+
+def random_words(seed: int, b: int, purpose: int, step: int, idx0: int, n: int, kind: int, device="cuda:0"):
+    """The generator words a call draws (kind 0: word 0 of counter (b, idx0 + i, purpose,
+    step); kind 1: word idx0 + i of the stream of (b, purpose, step)); uint32 as int32 [n]."""
+    dev = torch.device(device)
+    out = torch.empty(n, dtype=torch.int32, device=dev)
+    _check(lib().dspark_random_words(int(seed) & 0xFFFFFFFFFFFFFFFF, int(b) & 0xFFFFFFFF, int(purpose) & 0xFFFFFFFF,
+                                     int(step) & 0xFFFFFFFF, int(idx0) & 0xFFFFFFFF, int(n), int(kind), _ptr(out),
+                                     _stream(dev)))
+    return out
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20

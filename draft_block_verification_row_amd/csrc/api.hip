@@ -279,6 +279,16 @@ dspark_status dspark_draft_scatter(const void* reduced, const int32_t* vocab_ids
   return DSPARK_OK;
 }
 
+dspark_status dspark_random_words(uint64_t seed, uint32_t b, uint32_t purpose, uint32_t step, uint32_t idx0, int32_t n,
+                                  int32_t kind, uint32_t* out, void* stream) {
+  if (out == nullptr || n < 0 || (kind != 0 && kind != 1)) return DSPARK_ERR_INVALID_ARG;
+  if (n == 0) return DSPARK_OK;
+  if (launch_random_words(seed, b, purpose, step, idx0, n, kind, out, reinterpret_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return DSPARK_ERR_HIP;
+  return DSPARK_OK;
+}
+
 int32_t dspark_k_for_batch(const int32_t* schedule, int32_t n, int32_t batch, int32_t k_default) {
   if (schedule == nullptr) return k_default;
   for (int32_t i = 0; i < n; ++i)

@@ -330,6 +330,8 @@ hipError_t launch_verify(const Args& a, hipStream_t st, void* const* events);
 hipError_t launch_walk(const Args& a, int32_t* tokens_out, double* logq_out, hipStream_t st);
 hipError_t launch_markov_bias(const BiasArgs& ba, int NG, hipStream_t st);
 hipError_t launch_adaptive(const AdaptArgs& aa, hipStream_t st);
+hipError_t launch_random_words(uint64_t seed, uint32_t b, uint32_t purpose, uint32_t step, uint32_t idx0, int n,
+                               int kind, uint32_t* out, hipStream_t st);
 hipError_t launch_scatter(const void* in, const int32_t* ids, int rows, int K, int V, int dtype, void* out,
                           hipStream_t st);
 

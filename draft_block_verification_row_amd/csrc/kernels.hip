@@ -1956,6 +1956,28 @@ __global__ __launch_bounds__(kThreads) void walk_pick_kernel(Args a, int j, int3
 }
 
 // ---------------------------------------------------------------------------
+// The generator words the sampler draws, for callers that replay or audit a call:
+// kind 0, word 0 of counter (b, idx0 + i, purpose, step) (the accept uniforms' words);
+// kind 1, word idx0 + i of the stream of (b, purpose, step), i.e. word v mod 4 of
+// counter (b, v div 4, purpose, step) for v = idx0 + i (the race clocks' words).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void random_words_kernel(uint32_t k0, uint32_t k1, uint32_t b, uint32_t purpose,
+                                                                uint32_t step, uint32_t idx0, int n, int kind,
+                                                                uint32_t* out) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t idx = idx0 + (uint32_t)i;
+  out[i] = kind == 0 ? philox_word0(b, idx, purpose, step, k0, k1) : stream_word(k0, k1, b, idx, purpose, step);
+}
+
+hipError_t launch_random_words(uint64_t seed, uint32_t b, uint32_t purpose, uint32_t step, uint32_t idx0, int n,
+                               int kind, uint32_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(random_words_kernel, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, st,
+                     (uint32_t)(seed & 0xffffffffu), (uint32_t)(seed >> 32), b, purpose, step, idx0, n, kind, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Reduced draft vocabulary [P1 §3 "The Markov fix-up": the drafter scores a reduced
 // vocabulary and scatters its logits into target-vocabulary columns]: every other
 // column is -inf, so q = 0 there and the residual keeps the target's mass.

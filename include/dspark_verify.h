@@ -299,6 +299,18 @@ dspark_status dspark_cost_table_stats(const dspark_cost_table* table, int64_t* f
                                       int32_t* in_flight);
 int32_t dspark_cost_table_log(const dspark_cost_table* table, int32_t* tokens, float* ms, int32_t cap);
 
+/*
+ * The random words behind a call, for replaying or auditing it (see the conventions
+ * above): kind 0 writes word 0 of Philox counter (b, idx0 + i, purpose, step) for
+ * i < n (purpose 1: the words of the accept uniforms u_{b,j}, j = idx0 + i); kind 1
+ * writes word idx0 + i of the output stream of (b, purpose, step), i.e. word v mod 4
+ * of counter (b, v div 4, purpose, step) for v = idx0 + i (purpose 3: the words of
+ * the race clocks of the emitted token; 16 + j: slot j of the drafter's walk).
+ * out: device uint32 [n].  One launch.
+ */
+dspark_status dspark_random_words(uint64_t seed, uint32_t b, uint32_t purpose, uint32_t step, uint32_t idx0,
+                                  int32_t n, int32_t kind, uint32_t* out, void* stream);
+
 /* Static description of a status code. */
 const char* dspark_status_string(dspark_status status);
 

@@ -122,5 +122,10 @@ def compare(g, o, wl, method, tally: Tally, label=""):
 
 
 def assert_clean(tally: Tally, max_near_frac: float = 1e-4):
+    """No unexplained difference; near decisions at most max_near_frac of all decisions
+    (at least one is let through only while there are fewer than 10^4 decisions)."""
     assert not tally.unexplained, tally.summary() + "\n" + "\n".join(map(str, tally.unexplained[:20]))
-    assert tally.near <= max(1, int(max_near_frac * tally.decisions)), tally.summary()
+    limit = max_near_frac * tally.decisions
+    if tally.decisions <= 10000:
+        limit = max(1.0, limit)
+    assert tally.near <= limit, tally.summary()
