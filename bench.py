@@ -9,12 +9,17 @@ draft blocks (so a step verifies 2*B blocks).  Inputs are resident in HBM before
 the timed region; several copies of the whole input set rotate so that no call
 finds its inputs in the 256 MB Infinity Cache.
 
-Prints one JSON line.  ``value`` = verified draft blocks per second.
-``roofline`` is for the dominant launch (row statistics, pass 1), timed with
-HIP events recorded around it by the library's stage hook on the same stream,
-and compared both with the published HBM peak and with a plain streaming read
-measured on the same device (the package's stream-read kernel).
-``cpu_baseline`` is the fp64 oracle on the host, on the same batch.
+Prints one JSON line.  ``value`` = verified draft blocks per second over whole steps.
+``roofline`` is for the dominant launch: the fused verify launch (row statistics,
+scan, residual masses and sampler as phases of one grid), algorithmic bytes of the
+call (every draft-slot row pair once, the bonus row where it is sampled, W2 once,
+small I/O; the W1 rows are the pack launch's) over its duration from HIP events
+the library records around each launch on the call's stream.  ``per_call`` gives,
+per verifier, the whole call (pack + verify launch) against the same byte model, and
+``pass1_separate_launch`` the streaming pass alone when the stages run as separate
+launches.  ``configs`` times each named configuration by itself (median, 10th and
+90th percentile per call).  ``cpu_baseline`` is the fp64 oracle on the host: whole
+calls in parallel worker processes, and one thread.
 """
 from __future__ import annotations
 
@@ -31,12 +36,11 @@ METRIC = "verified draft blocks/s (B x k x V) and achieved HBM GB/s at B=64,k=5,
 HBM_PEAK_GBS = 8000.0
 STAGE_NAMES = ["pack W1 tiles", "pass1 row statistics", "scan", "pass2 residual masses", "finalize/sampler"]
 
-# HBM traffic of one pass-1 launch at this workload, from two rocprofv3 --pmc runs
-# (FETCH_SIZE, then WRITE_SIZE; profiles/pass1_headline_b64_k5_v129280_hbm_bytes.md):
-# FETCH_SIZE scaled by 2.0 (a 256 MiB device copy reads as 128 MiB), WRITE_SIZE by 1.0.
+# HBM traffic of one fused verify launch at this workload, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE; profiles/verify_fused_headline_b64_k5_v129280_hbm_bytes.md),
+# each scaled by what the same counter reads for a plain device copy of known size.
 # Valid only for the kernel sources it was measured on (hash below); otherwise null.
-PASS1_TRAFFIC = {"src_sha256_16": "4932efc03d18dfe3", "fetch_bytes": 114280.4 * 1024 * 2.0,
-                 "write_bytes": 2937.1 * 1024 * 1.0}
+FUSED_TRAFFIC = {"src_sha256_16": "", "fetch_bytes": 0.0, "write_bytes": 0.0}
 
 
 def kernel_src_hash() -> str:
@@ -122,11 +126,194 @@ def read_ceiling(torch, dev, nbytes=1 << 30, nbuf=3, reps=12):
     return best
 
 
+def launch_profile(dv, hip, run, n, launches):
+    """Launch durations of n calls from the library's stage events (run(i, events) makes
+    call i and records them).  A fused call (2 launches) records events 0..2 only: before
+    the pack launch, between the two launches, after the verify launch (every event
+    recorded on the stream adds a few microseconds to the call, so no empty ones)."""
+    fused = launches == 2
+    nev = 3 if fused else dv.STAGES + 1
+    evs = [hip.create(nev) for _ in range(n)]
+    for i in range(n):
+        run(i, evs[i] + [None] * (dv.STAGES + 1 - nev))
+    import torch
+    torch.cuda.synchronize()
+    st = np.array([[hip.ms(e[j], e[j + 1]) for j in range(nev - 1)] for e in evs])
+    for e in evs:
+        hip.destroy(e)
+    call = st.sum(axis=1)
+    names = (["pack_kernel", "verify_fused_kernel"] if fused else
+             ["pack_kernel", "pass1_kernel", "scan_kernel", "pass2_kernel", "finalize_kernel"])
+    return {"launches": launches, "stage_ms": st.mean(axis=0), "call_ms_mean": float(call.mean()),
+            "call_ms_pct": np.percentile(call, [10, 50, 90]), "main_ms_mean": float(st[:, 1].mean()),
+            "by_launch_ms": {name: float(st[:, j].mean()) for j, name in enumerate(names)}}
+
 def alg_bytes(B, k, V, R, e, s, gamma) -> float:
     """Algorithmic bytes of one verify call: every draft-slot row pair once, the bonus row
     only where it is sampled, W2 once and the gathered W1 rows, plus the small I/O."""
     rows = float(np.sum(2 * gamma + (s == gamma)))
     return e * V * rows + 2.0 * R * V + 2.0 * R * float(np.sum(gamma)) + 16.0 * B * k
+
+
+# ---------------------------------------------------------------------------
+# per-configuration table: each named workload alone, per-call times of both verifiers
+# ---------------------------------------------------------------------------
+CONFIG_TABLE = [
+    ("c2", "B=1 k=5 V=129280 fp32 logits, Markov rank 256, T=1"),
+    ("c3", "B=16 k=5 V=129280 bf16, Markov rank 256"),
+    ("h", "B=64 k=5 V=129280 bf16, Markov rank 256 (the headline shape)"),
+    ("h_nomarkov", "B=64 k=5 V=129280 bf16, no Markov bias"),
+    ("c4", "B=64 k=9 V=129280 bf16, Markov rank 256 (drafts past the trained block)"),
+    ("c5", "B=256 k=5 V=129280 bf16, Markov rank 256, ragged counts from the confidence head"),
+]
+
+
+def config_table(torch, dv, workloads, dev, ncalls):
+    """Per-call time of each verifier at each configuration, inputs resident, events
+    around every call on the library's stream; median, 10th and 90th percentiles."""
+    out = {}
+    for name, desc in CONFIG_TABLE:
+        wl = workloads.make(name)
+        B, k, V, R = wl.B, wl.k, wl.V, wl.R
+        e = 2 if wl.dtype == "bf16" else 4
+
+        def up(x):
+            if x is None:
+                return None
+            a = np.ascontiguousarray(x)
+            if a.dtype == np.uint16:
+                a = a.view(np.int16)
+            return torch.from_numpy(a).to(dev)
+
+        in_bytes = e * V * B * (2 * k + 1) + 2 * R * V
+        nsets = 3 if in_bytes < (300 << 20) else 1   # rotate copies unless one set already exceeds the cache
+        base = dict(target=up(wl.target), draft=up(wl.draft), tokens=up(wl.draft_tokens.astype(np.int32)),
+                    temp=up(wl.temperature), anchor=up(wl.anchor.astype(np.int32)), W1=up(wl.W1), W2t=up(wl.W2t))
+        nd = None
+        if wl.hidden is not None:
+            n, _, _ = dv.adaptive_k(up(wl.hidden), up(wl.conf_w), wl.conf_b, wl.verify_ms, want_c=False)
+            nd = n
+        sets = [base] + [{kk: (None if v is None else v.clone()) for kk, v in base.items()} for _ in range(nsets - 1)]
+        ws = torch.empty(dv.workspace_bytes(B, k, V, dv.DSPARK_BF16 if e == 2 else dv.DSPARK_F32),
+                         dtype=torch.uint8, device=dev)
+        fn = {"tokenwise": dv.verify_tokenwise, "block": dv.verify_block}
+        row = {"desc": desc, "B": B, "k": k, "V": V, "R": R, "input_sets_rotated": nsets}
+        for m in ("tokenwise", "block"):
+            o = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, k + 1, dtype=torch.int32, device=dev),
+                 None)
+
+            def run(i):
+                s = sets[i % nsets]
+                fn[m](s["target"], s["draft"], s["tokens"], num_drafts=nd, temperature=s["temp"], W1=s["W1"],
+                      W2t=s["W2t"], anchor=s["anchor"], seed=wl.seed, step=i, workspace=ws, out=o)
+
+            for i in range(5):
+                run(i)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ncalls)]
+            torch.cuda.synchronize()
+            for i in range(ncalls):
+                ev[i][0].record()
+                run(100 + i)
+                ev[i][1].record()
+            torch.cuda.synchronize()
+            t = np.array([a.elapsed_time(b) for a, b in ev])
+            acc = o[0].cpu().numpy()
+            gam = np.full(B, k) if nd is None else nd.cpu().numpy()
+            balg = alg_bytes(B, k, V, R, e, acc, gam)
+            p10, p50, p90 = np.percentile(t, [10, 50, 90])
+            row[m] = {"us_p10_p50_p90": [round(x * 1e3, 2) for x in (p10, p50, p90)],
+                      "blocks_per_s_median": round(B / (p50 * 1e-3), 1),
+                      "alg_bytes": int(balg),
+                      "frac_median": round(balg / (p50 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        out[name] = row
+        log(f"  {name}: tokenwise {row['tokenwise']['us_p10_p50_p90']} us, block {row['block']['us_p10_p50_p90']} us")
+        del sets, base, ws
+        torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------
+# cpu_baseline: the fp64 oracle, one thread, then whole calls in parallel processes
+# ---------------------------------------------------------------------------
+_CPU_WL = {}
+
+
+def _cpu_worker_init():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+    import workloads
+    _CPU_WL["wl"] = workloads.make_zipf("h", 64, 64, 5, confidence=True)
+
+
+def _cpu_worker_ready(_):
+    return os.getpid()
+
+
+def _cpu_worker_call(args):
+    method, step = args
+    from oracle import dspark as odsp   # cpu_baseline leg only
+    wl = _CPU_WL["wl"]
+    odsp.verify(wl.target, wl.draft, wl.dtype, wl.draft_tokens, wl.temperature, wl.anchor, wl.W1, wl.W2t,
+                seed=wl.seed, step=step, method=method)
+    return method
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(B):
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    import workloads
+    from oracle import dspark as odsp   # cpu_baseline leg only
+    from threadpoolctl import threadpool_limits
+    wl = workloads.make_zipf("h", 64, 64, 5, confidence=True)
+    one = {}
+    with threadpool_limits(1):
+        for m in ("tokenwise", "block"):
+            c0 = time.perf_counter()
+            odsp.verify(wl.target, wl.draft, wl.dtype, wl.draft_tokens, wl.temperature, wl.anchor, wl.W1, wl.W2t,
+                        seed=wl.seed, step=0, method=m)
+            one[m] = time.perf_counter() - c0
+        c0 = time.perf_counter()
+        odsp.adaptive_k(wl.hidden, wl.conf_w, wl.conf_b, wl.verify_ms)
+        one["adaptive"] = time.perf_counter() - c0
+    del wl
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    workers = max(1, min(avail, 16))
+    ncalls = 2 * workers
+    with ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn"), initializer=_cpu_worker_init) as ex:
+        pids, t_ready = set(), time.perf_counter()
+        while len(pids) < workers and time.perf_counter() - t_ready < 120.0:
+            pids |= set(ex.map(_cpu_worker_ready, range(4 * workers)))
+        c0 = time.perf_counter()
+        list(ex.map(_cpu_worker_call, [("tokenwise" if i % 2 == 0 else "block", i) for i in range(ncalls)]))
+        wall = time.perf_counter() - c0
+    return {
+        "value": round(B * ncalls / wall, 3),
+        "unit": "blocks/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"{ncalls} whole verify calls of the headline batch (B={B}, half token-wise, half block, "
+                  f"distinct steps) on {workers} worker processes, one BLAS thread each, {wall:.1f} s wall; "
+                  f"workload built in each worker before timing",
+        "cpu_model": _cpu_model(),
+        "nproc": os.cpu_count(),
+        "cpus_available": avail,
+        "one_thread": {
+            "ms_per_call": {m: round(one[m] * 1e3, 1) for m in ("tokenwise", "block")},
+            "adaptive_head_ms": round(one["adaptive"] * 1e3, 1),
+            "blocks_per_s": round(2 * B / (one["tokenwise"] + one["block"]), 3),
+        },
+    }
 
 
 def main() -> int:
@@ -136,6 +323,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=3, help="rotating copies of the input set")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration table")
+    ap.add_argument("--config-calls", type=int, default=100)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters)")
@@ -203,23 +392,21 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
 
-    # per-launch times: a separate pass with the library's stage events
+    # per-launch times: a pass with the library's stage events around every launch of
+    # each call (pack, then the fused verify launch, or the four separate launches)
     hip = HipEvents()
     nprof = min(args.steps, 50)
-    stage_ms = {m: np.zeros(dv.STAGES) for m in ("tokenwise", "block")}
+    s0 = sets[0]
+    plan = dv.verify_launches(s0["target"], s0["draft"], s0["tokens"], temperature=s0["temp"], W1=s0["W1"],
+                              W2t=s0["W2t"], anchor=s0["anchor"])
+    launch = {m: launch_profile(dv, hip, lambda i, ev, m=m: call(m, sets[i % len(sets)], i, ev), nprof, plan)
+              for m in ("tokenwise", "block")}
+    # the same calls with separate launches, for pass 1's own figure
+    os.environ["DSPARK_VERIFY_LAUNCH"] = "separate"
+    launch_sep = {m: launch_profile(dv, hip, lambda i, ev, m=m: call(m, sets[i % len(sets)], i, ev), nprof, 5)
+                  for m in ("tokenwise", "block")}
+    del os.environ["DSPARK_VERIFY_LAUNCH"]
     realized = {}
-    all_ev = []
-    for i in range(nprof):
-        evs = (hip.create(dv.STAGES + 1), hip.create(dv.STAGES + 1))
-        all_ev.append(evs)
-        one_step(i, evs)
-    torch.cuda.synchronize()
-    for evs in all_ev:
-        for m, e in zip(("tokenwise", "block"), evs):
-            stage_ms[m] += np.array([hip.ms(e[j], e[j + 1]) for j in range(dv.STAGES)])
-        hip.destroy(evs[0] + evs[1])
-    for m in stage_ms:
-        stage_ms[m] /= nprof
     for m in ("tokenwise", "block"):
         call(m, sets[0], 0)
         torch.cuda.synchronize()
@@ -232,12 +419,33 @@ def main() -> int:
     # W1 rows: all of it algorithmic (a sampled bonus row is read by pass 2, only where
     # the verifier stops there)
     full_pass1 = e * V * float(np.sum(2 * gamma)) + 2.0 * R * V + 2.0 * R * float(np.sum(gamma))
+    fused = plan == 2
+    main_name = "verify_fused_kernel" if fused else "pass1_kernel"
+    # the dominant launch: the fused verify launch (all of a call's work but the W1 tile
+    # pack), algorithmic bytes of the whole call less the pack's W1 rows
+    alg_main = {m: bytes_call[m] - (2.0 * R * float(np.sum(gamma)) if fused else 0.0) for m in bytes_call}
+    if not fused:
+        alg_main = {m: full_pass1 for m in bytes_call}
+    t_main = {m: launch[m]["main_ms_mean"] for m in launch}
+    achieved = sum(alg_main.values()) / (sum(t_main.values()) * 1e-3) / 1e9
+    per_call = {}
+    for m in launch:
+        t_call = launch[m]["call_ms_mean"]
+        per_call[m] = {
+            "alg_bytes": int(bytes_call[m]),
+            "call_us": round(t_call * 1e3, 2),
+            "call_us_p10_p50_p90": [round(x * 1e3, 2) for x in launch[m]["call_ms_pct"]],
+            "frac": round(bytes_call[m] / (t_call * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "launch_us": {kname: round(v * 1e3, 2) for kname, v in launch[m]["by_launch_ms"].items()},
+            "blocks_per_s": round(B / (t_call * 1e-3), 1),
+        }
     P1 = STAGE_NAMES.index("pass1 row statistics")
-    t_pass1 = 0.5 * (stage_ms["tokenwise"][P1] + stage_ms["block"][P1])
-    alg_pass1 = full_pass1
-    achieved = alg_pass1 / (t_pass1 * 1e-3) / 1e9
+    t_pass1 = 0.5 * (launch_sep["tokenwise"]["stage_ms"][P1] + launch_sep["block"]["stage_ms"][P1])
     blocks_per_s = 2 * B / (ms_step * 1e-3)
     step_bytes = bytes_call["tokenwise"] + bytes_call["block"] + 2.0 * B * k * 4096
+    traffic = None
+    if kernel_src_hash() == FUSED_TRAFFIC["src_sha256_16"]:
+        traffic = round(FUSED_TRAFFIC["fetch_bytes"] + FUSED_TRAFFIC["write_bytes"])
     result = {
         "metric": METRIC,
         "value": round(blocks_per_s, 1),
@@ -249,7 +457,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {
             "workload": "headline: B=64 k=5 V=129280, bf16 logits (Zipf-biased Gaussian target, correlated "
@@ -263,17 +471,22 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": (round(PASS1_TRAFFIC["fetch_bytes"] + PASS1_TRAFFIC["write_bytes"])
-                        if kernel_src_hash() == PASS1_TRAFFIC["src_sha256_16"] else None),
-            "kernel": "pass1_kernel (row statistics + fused Markov MFMA)",
-            "kernel_ms": round(t_pass1, 5),
-            "alg_bytes_per_launch": int(alg_pass1),
-            "bytes_read_by_design_per_launch": int(full_pass1),
-            "frac_on_bytes_read": round(full_pass1 / (t_pass1 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": main_name,
+            "kernel_us": {m: round(t_main[m] * 1e3, 2) for m in t_main},
+            "alg_bytes_per_launch": {m: int(alg_main[m]) for m in alg_main},
+            "per_call": per_call,
+            "pass1_separate_launch": {
+                "kernel": "pass1_kernel (row statistics + fused Markov MFMA), separate launches",
+                "us": round(t_pass1 * 1e3, 2),
+                "bytes_read_by_design": int(full_pass1),
+                "GBps": round(full_pass1 / (t_pass1 * 1e-3) / 1e9, 1),
+                "frac": round(full_pass1 / (t_pass1 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "stage_us": {m: [round(x * 1e3, 2) for x in launch_sep[m]["stage_ms"]] for m in launch_sep},
+                "stages": STAGE_NAMES,
+            },
         },
-        "stage_ms": {m: [round(x, 5) for x in stage_ms[m]] for m in stage_ms},
-        "stages": STAGE_NAMES,
-        "blocks_per_s_by_verifier": {m: round(B / (float(np.sum(stage_ms[m])) * 1e-3), 1) for m in stage_ms},
+        "blocks_per_s_by_verifier": {m: per_call[m]["blocks_per_s"] for m in per_call},
         "logits_per_s": round(2 * B * k * V / (ms_step * 1e-3), 1),
         "step_alg_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "accepted_mean": {m: round(float(np.mean(realized[m])), 4) for m in realized},
@@ -284,6 +497,8 @@ def main() -> int:
     ceil_gbps, ceil_grid = read_ceiling(torch, dev)
     result["roofline"]["measured_read_GBps"] = round(ceil_gbps, 1)
     result["roofline"]["frac_of_measured_read"] = round(achieved / ceil_gbps, 4)
+    result["roofline"]["pass1_separate_launch"]["frac_of_measured_read"] = round(
+        result["roofline"]["pass1_separate_launch"]["GBps"] / ceil_gbps, 4)
     result["stream_read_ceiling"] = {
         "GBps": round(ceil_gbps, 1), "grid": ceil_grid, "bytes_per_launch": 1 << 30, "buffers": 3,
         "kernel": "dspark_stream_read: grid-stride 16-B loads, 256-thread groups, random bytes",
@@ -396,33 +611,13 @@ def main() -> int:
         result["copy_reference_bytes"] = 2 * (args.copy_mib << 20)
         del src, dst
 
+    if not args.no_configs:
+        log(f"per-configuration table ({args.config_calls} calls per verifier each)")
+        result["configs"] = config_table(torch, dv, workloads, dev, args.config_calls)
+
     if not args.no_cpu_baseline:
-        from oracle import dspark as odsp   # cpu_baseline leg only
-        try:
-            from threadpoolctl import threadpool_info
-            blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        except Exception:
-            blas_threads = 1
-        log("timing the fp64 oracle on the host (the same batch, both verifiers + adaptive head; ~10 s)")
-        # whole steps (successive Philox steps) until about 10 s of host work, at most 20
-        c0 = time.perf_counter()
-        nsteps = 0
-        while nsteps < 20 and (nsteps == 0 or time.perf_counter() - c0 < 10.0):
-            odsp.adaptive_k(wl.hidden, wl.conf_w, wl.conf_b, wl.verify_ms)
-            for m in ("tokenwise", "block"):
-                odsp.verify(wl.target, wl.draft, wl.dtype, wl.draft_tokens, wl.temperature, wl.anchor, wl.W1,
-                            wl.W2t, seed=wl.seed, step=nsteps, method=m)
-            nsteps += 1
-        cpu_s = time.perf_counter() - c0
-        result["cpu_baseline"] = {
-            "value": round(2 * B * nsteps / cpu_s, 3),
-            "unit": "blocks/s",
-            "cores": int(blas_threads),
-            "kind": "oracle",
-            "sample": f"{nsteps} full steps of the same batch (adaptive head + token-wise + block verify of {B} "
-                      f"streams, steps 0..{nsteps - 1}) in fp64 numpy, {cpu_s:.1f} s; elementwise work "
-                      f"single-threaded, BLAS products on {blas_threads} threads",
-        }
+        log("timing the fp64 oracle on the host (1 thread, then one call per worker process)")
+        result["cpu_baseline"] = cpu_baseline(B)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -94,6 +94,10 @@ def lib() -> ctypes.CDLL:
         L.dspark_cost_table_log.restype = i32
         L.dspark_random_words.argtypes = [ctypes.c_uint64, u32, u32, u32, u32, i32, i32, vp, vp]
         L.dspark_random_words.restype = i32
+        L.dspark_w2_transpose.argtypes = [vp, i32, i32, vp, vp]
+        L.dspark_w2_transpose.restype = i32
+        L.dspark_verify_launches.argtypes = [vp, vp]
+        L.dspark_verify_launches.restype = i32
         L.dspark_status_string.argtypes = [i32]
         L.dspark_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -200,6 +204,15 @@ def _verify(fname, target, draft, draft_tokens, num_drafts=None, temperature=Non
     return acc, toks, dg
 
 
+def verify_launches(target, draft, draft_tokens, num_drafts=None, temperature=None, W1=None, W2t=None,
+                    anchor=None) -> int:
+    """Launches a verify call of this problem makes on the current device (2 or 5)."""
+    p, _ = _problem(target, draft, draft_tokens, num_drafts, temperature, W1, W2t, anchor, 0, 0)
+    n = ctypes.c_int32(0)
+    _check(lib().dspark_verify_launches(ctypes.byref(p), ctypes.byref(n)))
+    return int(n.value)
+
+
 def verify_tokenwise(target, draft, draft_tokens, **kw):
     """Token-by-token verification; returns (accepted_len [B], out_tokens [B, k+1], diag or None)."""
     return _verify("dspark_verify_tokenwise", target, draft, draft_tokens, **kw)
@@ -218,6 +231,19 @@ def random_words(seed: int, b: int, purpose: int, step: int, idx0: int, n: int, 
     _check(lib().dspark_random_words(int(seed) & 0xFFFFFFFFFFFFFFFF, int(b) & 0xFFFFFFFF, int(purpose) & 0xFFFFFFFF,
                                      int(step) & 0xFFFFFFFF, int(idx0) & 0xFFFFFFFF, int(n), int(kind), _ptr(out),
                                      _stream(dev)))
+    return out
+
+
+def w2_transpose(W2, out=None):
+    """W2 [R, V] bf16 -> W2t [V, R] bf16 (the layout the verify problem takes), one launch."""
+    if W2.dim() != 2:
+        raise ValueError("W2 must be [R, V]")
+    R, V = W2.shape
+    dev = W2.device
+    _need(W2, "W2", (R, V), _BF16, dev)
+    out = torch.empty(V, R, dtype=W2.dtype, device=dev) if out is None else out
+    _need(out, "out", (V, R), _BF16, dev)
+    _check(lib().dspark_w2_transpose(_ptr(W2), R, V, _ptr(out), _stream(dev)))
     return out
 
 

@@ -69,21 +69,9 @@ bool problem_sizes_ok(const dspark_verify_problem* p) {
   return true;
 }
 
-dspark_status verify_common(const dspark_verify_problem* p, const dspark_verify_outputs* o, void* ws,
-                            size_t ws_bytes, void* stream, int method) {
-  if (!problem_sizes_ok(p) || o == nullptr) return DSPARK_ERR_INVALID_ARG;
-  if (!p->target_logits || !p->draft_logits || !p->draft_tokens || !o->accepted_len || !o->out_tokens)
-    return DSPARK_ERR_INVALID_ARG;
-  if (p->W1 != nullptr) {
-    if (p->W2t == nullptr) return DSPARK_ERR_INVALID_ARG;
-    if (!rank_ok(p->R)) return DSPARK_ERR_UNSUPPORTED;
-    if (!aligned16(p->W1) || !aligned16(p->W2t)) return DSPARK_ERR_UNSUPPORTED;
-  }
-  if (verify_lds_bytes(p->B) > kMaxPassLds) return DSPARK_ERR_UNSUPPORTED;
-  const Layout L = layout(p->B, p->k, p->V);
-  if (ws == nullptr || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
-    return DSPARK_ERR_WORKSPACE;
-
+// The kernel arguments a problem fixes (inputs, sizes, generator key); outputs and
+// workspace are filled in by the caller.
+Args problem_args(const dspark_verify_problem* p) {
   Args a;
   memset(&a, 0, sizeof(a));
   a.B = p->B; a.k = p->k; a.V = p->V; a.R = p->W1 ? p->R : 0;
@@ -102,6 +90,25 @@ dspark_status verify_common(const dspark_verify_problem* p, const dspark_verify_
   a.key0 = (uint32_t)(p->seed & 0xffffffffu);
   a.key1 = (uint32_t)(p->seed >> 32);
   a.step = p->step;
+  return a;
+}
+
+dspark_status verify_common(const dspark_verify_problem* p, const dspark_verify_outputs* o, void* ws,
+                            size_t ws_bytes, void* stream, int method) {
+  if (!problem_sizes_ok(p) || o == nullptr) return DSPARK_ERR_INVALID_ARG;
+  if (!p->target_logits || !p->draft_logits || !p->draft_tokens || !o->accepted_len || !o->out_tokens)
+    return DSPARK_ERR_INVALID_ARG;
+  if (p->W1 != nullptr) {
+    if (p->W2t == nullptr) return DSPARK_ERR_INVALID_ARG;
+    if (!rank_ok(p->R)) return DSPARK_ERR_UNSUPPORTED;
+    if (!aligned16(p->W1) || !aligned16(p->W2t)) return DSPARK_ERR_UNSUPPORTED;
+  }
+  if (verify_lds_bytes(p->B) > kMaxPassLds) return DSPARK_ERR_UNSUPPORTED;
+  const Layout L = layout(p->B, p->k, p->V);
+  if (ws == nullptr || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
+    return DSPARK_ERR_WORKSPACE;
+
+  Args a = problem_args(p);
   a.method = method;
   a.accepted_len = o->accepted_len;
   a.out_tokens = o->out_tokens;
@@ -220,6 +227,15 @@ size_t dspark_workspace_bytes(const dspark_verify_problem* p) {
   return layout(p->B, p->k, p->V).total;
 }
 
+dspark_status dspark_verify_launches(const dspark_verify_problem* p, int32_t* launches) {
+  if (!problem_sizes_ok(p) || launches == nullptr) return DSPARK_ERR_INVALID_ARG;
+  if (p->W1 != nullptr && !rank_ok(p->R)) return DSPARK_ERR_UNSUPPORTED;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DSPARK_ERR_HIP;
+  *launches = verify_fused_grid(problem_args(p)) > 0 ? 2 : 1 + 4;
+  return DSPARK_OK;
+}
+
 dspark_status dspark_verify_tokenwise(const dspark_verify_problem* p, const dspark_verify_outputs* o,
                                       void* ws, size_t ws_bytes, void* stream) {
   return verify_common(p, o, ws, ws_bytes, stream, 0);
@@ -286,6 +302,16 @@ dspark_status dspark_random_words(uint64_t seed, uint32_t b, uint32_t purpose, u
   if (launch_random_words(seed, b, purpose, step, idx0, n, kind, out, reinterpret_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return DSPARK_ERR_HIP;
+  return DSPARK_OK;
+}
+
+dspark_status dspark_w2_transpose(const uint16_t* W2, int32_t R, int32_t V, uint16_t* W2t, void* stream) {
+  if (W2 == nullptr || W2t == nullptr || R < 1 || V < 1) return DSPARK_ERR_INVALID_ARG;
+  if ((size_t)R * (size_t)V > ((size_t)1 << 40)) return DSPARK_ERR_INVALID_ARG;
+  const char *a = reinterpret_cast<const char*>(W2), *b = reinterpret_cast<const char*>(W2t);
+  const size_t bytes = (size_t)R * V * sizeof(uint16_t);
+  if (a < b + bytes && b < a + bytes) return DSPARK_ERR_INVALID_ARG;   // no in-place transpose
+  if (launch_w2_transpose(W2, R, V, W2t, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return DSPARK_ERR_HIP;
   return DSPARK_OK;
 }
 

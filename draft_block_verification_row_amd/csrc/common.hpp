@@ -332,6 +332,8 @@ hipError_t launch_markov_bias(const BiasArgs& ba, int NG, hipStream_t st);
 hipError_t launch_adaptive(const AdaptArgs& aa, hipStream_t st);
 hipError_t launch_random_words(uint64_t seed, uint32_t b, uint32_t purpose, uint32_t step, uint32_t idx0, int n,
                                int kind, uint32_t* out, hipStream_t st);
+hipError_t launch_w2_transpose(const uint16_t* w2, int R, int V, uint16_t* w2t, hipStream_t st);
+int verify_fused_grid(const Args& a);   // workgroups of the fused verify launch, 0: separate launches
 hipError_t launch_scatter(const void* in, const int32_t* ids, int rows, int K, int V, int dtype, void* out,
                           hipStream_t st);
 

@@ -1978,6 +1978,36 @@ hipError_t launch_random_words(uint64_t seed, uint32_t b, uint32_t purpose, uint
 }
 
 // ---------------------------------------------------------------------------
+// W2 [R, V] -> W2t [V, R]: 64 x 64 tiles through LDS, reads coalesced along v and
+// writes along r.  Elements are moved as 16-bit words (bf16 bits).
+// ---------------------------------------------------------------------------
+constexpr int kTrTile = 64;
+
+__global__ __launch_bounds__(kThreads) void w2_transpose_kernel(const uint16_t* __restrict__ w2, int R, int V,
+                                                                 uint16_t* __restrict__ w2t) {
+  __shared__ uint32_t tile[kTrTile][kTrTile + 1];   // +1: column reads spread over banks
+  const int v0 = blockIdx.x * kTrTile, r0 = blockIdx.y * kTrTile;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < kTrTile / kWaves; ++i) {
+    const int r = r0 + ty + kWaves * i, v = v0 + tx;
+    tile[ty + kWaves * i][tx] = (r < R && v < V) ? w2[(size_t)r * V + v] : 0u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kTrTile / kWaves; ++i) {
+    const int v = v0 + ty + kWaves * i, r = r0 + tx;
+    if (v < V && r < R) w2t[(size_t)v * R + r] = (uint16_t)tile[tx][ty + kWaves * i];
+  }
+}
+
+hipError_t launch_w2_transpose(const uint16_t* w2, int R, int V, uint16_t* w2t, hipStream_t st) {
+  const dim3 grid((V + kTrTile - 1) / kTrTile, (R + kTrTile - 1) / kTrTile);
+  hipLaunchKernelGGL(w2_transpose_kernel, grid, dim3(kThreads), 0, st, w2, R, V, w2t);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Reduced draft vocabulary [P1 §3 "The Markov fix-up": the drafter scores a reduced
 // vocabulary and scatters its logits into target-vocabulary columns]: every other
 // column is -inf, so q = 0 there and the residual keeps the target's mass.
@@ -2218,6 +2248,20 @@ template <int DT>
 static hipError_t launch_dt(const Args& a, hipStream_t st, void* const* ev) {
   return (a.vec_ok && a.V >= 16) ? launch_vec<DT, true>(a, st, ev) : launch_vec<DT, false>(a, st, ev);
 }
+
+template <int DT>
+static int fused_grid_dt(const Args& a) {
+  if (!(a.vec_ok && a.V >= 16)) return 0;
+  if (a.W1 == nullptr) return fused_grid_for<DT, 1, false, true>(a);
+  switch (a.R) {
+    case 32: return fused_grid_for<DT, 1, true, true>(a);
+    case 64: return fused_grid_for<DT, 2, true, true>(a);
+    case 128: return fused_grid_for<DT, 4, true, true>(a);
+    default: return fused_grid_for<DT, 8, true, true>(a);
+  }
+}
+
+int verify_fused_grid(const Args& a) { return a.dtype == kBF16 ? fused_grid_dt<kBF16>(a) : fused_grid_dt<kF32>(a); }
 
 hipError_t launch_verify(const Args& a, hipStream_t st, void* const* ev) {
   return a.dtype == kBF16 ? launch_dt<kBF16>(a, st, ev) : launch_dt<kF32>(a, st, ev);

@@ -60,7 +60,12 @@ typedef enum {
 
 typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
 
-/* Largest draft block the verify entry points accept. */
+/*
+ * Largest draft block the verify entry points accept.  The drafter the pages describe
+ * is trained on blocks of 5 and is run with 3 to 9 drafts [P1 "The number to remember: five", §5, §6]; 32
+ * leaves room above that while each stream's candidate rows fit one 32-bit mask and
+ * its per-slot values fit fixed arrays in LDS.  Larger k returns DSPARK_ERR_INVALID_ARG.
+ */
 #define DSPARK_MAX_K 32
 
 /*
@@ -101,13 +106,27 @@ typedef struct {
   double* diag;                   /* device [B, k+1, 5] or NULL: per slot j, (log p_j(x_j),
                                      log q_j(x_j), P_j, R_j, h_j); NaN where not computed    */
   void* const* stage_events;      /* NULL, or DSPARK_STAGES + 1 hipEvent_t the call records on
-                                     `stream` before its first launch and after each launch
+                                     `stream` before its first launch and after each stage
                                      (W1 tile packing, row statistics, scan, residual masses,
-                                     sampler): a timing hook, nothing is allocated          */
+                                     sampler); NULL entries are skipped.  When the four
+                                     verify stages run as one launch (see
+                                     dspark_verify_launches), events 2..5 all follow that
+                                     launch.  A timing hook: nothing is allocated           */
 } dspark_verify_outputs;
 
-/* Launches per verify call (see stage_events). */
+/* Stages per verify call (see stage_events). */
 #define DSPARK_STAGES 5
+
+/* Launches a verify call of this problem makes on the current device: 2 (W1 tile
+ * packing, then row statistics, scan, residual masses and sampler as phases of one
+ * launch whose workgroups are all resident at once) or 5 (one launch per stage).
+ * The choice depends on the sizes, the dtype, whether the Markov bias is on, the
+ * 16-byte alignment of the two logit pointers, and the device's occupancy; setting
+ * DSPARK_VERIFY_LAUNCH=separate in the environment forces 5.  Host only; reads no
+ * device memory.  Errors: DSPARK_ERR_INVALID_ARG (invalid sizes, NULL out),
+ * DSPARK_ERR_UNSUPPORTED (Markov rank not in {32, 64, 128, 256}), DSPARK_ERR_HIP
+ * (device query failed). */
+dspark_status dspark_verify_launches(const dspark_verify_problem* p, int32_t* launches);
 
 /* Bytes of workspace the two verify entry points need for this problem (host, pure).
  * Returns 0 if the problem's sizes are invalid. */
@@ -310,6 +329,17 @@ int32_t dspark_cost_table_log(const dspark_cost_table* table, int32_t* tokens, f
  */
 dspark_status dspark_random_words(uint64_t seed, uint32_t b, uint32_t purpose, uint32_t step, uint32_t idx0,
                                   int32_t n, int32_t kind, uint32_t* out, void* stream);
+
+/*
+ * The Markov head's second factor in the layout the verify problem takes
+ * [P2 §6 "Why the Markov Head Helps": the bias is W1[prev] times W2, W2 of shape
+ * rank x vocabulary]: W2t[v, r] = W2[r, v].  W2: device bf16 [R, V] (row r holds
+ * the rank-r weights of every id); W2t: device bf16 [V, R], distinct from W2 (no
+ * in-place transpose); any R, V >= 1.  One launch; bit-exact (a copy).  Callers
+ * whose W2 already sits as a linear layer's weight [V, R] pass it directly.
+ * Errors: DSPARK_ERR_INVALID_ARG for NULL pointers, sizes < 1 or overlapping buffers.
+ */
+dspark_status dspark_w2_transpose(const uint16_t* W2, int32_t R, int32_t V, uint16_t* W2t, void* stream);
 
 /* Static description of a status code. */
 const char* dspark_status_string(dspark_status status);
