@@ -23,7 +23,7 @@ bool rank_ok(int R) { return R == 32 || R == 64 || R == 128 || R == 256; }
 
 // Offsets of every workspace region, in the order of dspark::Workspace.
 struct Layout {
-  size_t off[18];
+  size_t off[19];
   size_t total;
 };
 
@@ -31,7 +31,7 @@ Layout layout(int B, int k, int V) {
   const size_t NG = (size_t)(V + kGroup - 1) / kGroup;
   const size_t BT = (size_t)B * (k + 1), BD = (size_t)B * k;
   const size_t tiles = (BD + kChunk - 1) / kChunk;
-  const size_t sizes[18] = {
+  const size_t sizes[19] = {
       BT * NG * sizeof(float2),           // tpart
       BD * NG * sizeof(float2),           // dpart
       BD * NG * sizeof(float),            // wgrp
@@ -49,11 +49,12 @@ Layout layout(int B, int k, int V) {
       kCounterInts * sizeof(int32_t),   // nitems: list counts and pass-1 item counters
       tiles * 8 * 64 * sizeof(uint4),   // btile (sized for the largest rank, R = 256)
       BD * NG * sizeof(Top2),           // race candidates
+      (size_t)B * NG * kGroup * sizeof(int16_t),   // race clocks
       kSyncInts * sizeof(int32_t),      // barrier words of the fused launch
   };
   Layout L;
   size_t o = 0;
-  for (int i = 0; i < 18; ++i) {
+  for (int i = 0; i < 19; ++i) {
     L.off[i] = o;
     o += align_up(sizes[i] > 0 ? sizes[i] : 1);
   }
@@ -131,7 +132,8 @@ dspark_status verify_common(const dspark_verify_problem* p, const dspark_verify_
   a.ws.nitems = reinterpret_cast<int32_t*>(base + L.off[14]);
   a.ws.btile = reinterpret_cast<uint4*>(base + L.off[15]);
   a.ws.race = reinterpret_cast<Top2*>(base + L.off[16]);
-  a.ws.sync = reinterpret_cast<int32_t*>(base + L.off[17]);
+  a.ws.clk = reinterpret_cast<uint2*>(base + L.off[17]);
+  a.ws.sync = reinterpret_cast<int32_t*>(base + L.off[18]);
   if (launch_verify(a, reinterpret_cast<hipStream_t>(stream), o->stage_events) != hipSuccess)
     return DSPARK_ERR_HIP;
   return DSPARK_OK;

@@ -39,8 +39,10 @@ __device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint3
                                                  uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
-    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    // one 32 x 32 -> 64-bit product per multiplier (v_mad_u64_u32 gives both halves)
+    const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u, p1 = (uint64_t)c2 * 0xCD9E8D57u;
+    const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+    const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
     const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
     k0 += 0x9E3779B9u; k1 += 0xBB67AE85u;
@@ -53,8 +55,10 @@ __device__ __forceinline__ uint4 philox4(uint32_t c0, uint32_t c1, uint32_t c2, 
                                          uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
-    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    // one 32 x 32 -> 64-bit product per multiplier (v_mad_u64_u32 gives both halves)
+    const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u, p1 = (uint64_t)c2 * 0xCD9E8D57u;
+    const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+    const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
     const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
     k0 += 0x9E3779B9u; k1 += 0xBB67AE85u;
@@ -90,6 +94,21 @@ __device__ __forceinline__ float clock_f32(uint32_t x) {
   const float e = -__builtin_amdgcn_logf(t) * 0.69314718055994530942f;   // v_log_f32 is log2
   const float series = d * (1.0f + d * (0.5f + d * (1.0f / 3.0f)));
   return (upper && d < 0x1.0p-8f) ? series : e;
+}
+
+// log2 E of clock word x (E = -ln U, U = ((x >> 8) + 1/2) 2^-24) in units of 2^-10,
+// rounded, as an int16 value (log2 E lies in [-25, 4.2]): absolute error below 2^-10,
+// far inside the margin the candidate pass leaves for the fp64 check.  For U > 1 - 2^-8
+// the exact d = 1 - U gives log2 E = log2 d + d / (2 ln 2) + O(d^2); otherwise
+// E = -ln U from one logarithm of U.
+__device__ __forceinline__ int clock_log2_q10(uint32_t x) {
+  const uint32_t m = x >> 8;
+  const float U = ((float)m + 0.5f) * 0x1.0p-24f;
+  const float d = ((float)((1u << 24) - 1u - m) + 0.5f) * 0x1.0p-24f;   // exact
+  const bool small = d < 0x1.0p-8f;
+  const float E = small ? d : -__builtin_amdgcn_logf(U) * 0.69314718055994530942f;
+  const float L = __builtin_amdgcn_logf(E) + (small ? d * 0.72134752044448170368f : 0.f);
+  return (int)__builtin_rintf(L * 1024.f);
 }
 
 // Accept uniform u = ((x >> 8) + 1) * 2^-24, in (0, 1], exact in fp32 and fp64.
@@ -252,6 +271,8 @@ struct Workspace {
   int32_t* nitems;    // [kCounterInts] list counts and work counters (see kQueues)
   uint4* btile;       // [ceil(B*k/16)][R/32][64] W1 tiles of pass 2's rows in MFMA lane order
   Top2* race;         // [NG][B*k]       race candidates of the pass-2 rows (by list index); the walk: [NG][B]
+  uint2* clk;         // [B][NG*64]      race clocks of sampled streams: log2 E in units of 2^-10 as
+                      //                 int16, four ids to a uint2 (ids 4i .. 4i+3 of the stream)
   int32_t* sync;      // [kSyncInts]     fused launch: go word at [0], error word at [1], workgroup g's
                       //                 arrival word at [kSyncStride (1 + g)]; cleared by pack
 };

@@ -248,6 +248,16 @@ __device__ __forceinline__ void raw_to_f32(const Raw16<DT>& r, float (&x)[16]) {
   }
 }
 
+// Element e of a raw 16-id window as fp32.
+template <int DT>
+__device__ __forceinline__ float raw_elem(const Raw16<DT>& r, int e) {
+  if (DT == kBF16) {
+    const uint32_t w = reinterpret_cast<const Raw16<kBF16>&>(r).w[e >> 1];
+    return (e & 1) ? bf16hi(w) : bf16lo(w);
+  }
+  return reinterpret_cast<const Raw16<kF32>&>(r).f[e];
+}
+
 // Columns a clamped window repeats (the first `shift` of 16) do not count.
 __device__ __forceinline__ void mask_shift(float (&x)[16], int shift) {
 #pragma unroll
@@ -1069,9 +1079,55 @@ __device__ __forceinline__ void scan_body(const Args& a, int b, ScanPhaseLds& L)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Race clocks ahead of pass 2.  Row (b, grp) holds log2 E of the sampler's clocks of
+// stream b at ids grp * 256 .. + 255 (ws.clk, int16 in units of 2^-10): one generator
+// block of four ids per lane, one row per wave.  Workgroup `slot` of `nslots` takes
+// an equal share of the B NG rows.
+// ---------------------------------------------------------------------------
+// Four rows per turn, computed side by side (four independent generator chains); a
+// row past the share is computed from a clamped row and not stored.  Greedy streams'
+// rows are computed too (unused): the loop reads nothing from memory.
+__device__ __forceinline__ void clock_rows(const Args& a, int slot, int nslots) {
+  constexpr int kU = 4;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int rows = a.B * a.NG;
+  const int per = (rows + nslots - 1) / nslots;
+  const int r0 = slot * per, r1 = min(r0 + per, rows);
+  for (int rb = r0 + kU * w; rb < r1; rb += kU * kWaves) {
+    int b = rb / a.NG, grp = rb - b * a.NG;   // row rb; the next ones step from it
+    uint2 out[kU];
+    int dst[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (u > 0) {
+        ++grp;
+        while (grp >= a.NG) {   // at most once unless NG < 4
+          grp -= a.NG;
+          ++b;
+        }
+      }
+      const uint32_t bb = (uint32_t)min(b, a.B - 1);
+      dst[u] = rb + u < r1 ? (int)bb * a.NG * 64 + grp * 64 + l : -1;
+      const uint4 x = philox4(bb, (uint32_t)(grp * 64 + l), kPurposeSample, a.step, a.key0, a.key1);
+      const uint32_t q0 = (uint32_t)clock_log2_q10(x.x) & 0xffffu, q1 = (uint32_t)clock_log2_q10(x.y) & 0xffffu;
+      const uint32_t q2 = (uint32_t)clock_log2_q10(x.z) & 0xffffu, q3 = (uint32_t)clock_log2_q10(x.w) & 0xffffu;
+      out[u] = make_uint2(q0 | (q1 << 16), q2 | (q3 << 16));
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (dst[u] >= 0) st_c(&a.ws.clk[(size_t)dst[u]], out[u]);
+  }
+}
+
+// Workgroups 0..B-1 scan their stream; the rest compute the race clocks.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
   __shared__ ScanPhaseLds L;
+  if ((int)blockIdx.x >= a.B) {
+    clock_rows(a, (int)blockIdx.x - a.B, (int)gridDim.x - a.B);
+    return;
+  }
   scan_body<DT>(a, blockIdx.x, L);
 }
 
@@ -1125,29 +1181,28 @@ __device__ __forceinline__ Top2 top2_4lanes(Top2 t) {
   return swap_merge32(swap_merge16(t));
 }
 
-// A lane's best two race candidates while its ids arrive in increasing order, as
-// ratios w / E (0: none): a later id replaces an earlier one only with a strictly
-// larger ratio, so the smaller id wins ties without comparing ids.
+// A lane's best race candidate while its ids arrive in increasing order, as a ratio
+// w / E (0: none): a later id replaces an earlier one only with a strictly larger
+// ratio, so the smaller id wins ties without comparing ids.  Lanes keep one candidate
+// each and the best two of a row's lanes go on (top2_4lanes, then across waves): two
+// ids of one lane trade places only when their ratios agree to the fp32 rounding,
+// which the fp64 check of every candidate near the best does not need.
 struct LaneTop {
-  float s1, s2;
-  int32_t v1, v2;
+  float s;
+  int32_t v;
 };
-__device__ __forceinline__ LaneTop lane_top_empty() { return LaneTop{0.f, 0.f, INT_MAX, INT_MAX}; }
+__device__ __forceinline__ LaneTop lane_top_empty() { return LaneTop{0.f, INT_MAX}; }
 __device__ __forceinline__ void lane_top_add(LaneTop& t, float r, int v) {
-  const bool b1 = r > t.s1, b2 = r > t.s2;
-  t.s2 = b1 ? t.s1 : (b2 ? r : t.s2);
-  t.v2 = b1 ? t.v1 : (b2 ? v : t.v2);
-  t.s1 = b1 ? r : t.s1;
-  t.v1 = b1 ? v : t.v1;
+  const bool b = r > t.s;
+  t.s = b ? r : t.s;
+  t.v = b ? v : t.v;
 }
-// As log2 scores on the row's common scale: log2(w / E) + off, where the lane's
+// As a log2 score on the row's common scale: log2(w / E) + off, where the lane's
 // weights were w_v = 2^(log2 w_v - off).
 __device__ __forceinline__ Top2 lane_top_log2(const LaneTop& t, float off) {
-  Top2 r;
-  r.s1 = t.s1 > 0.f ? __builtin_amdgcn_logf(t.s1) + off : -INFINITY;
-  r.v1 = t.s1 > 0.f ? t.v1 : INT_MAX;
-  r.s2 = t.s2 > 0.f ? __builtin_amdgcn_logf(t.s2) + off : -INFINITY;
-  r.v2 = t.s2 > 0.f ? t.v2 : INT_MAX;
+  Top2 r = top2_empty();
+  r.s1 = t.s > 0.f ? __builtin_amdgcn_logf(t.s) + off : -INFINITY;
+  r.v1 = t.s > 0.f ? t.v : INT_MAX;
   return r;
 }
 
@@ -1189,6 +1244,39 @@ __device__ __forceinline__ float max16(const float (&v)[16]) {
   return m == -INFINITY ? 0.f : m;   // no weight in the lane: every ratio is 0
 }
 
+// A lane's best race score over its 16 ids c0 .. c0 + 15 in increasing order (a later
+// id replaces an earlier one only with a strictly larger score, so the smaller id wins
+// ties), from 16 clocks L (int16, units of 2^-10, two to a word).  Ratios (EXP =
+// false): y are weights w >= 0 and the score is log2 w - log2 E; exponents (EXP =
+// true): y are logits (-inf: none) with weights 2^(y c), and the score is y c - log2 E.
+// Either way the scores share the row's scale across lanes, waves and groups.
+template <bool EXP>
+__device__ __forceinline__ Top2 race16_clk(const float (&y)[16], const uint2 (&L)[4], float c, int c0) {
+  float best = -INFINITY;
+  int bv = INT_MAX;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const uint32_t word = (e & 2) ? L[e >> 2].y : L[e >> 2].x;
+    const int q = (e & 1) ? ((int32_t)word >> 16) : ((int32_t)(word << 16) >> 16);
+    const float lq = (float)q * 0x1.0p-10f;
+    const float sc = EXP ? fmaf(y[e], c, -lq) : (y[e] > 0.f ? __builtin_amdgcn_logf(y[e]) - lq : -INFINITY);
+    const bool better = sc > best;
+    best = better ? sc : best;
+    bv = better ? c0 + e : bv;
+  }
+  Top2 r = top2_empty();
+  r.s1 = best;
+  r.v1 = best > -INFINITY ? bv : INT_MAX;
+  return r;
+}
+
+// This lane's 16 clocks of stream b at ids c0 .. c0 + 15 (c0 a multiple of 4).
+__device__ __forceinline__ void load_clocks(const Args& a, uint32_t b, int c0, uint2 (&L)[4]) {
+  const uint2* p = a.ws.clk + (size_t)b * a.NG * 64 + (c0 >> 2);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) L[i] = ld_c(&p[i]);
+}
+
 // ---------------------------------------------------------------------------
 // pass2: per listed row and group, the residual mass sum max(0, P_i p_i - q_i) and
 // the race candidates of w = max(0, P_i p_i - q_i); then, for the bonus rows the
@@ -1197,11 +1285,33 @@ __device__ __forceinline__ float max16(const float (&v)[16]) {
 // and its packed W1 tile.  Waves reduce 64 ids each; the 4 wave results of a row
 // meet in LDS and are flushed every 256 rows.
 // ---------------------------------------------------------------------------
+constexpr int kItemWords = (int)(sizeof(Item) / sizeof(int32_t));
+static_assert(kItemWords == 12, "Item is 12 words: dr, tr, prev, b, Mt, Md, chi, clo, kph, kpl, kqh, kql");
+constexpr int kStageWords = kChunk * kItemWords;   // one chunk's items: 192 words, 3 per lane
 struct Pass2Lds {
   float part[kFlush * kChunk][kWaves];
   Top2 rpart[kFlush * kChunk][kWaves];
-  float4 park[kThreads][4];   // a lane's 16 race weights
+  int32_t items[kWaves][4][kStageWords];    // per wave, the items of chunks c .. c + 2 (ring of 4)
+  uint4 btile[2][8 * 64];                   // the W1 tiles of chunks c and c + 1 (R <= 256)
 };
+
+// x + bias with the B operand read from LDS one k-step at a time (unit kk * 64 + l).
+template <int KS>
+__device__ __forceinline__ void markov_mma_lds(const bf16x8 (&A)[4][KS], const uint4* bt, int l, float (&x)[16]) {
+  f32x4 acc[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc[s] = f32x4{x[4 * s], x[4 * s + 1], x[4 * s + 2], x[4 * s + 3]};
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    const bf16x8 b = __builtin_bit_cast(bf16x8, bt[kk * 64 + l]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[s][kk], b, acc[s], 0, 0, 0);
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[4 * s + i] = acc[s][i];
+}
 
 // Pass 2 for vocabulary group g.  slab_loaded: A already holds this workgroup's W2
 // slab (the fused launch's pass 1 left it there).
@@ -1209,7 +1319,6 @@ template <int DT, int KS, bool MARKOV, bool VEC>
 __device__ __forceinline__ void pass2_body(const Args& a, int g, Pass2Lds& L, bf16x8 (&A)[4][KS], bool slab_loaded) {
   auto& part = L.part;
   auto& rpart = L.rpart;
-  auto& park = L.park;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, q = l >> 4;
   const int cb = (g * kWaves + w) * kWaveCols;
   const int cw = cb + 16 * q;
@@ -1221,56 +1330,111 @@ __device__ __forceinline__ void pass2_body(const Args& a, int g, Pass2Lds& L, bf
 
   // the W2 slab does not depend on the list: its loads go out before the count is read
   if (MARKOV && !slab_loaded) load_w2_slab<KS, VEC>(a, cb, n, q, A);
-  // The first chunks' rows do not wait for the list count either: row indices are
-  // read speculatively (entries past the count are stale, clamped to valid rows and
-  // never written back), so the first logits loads follow one dependent load.
+  // Each wave stages the item records of its chunks in LDS, two chunks ahead: lane l
+  // holds words l, l + 64, l + 128 of a later chunk's 16 records across a chunk, and the
+  // rows and constants are read from LDS when they are needed (no registers held
+  // through the products, no load waited on in the loop).  Records past the count are
+  // stale: indices are clamped to valid rows and nothing computed from them is written
+  // back.
   const int NT = a.B * (a.k + 1);
-  auto item_at = [&](int c) { return min(c * kChunk + n, ND - 1); };
+  int32_t* stage = &L.items[w][0][0];
+  int32_t words[3];
+  const int32_t* item_words = reinterpret_cast<const int32_t*>(a.ws.items);
+  auto load_words = [&](int c) {   // word c * 192 + e of the list (clamped into it)
+#pragma unroll
+    for (int u = 0; u < 3; ++u) words[u] = ld_c(item_words + min(c * kStageWords + l + 64 * u, ND * kItemWords - 1));
+  };
+  auto store_words = [&](int c) {
+#pragma unroll
+    for (int u = 0; u < 3; ++u) stage[(c & 3) * kStageWords + l + 64 * u] = words[u];
+    __builtin_amdgcn_wave_barrier();
+  };
+  auto record = [&](int c) { return stage + (c & 3) * kStageWords + n * kItemWords; };
   auto rows_of = [&](int c) {   // (dr, tr) of this lane's row in chunk c, clamped
-    int2 h = ld_c(reinterpret_cast<const int2*>(&a.ws.items[item_at(c)].dr));
-    h.x = min(max(h.x, 0), ND - 1);
-    h.y = min(max(h.y, 0), NT - 1);
-    return h;
+    const int32_t* r = record(c);
+    return make_int2(min(max(r[0], 0), ND - 1), min(max(r[1], 0), NT - 1));
   };
   auto fetch = [&](int2 h, Raw16<DT>& t, Raw16<DT>& d) {
     raw_load<DT, VEC>(t, reinterpret_cast<const char*>(a.target) + (size_t)h.y * rb, c0, a.V);
     raw_load<DT, VEC>(d, reinterpret_cast<const char*>(a.draft) + (size_t)h.x * rb, c0, a.V);
   };
-  // pipeline: row indices two chunks ahead, logits one chunk ahead
-  Raw16<DT> tb, db;
-  fetch(rows_of(0), tb, db);
-  int2 hn = rows_of(1);
+  // pipeline: records three chunks ahead (registers), two ahead in LDS; the logits of
+  // chunk c in ring buffer c & 1, loaded two chunks ahead (the ring is indexed at
+  // compile time: the loop runs two chunks per turn).  The prologue issues its loads in
+  // the order the loop's first waits need them (the list counts first, the logits
+  // last), so that those waits never have to drain the logits.
   const int NI = ld_c(&a.ws.nitems[0]), NB = ld_c(&a.ws.nitems[1]);
+  // The W1 tile of a chunk (the B operand, the same for the 4 waves) goes through LDS,
+  // double-buffered: each thread holds its share of the tile two chunks ahead and
+  // stores it one chunk ahead; the workgroup barrier at the top of each chunk publishes
+  // it (and frees the buffer the previous chunk read).  Tiles past the list are stale
+  // (the region holds one per 16 draft rows) and unused.
+  constexpr int kBtUnits = KS * 64, kBtPer = (kBtUnits + kThreads - 1) / kThreads;
+  const int ntiles = (ND + kChunk - 1) / kChunk;
+  uint4 bt[kBtPer];
+  // (a share is whole when the tile is a multiple of the workgroup: no branch then)
+  auto bt_load = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < kBtPer; ++i) {
+      const int u = tid + kThreads * i;
+      if (kBtUnits % kThreads == 0 || u < kBtUnits)
+        bt[i] = ld_c(&a.ws.btile[(size_t)min(c, ntiles - 1) * kBtUnits + u]);
+    }
+  };
+  auto bt_store = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < kBtPer; ++i) {
+      const int u = tid + kThreads * i;
+      if (kBtUnits % kThreads == 0 || u < kBtUnits) L.btile[c & 1][u] = bt[i];
+    }
+  };
+  load_words(0);
+  if (MARKOV) bt_load(0);
+  store_words(0);
+  load_words(1);
+  if (MARKOV) {
+    bt_store(0);
+    bt_load(1);
+  }
+  store_words(1);
+  load_words(2);
+  Raw16<DT> tr0, dr0, tr1, dr1;
+  fetch(rows_of(0), tr0, dr0);
+  fetch(rows_of(1), tr1, dr1);
   const int nch = (NI + kChunk - 1) / kChunk;
-  bf16x8 Bc[KS];
-  if (MARKOV && NI > 0) load_btile<KS>(a, 0, l, Bc);
-  for (int c = 0; c < nch; ++c) {
-    const int2 hnn = rows_of(c + 2);
-    const Item& itc = a.ws.items[item_at(c)];
-    const float4* kc = reinterpret_cast<const float4*>(&itc.Mt);
-    const float4 k0 = ld_c(&kc[0]), k1 = ld_c(&kc[1]);   // (Mt, Md, chi, clo), (kph, kpl, kqh, kql)
-    const uint32_t sb = (uint32_t)min(max(ld_c(&itc.b), 0), a.B - 1);
-    float bias[16];   // the bias alone (not folded into the draft logits: the residual
-                      // compares P p with q and keeps their rounding apart)
+  auto step = [&](int c, Raw16<DT>& tb, Raw16<DT>& db) {
+    store_words(c + 2);   // loaded a chunk ago: the registers are free for the products
+    if (MARKOV) {
+      __syncthreads();
+      bt_store(c + 1);
+    }
+    float bias[16];       // the bias alone (not folded into the draft logits: the residual
+                          // compares P p with q and keeps their rounding apart)
     if (MARKOV) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) bias[e] = 0.f;
-      markov_mma<KS>(A, Bc, bias);
-      load_btile<KS>(a, min(c + 1, nch - 1), l, Bc);
+      markov_mma_lds<KS>(A, L.btile[c & 1], l, bias);
+      __builtin_amdgcn_sched_barrier(0);
+      bt_load(c + 2);
     }
-    float xt[16], xd[16];
-    raw_to_f32<DT>(tb, xt);
-    raw_to_f32<DT>(db, xd);
-    fetch(hn, tb, db);
-    hn = hnn;
-    if (rag) mask_shift(xt, shift);
-    // residual weights (normalised) and their sum; then the race over them
+    load_words(c + 3);
+    const int32_t* rc = record(c);
+    const float4 k0 = make_float4(__int_as_float(rc[4]), __int_as_float(rc[5]), __int_as_float(rc[6]),
+                                  __int_as_float(rc[7]));   // (Mt, Md, chi, clo)
+    const float4 k1 = make_float4(__int_as_float(rc[8]), __int_as_float(rc[9]), __int_as_float(rc[10]),
+                                  __int_as_float(rc[11]));  // (kph, kpl, kqh, kql)
+    const uint32_t sb = (uint32_t)min(max(rc[3], 0), a.B - 1);
+    uint2 ck[4];   // the row's clocks at this lane's ids, used by the race at the end
+    load_clocks(a, sb, c0, ck);
+    // residual weights (normalised) and their sum, straight from the raw logits (the
+    // buffers are refilled after); then the race over them
     float s = 0.f;
     float wr[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float tp = xt[e] - k0.x;
-      const float d = MARKOV ? xd[e] + bias[e] : xd[e];
+      const float xte = (rag && e < shift) ? -INFINITY : raw_elem<DT>(tb, e);
+      const float tp = xte - k0.x;
+      const float d = MARKOV ? raw_elem<DT>(db, e) + bias[e] : raw_elem<DT>(db, e);
       const float tq = d - k0.y;
       const float ep = fmaf(tp, k0.z, k1.x) + fmaf(tp, k0.w, k1.y);
       const float eq = fmaf(tq, k0.z, k1.z) + fmaf(tq, k0.w, k1.w);
@@ -1278,9 +1442,9 @@ __device__ __forceinline__ void pass2_body(const Args& a, int g, Pass2Lds& L, bf
       wr[e] = ((VEC || c0 + e < a.V) && wv > 0.f) ? wv : 0.f;
       s += wr[e];
     }
+    fetch(rows_of(c + 2), tb, db);
     s = sum4lanes(s);
-    park16(park[tid], wr);
-    const Top2 rt = top2_4lanes(race16<false>(park[tid], 0.f, 1.f, c0, sb, kPurposeSample, a));
+    const Top2 rt = top2_4lanes(race16_clk<false>(wr, ck, 0.f, c0));
     if (q == 0) {
       part[(c % kFlush) * kChunk + n][w] = s;
       rpart[(c % kFlush) * kChunk + n][w] = rt;
@@ -1298,6 +1462,10 @@ __device__ __forceinline__ void pass2_body(const Args& a, int g, Pass2Lds& L, bf
       }
       __syncthreads();
     }
+  };
+  for (int c = 0; c < nch; c += 2) {   // uniform: every wave runs the same chunks
+    step(c, tr0, dr0);
+    if (c + 1 < nch) step(c + 1, tr1, dr1);
   }
   // bonus rows the verifiers stop at (listed from the back of the list): race
   // candidates of p_gamma, log2 w = x log2(e) / T (unnormalised: every group of the
@@ -1310,13 +1478,14 @@ __device__ __forceinline__ void pass2_body(const Args& a, int g, Pass2Lds& L, bf
     const float chi = it.chi, clo = it.clo;   // log2(e) / T as hi + lo
     Raw16<DT> t;
     raw_load<DT, VEC>(t, reinterpret_cast<const char*>(a.target) + (size_t)tr * rb, c0, a.V);
+    uint2 ck[4];
+    load_clocks(a, sb, c0, ck);
     float x[16];
     raw_to_f32<DT>(t, x);
     if (rag) mask_shift(x, shift);
 #pragma unroll
     for (int e = 0; e < 16; ++e) x[e] = (VEC || c0 + e < a.V) ? x[e] : -INFINITY;
-    park16(park[tid], x);
-    const Top2 rt = top2_4lanes(race16<true>(park[tid], max16(x), chi + clo, c0, sb, kPurposeSample, a));
+    const Top2 rt = top2_4lanes(race16_clk<true>(x, ck, chi + clo, c0));
     if (q == 0) rpart[n][w] = rt;
     __syncthreads();
     if (tid < kChunk && c * kChunk + tid < NB) {
@@ -1644,7 +1813,8 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
 // launch of G >= NG workgroups, all resident at once (the host checks occupancy):
 //   phase 1  pass 1 for group g (g < NG); the workgroup keeps its W2 slab
 //   phase 2  the scan of streams g, g + G, ... (workgroups g < B, which load their
-//            slab again afterwards: the scan needs the registers)
+//            slab again afterwards: the scan needs the registers); the race clocks
+//            of every sampled stream, by the workgroups without a stream
 //   phase 3  pass 2 for group g, on the slab still in registers (W2 is read once
 //            but for the scanning workgroups' slabs)
 //   phase 4  finalize of streams g, g + G, ...
@@ -1703,6 +1873,10 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(Args a) {
   bf16x8 A[4][KS];
   if (g < a.NG) pass1_body<DT, KS, MARKOV, VEC>(a, g, a.NG, *reinterpret_cast<Pass1Lds<KS, MARKOV>*>(lds), table, A);
   grid_barrier(a, 1);
+  // workgroups without a stream to scan compute the race clocks meanwhile; when every
+  // workgroup scans, each takes its share of the clocks after its streams
+  const int nscan = a.B < G ? a.B : G;
+  const bool spare = G > nscan;
   if (g < a.B) {
     // a workgroup with streams to scan gives its slab's registers to the scan and loads
     // the slab again afterwards (at B = 64 of 505 groups: 8 MB of W2); the others keep
@@ -1711,6 +1885,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(Args a) {
       scan_body<DT>(a, b, *reinterpret_cast<ScanPhaseLds*>(lds));
       __syncthreads();
     }
+    if (!spare) clock_rows(a, g, G);
     grid_barrier(a, 2);
     if (MARKOV) {   // A is defined on every path here, so the old slab is dead during the scan
       if (g < a.NG) {
@@ -1724,6 +1899,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(Args a) {
       }
     }
   } else {
+    clock_rows(a, g - nscan, G - nscan);
     grid_barrier(a, 2);
   }
   if (g < a.NG) pass2_body<DT, KS, MARKOV, VEC>(a, g, *reinterpret_cast<Pass2Lds*>(lds), A, true);
@@ -2224,7 +2400,7 @@ static hipError_t launch_passes(const Args& a0, hipStream_t st, void* const* ev)
   }
   hipLaunchKernelGGL((pass1_kernel<DT, KS, MARKOV, VEC>), dim3(a.NG), dim3(kThreads), stream_table_bytes(a.B), st, a);
   mark(2);
-  hipLaunchKernelGGL((scan_kernel<DT>), dim3(a.B), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((scan_kernel<DT>), dim3(a.B + a.NG), dim3(kThreads), 0, st, a);
   mark(3);
   hipLaunchKernelGGL((pass2_kernel<DT, KS, MARKOV, VEC>), dim3(a.NG), dim3(kThreads), 0, st, a);
   mark(4);
