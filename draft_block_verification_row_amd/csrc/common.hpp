@@ -274,13 +274,20 @@ struct Workspace {
   uint2* clk;         // [B][NG*64]      race clocks of sampled streams: log2 E in units of 2^-10 as
                       //                 int16, four ids to a uint2 (ids 4i .. 4i+3 of the stream)
   int32_t* sync;      // [kSyncInts]     fused launch: go word at [0], error word at [1], workgroup g's
-                      //                 arrival word at [kSyncStride (1 + g)]; cleared by pack
+                      //                 arrival word at [kSyncStride (1 + g)], go-word copies from
+                      //                 [kGoBase]; cleared by pack
 };
 
-// The fused verify launch's barrier words (one 64-byte line each).
+// The fused verify launch's barrier words: the go word at [0] and the error word at
+// [1], workgroup g's arrival word at [kSyncStride (1 + g)] (one 64-byte line each),
+// then kGoCopies copies of the go word, one 128-byte line apart (workgroup g waits on
+// copy g % kGoCopies, so that hundreds of waiting workgroups do not all poll one line).
 constexpr int kSyncStride = 16;
 constexpr int kMaxFusedGrid = 2048;
-constexpr int kSyncInts = kSyncStride * (1 + kMaxFusedGrid);
+constexpr int kGoCopies = 16;
+constexpr int kGoStride = 32;
+constexpr int kGoBase = kSyncStride * (1 + kMaxFusedGrid);
+constexpr int kSyncInts = kGoBase + kGoCopies * kGoStride;
 
 struct Args {
   int B, k, V, R, NG, dtype;
@@ -341,10 +348,10 @@ struct AdaptArgs {
   float ms[kMaxMs];
 };
 
-// Dynamic LDS of pass 1 (the per-stream table, 8 bytes a stream); calls needing
-// more than kMaxPassLds (B > 4096) are rejected as unsupported.
+// Dynamic LDS of pass 1 (the per-stream table, 12 bytes a stream and 16 more); calls
+// needing more than kMaxPassLds (B > 4096) are rejected as unsupported.
 size_t verify_lds_bytes(int B);
-constexpr size_t kMaxPassLds = 32 * 1024;
+constexpr size_t kMaxPassLds = 12 * 4096 + 16;
 
 // launchers (kernels.hip)
 hipError_t launch_verify(const Args& a, hipStream_t st, void* const* events);

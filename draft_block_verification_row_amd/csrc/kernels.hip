@@ -306,6 +306,7 @@ __global__ __launch_bounds__(64) void pack_kernel(Args a) {
   if (c == 0 && l < kQueues) st_c(&a.ws.nitems[kQueueStride * (1 + l)], 0);
   if (a.fused_grid > 0) {   // the fused launch's go and error words, and every arrival word
     if (c == 0 && l == 0) st_c(&a.ws.sync[1], 0);
+    if (c == 0 && l < kGoCopies) st_c(&a.ws.sync[kGoBase + kGoStride * l], 0);
     for (int i = c * 64 + l; i <= a.fused_grid; i += gridDim.x * 64) st_c(&a.ws.sync[kSyncStride * i], 0);
   }
   if (a.W1 == nullptr) return;
@@ -356,7 +357,7 @@ __device__ __forceinline__ void markov_mma(const bf16x8 (&A)[4][KS], const bf16x
 __host__ __device__ __forceinline__ size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
 __host__ __device__ __forceinline__ size_t stream_table_bytes(int B) {
-  return align16((size_t)B * sizeof(float)) + align16((size_t)B * sizeof(int)) + 16;
+  return 2 * align16((size_t)B * sizeof(float)) + align16((size_t)B * sizeof(int)) + 16;
 }
 
 // Stand-in temperature constant of a greedy stream (T = 0) in the stream table; no
@@ -364,11 +365,22 @@ __host__ __device__ __forceinline__ size_t stream_table_bytes(int B) {
 constexpr float kGreedyTcValue = 1e-30f;
 constexpr float kGreedyTc = 1e-20f;
 
+// tc[b] = log2(e) / T_b (fp32; a stand-in for a greedy stream), gam[b] = gamma_b, a
+// flag word (any greedy stream), and T[b] itself (the fused launch's scan and
+// finalize read T_b and gamma_b from here instead of from global memory).
 struct StreamTable {
   const float* tc;
   const int* gam;
   bool any_greedy;
+  const float* T;
 };
+__device__ __forceinline__ const float* stream_table_T(const Args& a, const char* smem) {
+  return reinterpret_cast<const float*>(smem + align16((size_t)a.B * sizeof(float)) +
+                                        align16((size_t)a.B * sizeof(int)) + 16);
+}
+__device__ __forceinline__ const int* stream_table_gam(const Args& a, const char* smem) {
+  return reinterpret_cast<const int*>(smem + align16((size_t)a.B * sizeof(float)));
+}
 
 // T0, gam0: stream threadIdx.x's temperature and draft count when the caller has
 // loaded them already (pass 1 issues those loads ahead of its W2 slab); NaN = not loaded.
@@ -378,17 +390,19 @@ __device__ __forceinline__ StreamTable build_stream_table(const Args& a, char* s
   int* flag = reinterpret_cast<int*>(smem + align16((size_t)a.B * sizeof(float)) + align16((size_t)a.B * sizeof(int)));
   if (threadIdx.x == 0) flag[0] = 0;
   __syncthreads();
+  float* tt = const_cast<float*>(stream_table_T(a, smem));
   auto put = [&](int b, float T, int gm) {
     // T = 0 (greedy) only needs the row maxima: any finite positive c keeps the sums finite
     tc[b] = T > 0.f ? (float)(kLog2e / (double)T) : kGreedyTcValue;
     gam[b] = gm;
+    tt[b] = T;
     if (!(T > 0.f)) flag[0] = 1;
   };
   const bool pre = !isnan(T0);
   if (pre && (int)threadIdx.x < a.B) put(threadIdx.x, T0, gam0);
   for (int b = threadIdx.x + (pre ? kThreads : 0); b < a.B; b += kThreads) put(b, stream_temp(a, b), stream_gamma(a, b));
   __syncthreads();
-  return StreamTable{tc, gam, flag[0] != 0};
+  return StreamTable{tc, gam, flag[0] != 0, tt};
 }
 
 // ---------------------------------------------------------------------------
@@ -864,7 +878,7 @@ __device__ __forceinline__ void greedy_scan(const Args& a, int b, int gamma, int
 
 // LDS of the scan of one stream.
 struct ScanPhaseLds {
-  ScanLds sh;
+  ScanLds sh[2];   // the group passes in turn (the first two loaded at the start)
   float s_M[2 * kMaxK + 1];
   double s_l2s[2 * kMaxK + 1];
   double s_lt[kMaxK], s_ld[kMaxK], s_u[kMaxK], s_lr[kMaxK], s_lp[kMaxK + 1];
@@ -876,8 +890,10 @@ struct ScanPhaseLds {
 
 // The scan of stream b.  Every thread of the workgroup calls it.
 template <int DT>
-__device__ __forceinline__ void scan_body(const Args& a, int b, ScanPhaseLds& L) {
-  ScanLds& sh = L.sh;
+// tT, tgam: the stream table's T_b and gamma_b in LDS (the fused launch), or null (read
+// from the inputs).
+__device__ __forceinline__ void scan_body(const Args& a, int b, ScanPhaseLds& L, const float* tT = nullptr,
+                                          const int* tgam = nullptr) {
   float* s_M = L.s_M;
   double* s_l2s = L.s_l2s;
   double *s_lt = L.s_lt, *s_ld = L.s_ld, *s_u = L.s_u, *s_lr = L.s_lr, *s_lp = L.s_lp;
@@ -885,8 +901,18 @@ __device__ __forceinline__ void scan_body(const Args& a, int b, ScanPhaseLds& L)
   int& s_base = L.s_base;
   uint32_t& s_mask = L.s_mask;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int gamma = stream_gamma(a, b);
-  const float Tf = stream_temp(a, b);
+  // The row statistics of the first two group passes go out first: they depend on b
+  // alone (rows 0 .. min(6, k) - 1, a bound on gamma_b: the rows at and past gamma_b
+  // are loaded and not used; a second pass past the last group re-reads group NG - 1),
+  // and the stream's draft count and temperature arrive meanwhile.
+  const int kr = min(kScanRows, a.k);
+  const int ngp = min(a.NG, kScanGroups);
+  const int ng2 = min(a.NG - kScanGroups, kScanGroups);   // groups of the second pass (<= 0: none)
+  StageRegs sreg, sreg2;
+  stage_load(sreg, a, b, 0, kr, kr, 0, ngp, tid);
+  stage_load(sreg2, a, b, 0, kr, kr, min(kScanGroups, a.NG - 1), max(ng2, 1), tid);
+  const int gamma = tgam != nullptr ? tgam[b] : stream_gamma(a, b);
+  const float Tf = tT != nullptr ? tT[b] : stream_temp(a, b);
   if (Tf == 0.f) {   // the whole workgroup takes the greedy branch
     greedy_scan<DT>(a, b, gamma, L.s_am);
     return;
@@ -896,11 +922,10 @@ __device__ __forceinline__ void scan_body(const Args& a, int b, ScanPhaseLds& L)
   const int k1 = a.k + 1;
   const int NT = a.B * k1, ND = a.B * a.k;
   const size_t esz = DT == kBF16 ? 2 : 4;
-
-  // the first row-statistics loads, then the logits at the drafts
-  const int ngp = min(a.NG, kScanGroups);
-  StageRegs sreg;
-  stage_load(sreg, a, b, 0, min(kScanRows, gamma), min(kScanRows, gamma), 0, ngp, tid);
+  // the first two passes into LDS now (issued before the temperature, so arrived):
+  // their registers are free for the gathers
+  stage_store(sreg, L.sh[0], tid);
+  stage_store(sreg2, L.sh[1], tid);
 
   if (tid < gamma) s_u[tid] = accept_uniform(a.key0, a.key1, (uint32_t)b, (uint32_t)tid, a.step);
 
@@ -953,9 +978,15 @@ __device__ __forceinline__ void scan_body(const Args& a, int b, ScanPhaseLds& L)
     double S[3] = {0.0, 0.0, 0.0};
     for (int g0 = 0; g0 < a.NG; g0 += kScanGroups) {
       const int ng = min(kScanGroups, a.NG - g0);
-      if (r0 > 0 || g0 > 0) stage_load(sreg, a, b, r0, nt, nd, g0, ng, tid);
-      __syncthreads();   // the previous pass's readers are done with the LDS rows
-      stage_store(sreg, sh, tid);
+      // rows 0..5 of groups 0..511 were loaded at the start (buffers 0 and 1); any other
+      // pass is loaded now into buffer 0, once its readers are done with it
+      const bool pre = r0 == 0 && g0 <= kScanGroups;
+      ScanLds& sh = L.sh[pre && g0 == kScanGroups ? 1 : 0];
+      if (!pre) {
+        stage_load(sreg, a, b, r0, nt, nd, g0, ng, tid);
+        __syncthreads();
+        stage_store(sreg, sh, tid);
+      }
       __syncthreads();
       stage_reduce(sh, w, l, ng, c, M, S);
     }
@@ -1060,22 +1091,6 @@ __device__ __forceinline__ void scan_body(const Args& a, int b, ScanPhaseLds& L)
     it.kqh = (float)kq;
     it.kql = (float)(kq - (double)it.kqh);
     st_c(&a.ws.items[s_base + __popc(mask & ((1u << i) - 1u))], it);
-  }
-  // W1 tiles of the listed rows for pass 2 (pass 1, the only other reader, is done)
-  if (a.W1 != nullptr && mask != 0u) {
-    const int ks = a.R / 32;
-    int it = s_base;
-    for (int i = 0; i < gamma; ++i) {
-      if (!((mask >> i) & 1u)) continue;
-      if (tid < 4 * ks) {
-        const int kk = tid >> 2, q = tid & 3;
-        const int prev = draft_prev(a, b, i);
-        st_c(&a.ws.btile[((size_t)(it >> 4) * ks + kk) * 64 + (it & 15) + 16 * q],
-             prev >= 0 ? *reinterpret_cast<const uint4*>(a.W1 + (size_t)prev * a.R + kk * 32 + 8 * q)
-                       : make_uint4(0, 0, 0, 0));
-      }
-      ++it;
-    }
   }
 }
 
@@ -1270,6 +1285,28 @@ __device__ __forceinline__ Top2 race16_clk(const float (&y)[16], const uint2 (&L
   return r;
 }
 
+// The race of pass 2's rows, listed or bonus (per lane): a listed row's y are residual
+// weights w >= 0 (score log2 w - log2 E), a bonus row's y are y = x c, the logits
+// scaled to log2 units (-inf: none; score y - log2 E).
+__device__ __forceinline__ Top2 race16_row(const float (&y)[16], const uint2 (&L)[4], bool bonus, int c0) {
+  float best = -INFINITY;
+  int bv = INT_MAX;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const uint32_t word = (e & 2) ? L[e >> 2].y : L[e >> 2].x;
+    const int q = (e & 1) ? ((int32_t)word >> 16) : ((int32_t)(word << 16) >> 16);
+    const float lq = (float)q * 0x1.0p-10f;
+    const float sc = bonus ? y[e] - lq : (y[e] > 0.f ? __builtin_amdgcn_logf(y[e]) - lq : -INFINITY);
+    const bool better = sc > best;
+    best = better ? sc : best;
+    bv = better ? c0 + e : bv;
+  }
+  Top2 r = top2_empty();
+  r.s1 = best;
+  r.v1 = best > -INFINITY ? bv : INT_MAX;
+  return r;
+}
+
 // This lane's 16 clocks of stream b at ids c0 .. c0 + 15 (c0 a multiple of 4).
 __device__ __forceinline__ void load_clocks(const Args& a, uint32_t b, int c0, uint2 (&L)[4]) {
   const uint2* p = a.ws.clk + (size_t)b * a.NG * 64 + (c0 >> 2);
@@ -1330,19 +1367,27 @@ __device__ __forceinline__ void pass2_body(const Args& a, int g, Pass2Lds& L, bf
 
   // the W2 slab does not depend on the list: its loads go out before the count is read
   if (MARKOV && !slab_loaded) load_w2_slab<KS, VEC>(a, cb, n, q, A);
-  // Each wave stages the item records of its chunks in LDS, two chunks ahead: lane l
-  // holds words l, l + 64, l + 128 of a later chunk's 16 records across a chunk, and the
-  // rows and constants are read from LDS when they are needed (no registers held
-  // through the products, no load waited on in the loop).  Records past the count are
-  // stale: indices are clamped to valid rows and nothing computed from them is written
-  // back.
+  // The rows in list order: the NI residual rows (items 0 .. NI-1), then the NB bonus
+  // rows (items ND-1, ND-2, ...), chunk c holding positions 16c .. 16c + 15.  Each wave
+  // stages the item records of its chunks in LDS, two chunks ahead: lane l holds words
+  // l, l + 64, l + 128 of a later chunk's 16 records across a chunk, and the rows and
+  // constants are read from LDS when they are needed (no registers held through the
+  // products, no load waited on in the loop).  Positions past the list read a clamped
+  // record: stale, indices clamped to valid rows, nothing computed from it written back.
   const int NT = a.B * (a.k + 1);
+  const int NI = ld_c(&a.ws.nitems[0]), NB = ld_c(&a.ws.nitems[1]);
+  const int NV = NI + NB;
+  auto item_of = [&](int i) { return i < NI ? i : ND - 1 - min(i - NI, ND - 1); };
   int32_t* stage = &L.items[w][0][0];
   int32_t words[3];
   const int32_t* item_words = reinterpret_cast<const int32_t*>(a.ws.items);
-  auto load_words = [&](int c) {   // word c * 192 + e of the list (clamped into it)
+  auto load_words = [&](int c) {
 #pragma unroll
-    for (int u = 0; u < 3; ++u) words[u] = ld_c(item_words + min(c * kStageWords + l + 64 * u, ND * kItemWords - 1));
+    for (int u = 0; u < 3; ++u) {
+      const int e = l + 64 * u;   // record e / 12 of the chunk, word e % 12 (compile-time per u and l range)
+      const int r = min(c * kChunk + e / kItemWords, ND - 1);
+      words[u] = ld_c(item_words + (size_t)item_of(r) * kItemWords + e % kItemWords);
+    }
   };
   auto store_words = [&](int c) {
 #pragma unroll
@@ -1361,47 +1406,52 @@ __device__ __forceinline__ void pass2_body(const Args& a, int g, Pass2Lds& L, bf
   // pipeline: records three chunks ahead (registers), two ahead in LDS; the logits of
   // chunk c in ring buffer c & 1, loaded two chunks ahead (the ring is indexed at
   // compile time: the loop runs two chunks per turn).  The prologue issues its loads in
-  // the order the loop's first waits need them (the list counts first, the logits
-  // last), so that those waits never have to drain the logits.
-  const int NI = ld_c(&a.ws.nitems[0]), NB = ld_c(&a.ws.nitems[1]);
-  // The W1 tile of a chunk (the B operand, the same for the 4 waves) goes through LDS,
-  // double-buffered: each thread holds its share of the tile two chunks ahead and
-  // stores it one chunk ahead; the workgroup barrier at the top of each chunk publishes
-  // it (and frees the buffer the previous chunk read).  Tiles past the list are stale
-  // (the region holds one per 16 draft rows) and unused.
+  // the order the loop's first waits need them (the logits last), so that those waits
+  // never have to drain the logits.
+  // The W1 tile of a chunk (the B operand, the same for the 4 waves: row n's previous
+  // token's W1 row in MFMA lane order, zero for a row with no previous token) goes
+  // through LDS, double-buffered: each thread gathers its share of the tile two chunks
+  // ahead (unit u: k-step u / 64, lane u % 64, from the chunk's records in this wave's
+  // stage) and stores it one chunk ahead; the workgroup barrier at the top of each
+  // chunk publishes it (and frees the buffer the previous chunk read).  Loads are
+  // unconditional (a row with no previous token reads W1 row 0), masked at the store.
   constexpr int kBtUnits = KS * 64, kBtPer = (kBtUnits + kThreads - 1) / kThreads;
-  const int ntiles = (ND + kChunk - 1) / kChunk;
   uint4 bt[kBtPer];
+  bool btv[kBtPer];
   // (a share is whole when the tile is a multiple of the workgroup: no branch then)
   auto bt_load = [&](int c) {
 #pragma unroll
     for (int i = 0; i < kBtPer; ++i) {
       const int u = tid + kThreads * i;
-      if (kBtUnits % kThreads == 0 || u < kBtUnits)
-        bt[i] = ld_c(&a.ws.btile[(size_t)min(c, ntiles - 1) * kBtUnits + u]);
+      if (kBtUnits % kThreads == 0 || u < kBtUnits) {
+        const int kk = u >> 6, ll = u & 63;
+        const int prev = stage[(c & 3) * kStageWords + (ll & 15) * kItemWords + 2];
+        btv[i] = prev >= 0 && prev < a.V;
+        bt[i] = *reinterpret_cast<const uint4*>(a.W1 + (size_t)(btv[i] ? prev : 0) * a.R + kk * 32 + 8 * (ll >> 4));
+      }
     }
   };
   auto bt_store = [&](int c) {
 #pragma unroll
     for (int i = 0; i < kBtPer; ++i) {
       const int u = tid + kThreads * i;
-      if (kBtUnits % kThreads == 0 || u < kBtUnits) L.btile[c & 1][u] = bt[i];
+      if (kBtUnits % kThreads == 0 || u < kBtUnits) L.btile[c & 1][u] = btv[i] ? bt[i] : make_uint4(0, 0, 0, 0);
     }
   };
   load_words(0);
-  if (MARKOV) bt_load(0);
   store_words(0);
   load_words(1);
+  if (MARKOV) bt_load(0);
+  store_words(1);
   if (MARKOV) {
     bt_store(0);
     bt_load(1);
   }
-  store_words(1);
   load_words(2);
   Raw16<DT> tr0, dr0, tr1, dr1;
   fetch(rows_of(0), tr0, dr0);
   fetch(rows_of(1), tr1, dr1);
-  const int nch = (NI + kChunk - 1) / kChunk;
+  const int nch = (NV + kChunk - 1) / kChunk;
   auto step = [&](int c, Raw16<DT>& tb, Raw16<DT>& db) {
     store_words(c + 2);   // loaded a chunk ago: the registers are free for the products
     if (MARKOV) {
@@ -1419,6 +1469,7 @@ __device__ __forceinline__ void pass2_body(const Args& a, int g, Pass2Lds& L, bf
     }
     load_words(c + 3);
     const int32_t* rc = record(c);
+    const bool bonus = rc[0] < 0;   // a bonus row: no draft row, raced over p_gamma
     const float4 k0 = make_float4(__int_as_float(rc[4]), __int_as_float(rc[5]), __int_as_float(rc[6]),
                                   __int_as_float(rc[7]));   // (Mt, Md, chi, clo)
     const float4 k1 = make_float4(__int_as_float(rc[8]), __int_as_float(rc[9]), __int_as_float(rc[10]),
@@ -1426,10 +1477,12 @@ __device__ __forceinline__ void pass2_body(const Args& a, int g, Pass2Lds& L, bf
     const uint32_t sb = (uint32_t)min(max(rc[3], 0), a.B - 1);
     uint2 ck[4];   // the row's clocks at this lane's ids, used by the race at the end
     load_clocks(a, sb, c0, ck);
-    // residual weights (normalised) and their sum, straight from the raw logits (the
-    // buffers are refilled after); then the race over them
+    // a residual row: weights w = max(0, P p - q) (normalised) and their sum; a bonus
+    // row: y = x log2(e) / T (unnormalised: every group of the row uses the same scale,
+    // which is all the race needs).  Straight from the raw logits (the buffers are
+    // refilled after); then the race over them.
     float s = 0.f;
-    float wr[16];
+    float y[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float xte = (rag && e < shift) ? -INFINITY : raw_elem<DT>(tb, e);
@@ -1439,22 +1492,27 @@ __device__ __forceinline__ void pass2_body(const Args& a, int g, Pass2Lds& L, bf
       const float ep = fmaf(tp, k0.z, k1.x) + fmaf(tp, k0.w, k1.y);
       const float eq = fmaf(tq, k0.z, k1.z) + fmaf(tq, k0.w, k1.w);
       const float wv = __builtin_amdgcn_exp2f(ep) - __builtin_amdgcn_exp2f(eq);
-      wr[e] = ((VEC || c0 + e < a.V) && wv > 0.f) ? wv : 0.f;
-      s += wr[e];
+      const bool in = VEC || c0 + e < a.V;
+      const float wr = (in && wv > 0.f) ? wv : 0.f;
+      y[e] = bonus ? (in ? xte * (k0.z + k0.w) : -INFINITY) : wr;
+      s += bonus ? 0.f : wr;
     }
     fetch(rows_of(c + 2), tb, db);
     s = sum4lanes(s);
-    const Top2 rt = top2_4lanes(race16_clk<false>(wr, ck, 0.f, c0));
+    const Top2 rt = top2_4lanes(race16_row(y, ck, bonus, c0));
     if (q == 0) {
       part[(c % kFlush) * kChunk + n][w] = s;
       rpart[(c % kFlush) * kChunk + n][w] = rt;
     }
     if (c % kFlush == kFlush - 1 || c == nch - 1) {
       __syncthreads();
-      const int it = (c - c % kFlush) * kChunk + tid;
-      if (tid < (c % kFlush + 1) * kChunk && it < NI) {
-        const int dr = min(max(ld_c(&a.ws.items[it].dr), 0), ND - 1);
-        st_c(&a.ws.wgrp[(size_t)g * ND + dr], (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]));
+      const int i = (c - c % kFlush) * kChunk + tid;
+      if (tid < (c % kFlush + 1) * kChunk && i < NV) {
+        const int it = item_of(i);
+        if (i < NI) {
+          const int dr = min(max(ld_c(&a.ws.items[it].dr), 0), ND - 1);
+          st_c(&a.ws.wgrp[(size_t)g * ND + dr], (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]));
+        }
         Top2 r = rpart[tid][0];
 #pragma unroll
         for (int ww = 1; ww < kWaves; ++ww) top2_merge(r, rpart[tid][ww]);
@@ -1466,35 +1524,6 @@ __device__ __forceinline__ void pass2_body(const Args& a, int g, Pass2Lds& L, bf
   for (int c = 0; c < nch; c += 2) {   // uniform: every wave runs the same chunks
     step(c, tr0, dr0);
     if (c + 1 < nch) step(c + 1, tr1, dr1);
-  }
-  // bonus rows the verifiers stop at (listed from the back of the list): race
-  // candidates of p_gamma, log2 w = x log2(e) / T (unnormalised: every group of the
-  // row uses the same scale, which is all the race needs)
-  for (int c = 0; c < (NB + kChunk - 1) / kChunk; ++c) {
-    const int ib = ND - 1 - min(c * kChunk + n, NB - 1);
-    const Item it = ld_c(&a.ws.items[ib]);
-    const int tr = min(max(it.tr, 0), NT - 1);
-    const uint32_t sb = (uint32_t)min(max(it.b, 0), a.B - 1);
-    const float chi = it.chi, clo = it.clo;   // log2(e) / T as hi + lo
-    Raw16<DT> t;
-    raw_load<DT, VEC>(t, reinterpret_cast<const char*>(a.target) + (size_t)tr * rb, c0, a.V);
-    uint2 ck[4];
-    load_clocks(a, sb, c0, ck);
-    float x[16];
-    raw_to_f32<DT>(t, x);
-    if (rag) mask_shift(x, shift);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) x[e] = (VEC || c0 + e < a.V) ? x[e] : -INFINITY;
-    const Top2 rt = top2_4lanes(race16_clk<true>(x, ck, chi + clo, c0));
-    if (q == 0) rpart[n][w] = rt;
-    __syncthreads();
-    if (tid < kChunk && c * kChunk + tid < NB) {
-      Top2 r = rpart[tid][0];
-#pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) top2_merge(r, rpart[tid][ww]);
-      st_c(&a.ws.race[(size_t)g * ND + (ND - 1 - (c * kChunk + tid))], r);
-    }
-    __syncthreads();
   }
 }
 
@@ -1508,7 +1537,7 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_kernel(Args a) {
 // ---------------------------------------------------------------------------
 // finalize: tau, the race, outputs.  One workgroup per stream.
 // ---------------------------------------------------------------------------
-__device__ double block_sum(double v, double* red) {
+__device__ __forceinline__ double block_sum(double v, double* red) {
   const int tid = threadIdx.x;
   v = wave_sum(v);
   if ((tid & 63) == 0) red[tid >> 6] = v;
@@ -1519,7 +1548,7 @@ __device__ double block_sum(double v, double* red) {
 }
 
 // Arg-max of score with the lowest index on ties; score < 0 means "not a contestant".
-__device__ void block_argmax(double& score, int& idx, double* rs, int* ri) {
+__device__ __forceinline__ void block_argmax(double& score, int& idx, double* rs, int* ri) {
   const int tid = threadIdx.x;
   wave_argmax(score, idx);
   if ((tid & 63) == 0) { rs[tid >> 6] = score; ri[tid >> 6] = idx; }
@@ -1602,7 +1631,7 @@ struct RaceLds {
 };
 
 template <class Score64>
-__device__ int race_pick(const Args& a, int it, int ND, RaceLds& sh, double* rs, int* ri, Score64 score64) {
+__device__ __forceinline__ int race_pick(const Args& a, int it, int ND, RaceLds& sh, double* rs, int* ri, Score64 score64) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int NG = a.NG;
   // every thread's first two groups are loaded at once (clamped, masked after)
@@ -1648,7 +1677,7 @@ __device__ int race_pick(const Args& a, int it, int ND, RaceLds& sh, double* rs,
 // The race over a whole target row in fp64 (w = exp2(x c) up to a common factor):
 // only when a residual has no mass anywhere (rounding; the verifiers then draw from p_s).
 template <int DT>
-__device__ int full_row_race(const Args& a, const char* row, uint32_t b, double c, double* rs, int* ri) {
+__device__ __forceinline__ int full_row_race(const Args& a, const char* row, uint32_t b, double c, double* rs, int* ri) {
   double bs = -INFINITY;
   int bv = 0x7fffffff;
   for (int v0 = 4 * threadIdx.x; v0 < a.V; v0 += 4 * kThreads) {
@@ -1675,7 +1704,7 @@ struct FinalLds {
 
 // Finalize of stream b.  Every thread of the workgroup calls it.
 template <int DT, int KS>
-__device__ __forceinline__ void finalize_body(const Args& a, int b, FinalLds& L) {
+__device__ __forceinline__ void finalize_body(const Args& a, int b, FinalLds& L, const float* tT = nullptr) {
   RaceLds& rl = L.rl;
   double* rs = L.rs;
   int* ri = L.ri;
@@ -1688,7 +1717,7 @@ __device__ __forceinline__ void finalize_body(const Args& a, int b, FinalLds& L)
   const int gamma = info.x, f = info.z;
   int stop = info.y;
   const uint32_t mask = ld_c(&a.ws.rowmask[b]);
-  const float Tf = stream_temp(a, b);
+  const float Tf = tT != nullptr ? tT[b] : stream_temp(a, b);
   if (Tf == 0.f) {   // greedy: the scan decided the stop and the token
     if (tid <= a.k) {
       const int s = stop;
@@ -1821,7 +1850,8 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(Args a) {
 // with a grid barrier between phases.  Data one phase leaves for another goes
 // through agent-coherent accesses (ld_c / st_c), so the barrier needs no cache
 // maintenance: each wave waits for its own memory operations, workgroup g then
-// writes its arrival word, workgroup 0 waits for all of them and writes the go word.
+// writes its arrival word, workgroup 0 waits for all of them and writes the go word
+// (its copies: workgroup g waits on copy g % kGoCopies).
 // A wait gives up after ~0.2 s (s_memrealtime counts at 100 MHz), sets the error
 // word and goes on; finalize then marks its streams' outputs invalid (accepted
 // length -1).  That can only happen if the workgroups are not all resident (for
@@ -1849,9 +1879,9 @@ __device__ __forceinline__ void grid_barrier(const Args& a, int phase) {
   if (g == 0) {
     for (int i = threadIdx.x; i < G; i += kThreads) spin_until_ge(&sync[kSyncStride * (1 + i)], phase, &sync[1]);
     __syncthreads();
-    if (threadIdx.x == 0) st_c(&sync[0], phase);
+    if (threadIdx.x < kGoCopies) st_c(&sync[kGoBase + kGoStride * threadIdx.x], phase);
   } else if (threadIdx.x == 0) {
-    spin_until_ge(&sync[0], phase, &sync[1]);
+    spin_until_ge(&sync[kGoBase + kGoStride * (g % kGoCopies)], phase, &sync[1]);
   }
   __syncthreads();
 }
@@ -1873,6 +1903,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(Args a) {
   bf16x8 A[4][KS];
   if (g < a.NG) pass1_body<DT, KS, MARKOV, VEC>(a, g, a.NG, *reinterpret_cast<Pass1Lds<KS, MARKOV>*>(lds), table, A);
   grid_barrier(a, 1);
+  const bool has_table = g < a.NG;   // pass 1 built the stream table in this workgroup's LDS
   // workgroups without a stream to scan compute the race clocks meanwhile; when every
   // workgroup scans, each takes its share of the clocks after its streams
   const int nscan = a.B < G ? a.B : G;
@@ -1882,7 +1913,8 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(Args a) {
     // the slab again afterwards (at B = 64 of 505 groups: 8 MB of W2); the others keep
     // theirs through phase 2
     for (int b = g; b < a.B; b += G) {
-      scan_body<DT>(a, b, *reinterpret_cast<ScanPhaseLds*>(lds));
+      scan_body<DT>(a, b, *reinterpret_cast<ScanPhaseLds*>(lds), has_table ? stream_table_T(a, table) : nullptr,
+                    has_table ? stream_table_gam(a, table) : nullptr);
       __syncthreads();
     }
     if (!spare) clock_rows(a, g, G);
@@ -1911,7 +1943,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(Args a) {
       if (threadIdx.x == 0) a.accepted_len[b] = -1;
       continue;
     }
-    finalize_body<DT, KS>(a, b, *reinterpret_cast<FinalLds*>(lds));
+    finalize_body<DT, KS>(a, b, *reinterpret_cast<FinalLds*>(lds), has_table ? stream_table_T(a, table) : nullptr);
     __syncthreads();
   }
 }
@@ -2025,7 +2057,7 @@ __global__ __launch_bounds__(kThreads, 2) void walk_partials_kernel(Args a, int 
 }
 
 // (value, index) maximum over the workgroup, lowest index among equal values.
-__device__ void block_max_index(double& val, int& idx, double* rs, int* ri) { block_argmax(val, idx, rs, ri); }
+__device__ __forceinline__ void block_max_index(double& val, int& idx, double* rs, int* ri) { block_argmax(val, idx, rs, ri); }
 
 template <int DT, int KS>
 __global__ __launch_bounds__(kThreads) void walk_pick_kernel(Args a, int j, int32_t* tokens_out, double* logq_out) {
