@@ -40,7 +40,8 @@ STAGE_NAMES = ["pack W1 tiles", "pass1 row statistics", "scan", "pass2 residual 
 # (FETCH_SIZE, then WRITE_SIZE; profiles/verify_fused_headline_b64_k5_v129280_hbm_bytes.md),
 # each scaled by what the same counter reads for a plain device copy of known size.
 # Valid only for the kernel sources it was measured on (hash below); otherwise null.
-FUSED_TRAFFIC = {"src_sha256_16": "", "fetch_bytes": 0.0, "write_bytes": 0.0}
+FUSED_TRAFFIC = {"src_sha256_16": "92e84a609f7de20c", "fetch_bytes": 151113.4 * 1024 * 2.0,
+                 "write_bytes": 21703.0 * 1024 * 1.0}
 
 
 def kernel_src_hash() -> str:
@@ -325,6 +326,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration table")
     ap.add_argument("--config-calls", type=int, default=100)
+    ap.add_argument("--verify-only", action="store_true",
+                    help="time the verify calls only (no read ceiling, walk, scheduler, table or host "
+                         "baseline): for profiler runs")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters)")
@@ -492,115 +496,116 @@ def main() -> int:
         "accepted_mean": {m: round(float(np.mean(realized[m])), 4) for m in realized},
     }
 
-    # the measured read ceiling of this device, beside the published peak
-    log("timing a plain streaming read (3 x 1 GiB buffers)")
-    ceil_gbps, ceil_grid = read_ceiling(torch, dev)
-    result["roofline"]["measured_read_GBps"] = round(ceil_gbps, 1)
-    result["roofline"]["frac_of_measured_read"] = round(achieved / ceil_gbps, 4)
-    result["roofline"]["pass1_separate_launch"]["frac_of_measured_read"] = round(
-        result["roofline"]["pass1_separate_launch"]["GBps"] / ceil_gbps, 4)
-    result["stream_read_ceiling"] = {
-        "GBps": round(ceil_gbps, 1), "grid": ceil_grid, "bytes_per_launch": 1 << 30, "buffers": 3,
-        "kernel": "dspark_stream_read: grid-stride 16-B loads, 256-thread groups, random bytes",
-    }
+    if not args.verify_only:
+        # the measured read ceiling of this device, beside the published peak
+        log("timing a plain streaming read (3 x 1 GiB buffers)")
+        ceil_gbps, ceil_grid = read_ceiling(torch, dev)
+        result["roofline"]["measured_read_GBps"] = round(ceil_gbps, 1)
+        result["roofline"]["frac_of_measured_read"] = round(achieved / ceil_gbps, 4)
+        result["roofline"]["pass1_separate_launch"]["frac_of_measured_read"] = round(
+            result["roofline"]["pass1_separate_launch"]["GBps"] / ceil_gbps, 4)
+        result["stream_read_ceiling"] = {
+            "GBps": round(ceil_gbps, 1), "grid": ceil_grid, "bytes_per_launch": 1 << 30, "buffers": 3,
+            "kernel": "dspark_stream_read: grid-stride 16-B loads, 256-thread groups, random bytes",
+        }
 
-    # the drafter's Markov walk at the same shape (the step before verification)
-    log("timing the drafter walk (B=64, k=5 slots)")
-    wtoks = torch.empty(B, k, dtype=torch.int32, device=dev)
-    for i in range(5):
-        s = sets[i % len(sets)]
-        dv.draft_sample(s["draft"], temperature=s["temp"], W1=s["W1"], W2t=s["W2t"], anchor=s["anchor"],
-                        seed=wl.seed, step=i, workspace=ws, out=wtoks)
-    nwalk = 30
-    torch.cuda.synchronize()
-    t0.record()
-    for i in range(nwalk):
-        s = sets[i % len(sets)]
-        dv.draft_sample(s["draft"], temperature=s["temp"], W1=s["W1"], W2t=s["W2t"], anchor=s["anchor"],
-                        seed=wl.seed, step=1000 + i, workspace=ws, out=wtoks)
-    t1.record()
-    torch.cuda.synchronize()
-    walk_ms = t0.elapsed_time(t1) / nwalk
-    walk_alg = 2.0 * V * B * k + 2.0 * R * V + 2.0 * R * B * k   # draft rows once, W2 once, W1 rows
-    walk_read = 2.0 * V * B * k + k * 2.0 * R * V + 2.0 * R * B * k   # W2 is read again for every slot
-    result["draft_walk"] = {
-        "ms_per_call": round(walk_ms, 5),
-        "drafts_per_s": round(B * k / (walk_ms * 1e-3), 1),
-        "alg_GBps": round(walk_alg / (walk_ms * 1e-3) / 1e9, 1),
-        "bytes_read_by_design_GBps": round(walk_read / (walk_ms * 1e-3) / 1e9, 1),
-        "launches": 2 * k,
-    }
-
-    # batch-level scheduler at the adaptive ragged shape (B=256 streams, k=5), and the
-    # host cost of the online cost table's event pairs around each call
-    log("timing the batch scheduler (B=256, k=5) and the online cost table")
-    Bs, ks = 256, 5
-    gsch = np.random.Generator(np.random.PCG64(5))
-    c_s = torch.from_numpy(gsch.uniform(0.5, 0.95, size=(Bs, ks)).astype(np.float32)).to(dev)
-    ms_s = torch.from_numpy((10.0 + 0.05 * np.arange(Bs * (ks + 1) + 1)).astype(np.float32)).to(dev)
-    n_s = torch.empty(Bs, dtype=torch.int32, device=dev)
-    for _ in range(10):
-        dv.schedule_batch(c_s, ms_s, n_out=n_s)
-    nsch = 200
-    tot_s = torch.empty(1, dtype=torch.int32, device=dev)
-    exp_s = torch.empty(1, dtype=torch.float64, device=dev)
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(nsch):
-        dv.schedule_batch(c_s, ms_s, n_out=n_s, total_out=tot_s, expected_out=exp_s)
-    t1.record()
-    torch.cuda.synchronize()
-    sched_ms = t0.elapsed_time(t1) / nsch   # bounded by the Python call, not the kernel
-    n_eager = n_s.clone()
-    # the kernel alone: 20 launches captured in a HIP graph, replayed 10 times, every
-    # replay's counts checked against the eager ones
-    sched_graph_ms = None
-    try:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(graph, stream=side):
-                for _ in range(20):
-                    dv.schedule_batch(c_s, ms_s, n_out=n_s, total_out=tot_s, expected_out=exp_s)
-        torch.cuda.current_stream().wait_stream(side)
+        # the drafter's Markov walk at the same shape (the step before verification)
+        log("timing the drafter walk (B=64, k=5 slots)")
+        wtoks = torch.empty(B, k, dtype=torch.int32, device=dev)
+        for i in range(5):
+            s = sets[i % len(sets)]
+            dv.draft_sample(s["draft"], temperature=s["temp"], W1=s["W1"], W2t=s["W2t"], anchor=s["anchor"],
+                            seed=wl.seed, step=i, workspace=ws, out=wtoks)
+        nwalk = 30
         torch.cuda.synchronize()
-        total_ms = 0.0
+        t0.record()
+        for i in range(nwalk):
+            s = sets[i % len(sets)]
+            dv.draft_sample(s["draft"], temperature=s["temp"], W1=s["W1"], W2t=s["W2t"], anchor=s["anchor"],
+                            seed=wl.seed, step=1000 + i, workspace=ws, out=wtoks)
+        t1.record()
+        torch.cuda.synchronize()
+        walk_ms = t0.elapsed_time(t1) / nwalk
+        walk_alg = 2.0 * V * B * k + 2.0 * R * V + 2.0 * R * B * k   # draft rows once, W2 once, W1 rows
+        walk_read = 2.0 * V * B * k + k * 2.0 * R * V + 2.0 * R * B * k   # W2 is read again for every slot
+        result["draft_walk"] = {
+            "ms_per_call": round(walk_ms, 5),
+            "drafts_per_s": round(B * k / (walk_ms * 1e-3), 1),
+            "alg_GBps": round(walk_alg / (walk_ms * 1e-3) / 1e9, 1),
+            "bytes_read_by_design_GBps": round(walk_read / (walk_ms * 1e-3) / 1e9, 1),
+            "launches": 2 * k,
+        }
+
+        # batch-level scheduler at the adaptive ragged shape (B=256 streams, k=5), and the
+        # host cost of the online cost table's event pairs around each call
+        log("timing the batch scheduler (B=256, k=5) and the online cost table")
+        Bs, ks = 256, 5
+        gsch = np.random.Generator(np.random.PCG64(5))
+        c_s = torch.from_numpy(gsch.uniform(0.5, 0.95, size=(Bs, ks)).astype(np.float32)).to(dev)
+        ms_s = torch.from_numpy((10.0 + 0.05 * np.arange(Bs * (ks + 1) + 1)).astype(np.float32)).to(dev)
+        n_s = torch.empty(Bs, dtype=torch.int32, device=dev)
         for _ in range(10):
-            n_s.fill_(-1)
-            t0.record()
-            graph.replay()
-            t1.record()
+            dv.schedule_batch(c_s, ms_s, n_out=n_s)
+        nsch = 200
+        tot_s = torch.empty(1, dtype=torch.int32, device=dev)
+        exp_s = torch.empty(1, dtype=torch.float64, device=dev)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(nsch):
+            dv.schedule_batch(c_s, ms_s, n_out=n_s, total_out=tot_s, expected_out=exp_s)
+        t1.record()
+        torch.cuda.synchronize()
+        sched_ms = t0.elapsed_time(t1) / nsch   # bounded by the Python call, not the kernel
+        n_eager = n_s.clone()
+        # the kernel alone: 20 launches captured in a HIP graph, replayed 10 times, every
+        # replay's counts checked against the eager ones
+        sched_graph_ms = None
+        try:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(graph, stream=side):
+                    for _ in range(20):
+                        dv.schedule_batch(c_s, ms_s, n_out=n_s, total_out=tot_s, expected_out=exp_s)
+            torch.cuda.current_stream().wait_stream(side)
             torch.cuda.synchronize()
-            total_ms += t0.elapsed_time(t1)
-            if not torch.equal(n_s, n_eager):
-                raise RuntimeError("graph replay of the scheduler disagrees with the eager call")
-        sched_graph_ms = total_ms / 200
-        del graph
-    except RuntimeError as e:
-        log(f"scheduler graph timing skipped: {e}")
-    table = dv.CostTable((10.0 + 0.05 * np.arange(Bs * (ks + 1) + 1)).astype(np.float32))
-    host_s = 0.0
-    for _ in range(nsch):
-        h0 = time.perf_counter()
-        table.begin(Bs + ks)
-        host_s += time.perf_counter() - h0
-        dv.schedule_batch(c_s, ms_s, n_out=n_s, total_out=tot_s, expected_out=exp_s)
-        h0 = time.perf_counter()
-        table.end()
+            total_ms = 0.0
+            for _ in range(10):
+                n_s.fill_(-1)
+                t0.record()
+                graph.replay()
+                t1.record()
+                torch.cuda.synchronize()
+                total_ms += t0.elapsed_time(t1)
+                if not torch.equal(n_s, n_eager):
+                    raise RuntimeError("graph replay of the scheduler disagrees with the eager call")
+            sched_graph_ms = total_ms / 200
+            del graph
+        except RuntimeError as e:
+            log(f"scheduler graph timing skipped: {e}")
+        table = dv.CostTable((10.0 + 0.05 * np.arange(Bs * (ks + 1) + 1)).astype(np.float32))
+        host_s = 0.0
+        for _ in range(nsch):
+            h0 = time.perf_counter()
+            table.begin(Bs + ks)
+            host_s += time.perf_counter() - h0
+            dv.schedule_batch(c_s, ms_s, n_out=n_s, total_out=tot_s, expected_out=exp_s)
+            h0 = time.perf_counter()
+            table.end()
+            table.poll()
+            host_s += time.perf_counter() - h0
+        torch.cuda.synchronize()
         table.poll()
-        host_s += time.perf_counter() - h0
-    torch.cuda.synchronize()
-    table.poll()
-    result["batch_schedule"] = {
-        "B": Bs, "k": ks,
-        "us_per_call_python": round(sched_ms * 1e3, 2),
-        "us_per_launch_graph": None if sched_graph_ms is None else round(sched_graph_ms * 1e3, 2),
-        "drafts_chosen": int(n_s.sum().item()),
-        "cost_table_host_us_per_step": round(host_s / nsch * 1e6, 2),
-        "cost_table_filed": table.stats()["filed"],
-    }
-    del table
+        result["batch_schedule"] = {
+            "B": Bs, "k": ks,
+            "us_per_call_python": round(sched_ms * 1e3, 2),
+            "us_per_launch_graph": None if sched_graph_ms is None else round(sched_graph_ms * 1e3, 2),
+            "drafts_chosen": int(n_s.sum().item()),
+            "cost_table_host_us_per_step": round(host_s / nsch * 1e6, 2),
+            "cost_table_filed": table.stats()["filed"],
+        }
+        del table
 
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -611,11 +616,11 @@ def main() -> int:
         result["copy_reference_bytes"] = 2 * (args.copy_mib << 20)
         del src, dst
 
-    if not args.no_configs:
+    if not args.no_configs and not args.verify_only:
         log(f"per-configuration table ({args.config_calls} calls per verifier each)")
         result["configs"] = config_table(torch, dv, workloads, dev, args.config_calls)
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.verify_only:
         log("timing the fp64 oracle on the host (1 thread, then one call per worker process)")
         result["cpu_baseline"] = cpu_baseline(B)
     print(json.dumps(result), flush=True)
