@@ -1704,7 +1704,10 @@ struct FinalLds {
 
 // Finalize of stream b.  Every thread of the workgroup calls it.
 template <int DT, int KS>
-__device__ __forceinline__ void finalize_body(const Args& a, int b, FinalLds& L, const float* tT = nullptr) {
+// err: the fused launch's error word (set when a grid-wide wait gave up), or null: when
+// set, the stream's outputs are marked invalid (accepted length -1, tokens -1).
+__device__ __forceinline__ void finalize_body(const Args& a, int b, FinalLds& L, const float* tT = nullptr,
+                                              const int32_t* err = nullptr) {
   RaceLds& rl = L.rl;
   double* rs = L.rs;
   int* ri = L.ri;
@@ -1714,23 +1717,24 @@ __device__ __forceinline__ void finalize_body(const Args& a, int b, FinalLds& L,
   const int NG = a.NG;
   const int ND = a.B * a.k;
   const int4 info = ld_c(reinterpret_cast<const int4*>(a.ws.info + 4 * b));
+  const int2 info2 = ld_c(reinterpret_cast<const int2*>(a.ws.info2 + 4 * b));
+  const bool failed = err != nullptr && ld_c(err) != 0;
   const int gamma = info.x, f = info.z;
   int stop = info.y;
   const uint32_t mask = ld_c(&a.ws.rowmask[b]);
   const float Tf = tT != nullptr ? tT[b] : stream_temp(a, b);
-  if (Tf == 0.f) {   // greedy: the scan decided the stop and the token
+  if (Tf == 0.f || failed) {   // greedy: the scan decided the stop and the token
     if (tid <= a.k) {
-      const int s = stop;
-      a.out_tokens[b * k1 + tid] = tid < s ? a.tokens[b * a.k + tid] : (tid == s ? info.w : -1);
+      const int s = failed ? -1 : stop;
+      a.out_tokens[b * k1 + tid] = failed ? -1 : (tid < s ? a.tokens[b * a.k + tid] : (tid == s ? info.w : -1));
       if (a.diag != nullptr) {
         double* dg = a.diag + ((size_t)b * k1 + tid) * 5;
         for (int e = 0; e < 5; ++e) dg[e] = NAN;
       }
     }
-    if (tid == 0) a.accepted_len[b] = stop;
+    if (tid == 0) a.accepted_len[b] = failed ? -1 : stop;
     return;
   }
-  const int2 info2 = ld_c(reinterpret_cast<const int2*>(a.ws.info2 + 4 * b));
   const double T = (double)Tf;
   const double c = kLog2e / T;
   const size_t esz = DT == kBF16 ? 2 : 4;
@@ -1936,14 +1940,9 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(Args a) {
   }
   if (g < a.NG) pass2_body<DT, KS, MARKOV, VEC>(a, g, *reinterpret_cast<Pass2Lds*>(lds), A, true);
   grid_barrier(a, 3);
-  const bool failed = ld_c(&a.ws.sync[1]) != 0;
   for (int b = g; b < a.B; b += G) {
-    if (failed) {
-      if (threadIdx.x <= a.k) a.out_tokens[b * (a.k + 1) + threadIdx.x] = -1;
-      if (threadIdx.x == 0) a.accepted_len[b] = -1;
-      continue;
-    }
-    finalize_body<DT, KS>(a, b, *reinterpret_cast<FinalLds*>(lds), has_table ? stream_table_T(a, table) : nullptr);
+    finalize_body<DT, KS>(a, b, *reinterpret_cast<FinalLds*>(lds), has_table ? stream_table_T(a, table) : nullptr,
+                          &a.ws.sync[1]);
     __syncthreads();
   }
 }
