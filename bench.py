@@ -526,14 +526,20 @@ def main() -> int:
         t1.record()
         torch.cuda.synchronize()
         walk_ms = t0.elapsed_time(t1) / nwalk
+        s = sets[0]
+        walk_launches = dv.draft_launches(s["draft"], temperature=s["temp"], W1=s["W1"], W2t=s["W2t"],
+                                          anchor=s["anchor"])
         walk_alg = 2.0 * V * B * k + 2.0 * R * V + 2.0 * R * B * k   # draft rows once, W2 once, W1 rows
-        walk_read = 2.0 * V * B * k + k * 2.0 * R * V + 2.0 * R * B * k   # W2 is read again for every slot
+        # by design: the resident walk reads W2 once, plus the B drawing workgroups' slabs
+        # again after each slot's draws; two launches per slot read W2 in every slot
+        w2_reads = 1.0 + (k - 1) * min(B, (V + 255) // 256) / ((V + 255) // 256) if walk_launches == 2 else float(k)
+        walk_read = 2.0 * V * B * k + w2_reads * 2.0 * R * V + 2.0 * R * B * k
         result["draft_walk"] = {
             "ms_per_call": round(walk_ms, 5),
             "drafts_per_s": round(B * k / (walk_ms * 1e-3), 1),
             "alg_GBps": round(walk_alg / (walk_ms * 1e-3) / 1e9, 1),
             "bytes_read_by_design_GBps": round(walk_read / (walk_ms * 1e-3) / 1e9, 1),
-            "launches": 2 * k,
+            "launches": walk_launches,
         }
 
         # batch-level scheduler at the adaptive ragged shape (B=256 streams, k=5), and the

@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.dspark_verify_noalloc.restype = i32
         L.dspark_draft_sample.argtypes = [ctypes.POINTER(VerifyProblem), vp, vp, vp, sz, vp]
         L.dspark_draft_sample.restype = i32
+        L.dspark_draft_launches.argtypes = [ctypes.POINTER(VerifyProblem), ctypes.POINTER(i32)]
+        L.dspark_draft_launches.restype = i32
         L.dspark_draft_scatter.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
         L.dspark_draft_scatter.restype = i32
         L.dspark_k_for_batch.argtypes = [vp, i32, i32, i32]
@@ -272,12 +274,7 @@ def verify_noalloc(method, target, draft, draft_tokens, num_drafts=None, tempera
     return acc, toks, dg
 
 
-def draft_sample(draft, num_drafts=None, temperature=None, W1=None, W2t=None, anchor=None, seed=0, step=0,
-                 logq=False, workspace=None, out=None):
-    """The drafter's Markov walk: x_j ~ softmax((d_j + W1[x_{j-1}] W2)/T) slot by slot.
-
-    draft [B, k, V]; returns (tokens [B, k] int32 with -1 past gamma_b, log q_j(x_j) [B, k] fp64 or None).
-    """
+def _walk_problem(draft, num_drafts, temperature, W1, W2t, anchor, seed, step):
     if draft.dim() != 3:
         raise ValueError("draft_logits must be [B, k, V]")
     B, k, V = draft.shape
@@ -302,10 +299,21 @@ def draft_sample(draft, num_drafts=None, temperature=None, W1=None, W2t=None, an
         _need(W2t, "W2t", (V, R), _BF16, dev)
     if anchor is not None:
         _need(anchor, "anchor_tokens", (B,), (torch.int32,), dev)
-    p = VerifyProblem(B=B, k=k, V=V, dtype=dt, target_logits=None, draft_logits=_ptr(draft), draft_tokens=None,
-                      num_drafts=_ptr(num_drafts), temperature=_ptr(temperature), W1=_ptr(W1),
-                      W2t=_ptr(W2t) if W1 is not None else None, anchor_tokens=_ptr(anchor), R=R,
-                      step=int(step) & 0xFFFFFFFF, seed=int(seed) & 0xFFFFFFFFFFFFFFFF)
+    return VerifyProblem(B=B, k=k, V=V, dtype=dt, target_logits=None, draft_logits=_ptr(draft), draft_tokens=None,
+                         num_drafts=_ptr(num_drafts), temperature=_ptr(temperature), W1=_ptr(W1),
+                         W2t=_ptr(W2t) if W1 is not None else None, anchor_tokens=_ptr(anchor), R=R,
+                         step=int(step) & 0xFFFFFFFF, seed=int(seed) & 0xFFFFFFFFFFFFFFFF)
+
+
+def draft_sample(draft, num_drafts=None, temperature=None, W1=None, W2t=None, anchor=None, seed=0, step=0,
+                 logq=False, workspace=None, out=None):
+    """The drafter's Markov walk: x_j ~ softmax((d_j + W1[x_{j-1}] W2)/T) slot by slot.
+
+    draft [B, k, V]; returns (tokens [B, k] int32 with -1 past gamma_b, log q_j(x_j) [B, k] fp64 or None).
+    """
+    p = _walk_problem(draft, num_drafts, temperature, W1, W2t, anchor, seed, step)
+    B, k, _ = draft.shape
+    dev = draft.device
     need = lib().dspark_workspace_bytes(ctypes.byref(p))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -315,6 +323,14 @@ def draft_sample(draft, num_drafts=None, temperature=None, W1=None, W2t=None, an
     _check(lib().dspark_draft_sample(ctypes.byref(p), _ptr(toks), _ptr(lq), _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(dev)))
     return toks, lq
+
+
+def draft_launches(draft, num_drafts=None, temperature=None, W1=None, W2t=None, anchor=None) -> int:
+    """Launches a walk of this problem makes on the current device (2, or 2 k)."""
+    p = _walk_problem(draft, num_drafts, temperature, W1, W2t, anchor, 0, 0)
+    n = ctypes.c_int32(0)
+    _check(lib().dspark_draft_launches(ctypes.byref(p), ctypes.byref(n)))
+    return int(n.value)
 
 
 def draft_scatter(reduced, vocab_ids, V: int, out=None):

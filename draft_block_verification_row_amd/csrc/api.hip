@@ -4,6 +4,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/dspark_verify.h"
@@ -48,8 +49,9 @@ Layout layout(int B, int k, int V) {
       BD * sizeof(Item),                // items
       kCounterInts * sizeof(int32_t),   // nitems: list counts and pass-1 item counters
       tiles * 8 * 64 * sizeof(uint4),   // btile (sized for the largest rank, R = 256)
-      BD * NG * sizeof(Top2),           // race candidates
-      (size_t)B * NG * kGroup * sizeof(int16_t),   // race clocks
+      std::max(BD * NG * sizeof(Top2), (size_t)B * NG * sizeof(WalkTop2)),   // race candidates
+      // race clocks; the resident walk: the drawing workgroups' next-slot clocks
+      std::max((size_t)B * NG * kGroup * sizeof(int16_t), 2 * std::min((size_t)B, NG) * kWalkClockBytes),
       kSyncInts * sizeof(int32_t),      // barrier words of the fused launch
   };
   Layout L;
@@ -141,17 +143,17 @@ dspark_status verify_common(const dspark_verify_problem* p, const dspark_verify_
 
 // The drafter walk: the verify problem's shapes, draft logits, temperatures, Markov
 // factors, anchors, num_drafts, seed and step; no target logits or draft tokens.
-dspark_status walk_common(const dspark_verify_problem* p, int32_t* tokens_out, double* logq_out, void* ws,
-                          size_t ws_bytes, void* stream) {
-  if (!problem_sizes_ok(p) || !p->draft_logits || !tokens_out) return DSPARK_ERR_INVALID_ARG;
+dspark_status walk_check(const dspark_verify_problem* p) {
+  if (!problem_sizes_ok(p) || !p->draft_logits) return DSPARK_ERR_INVALID_ARG;
   if (p->W1 != nullptr) {
     if (p->W2t == nullptr) return DSPARK_ERR_INVALID_ARG;
     if (!rank_ok(p->R)) return DSPARK_ERR_UNSUPPORTED;
     if (!aligned16(p->W1) || !aligned16(p->W2t)) return DSPARK_ERR_UNSUPPORTED;
   }
-  const Layout L = layout(p->B, p->k, p->V);
-  if (ws == nullptr || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
-    return DSPARK_ERR_WORKSPACE;
+  return DSPARK_OK;
+}
+
+Args walk_args(const dspark_verify_problem* p, int32_t* tokens_out) {
   Args a;
   memset(&a, 0, sizeof(a));
   a.B = p->B; a.k = p->k; a.V = p->V; a.R = p->W1 ? p->R : 0;
@@ -169,8 +171,23 @@ dspark_status walk_common(const dspark_verify_problem* p, int32_t* tokens_out, d
   a.key0 = (uint32_t)(p->seed & 0xffffffffu);
   a.key1 = (uint32_t)(p->seed >> 32);
   a.step = p->step;
-  a.ws.tpart = reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) + L.off[0]);   // [NG][B] partials
-  a.ws.race = reinterpret_cast<Top2*>(reinterpret_cast<char*>(ws) + L.off[16]);    // [NG][B] candidates
+  return a;
+}
+
+dspark_status walk_common(const dspark_verify_problem* p, int32_t* tokens_out, double* logq_out, void* ws,
+                          size_t ws_bytes, void* stream) {
+  const dspark_status st = walk_check(p);
+  if (st != DSPARK_OK) return st;
+  if (!tokens_out) return DSPARK_ERR_INVALID_ARG;
+  const Layout L = layout(p->B, p->k, p->V);
+  if (ws == nullptr || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
+    return DSPARK_ERR_WORKSPACE;
+  Args a = walk_args(p, tokens_out);
+  char* base = reinterpret_cast<char*>(ws);
+  a.ws.tpart = reinterpret_cast<float2*>(base + L.off[0]);    // [NG][B] partials
+  a.ws.race = reinterpret_cast<Top2*>(base + L.off[16]);      // [NG][B] candidates
+  a.ws.clk = reinterpret_cast<uint2*>(base + L.off[17]);     // the resident walk's offloaded clocks
+  a.ws.sync = reinterpret_cast<int32_t*>(base + L.off[18]);   // the resident walk's grid-wide waits
   if (launch_walk(a, tokens_out, logq_out, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return DSPARK_ERR_HIP;
   return DSPARK_OK;
@@ -222,6 +239,18 @@ dspark_status dspark_verify_noalloc(const dspark_verify_problem* p, const dspark
 dspark_status dspark_draft_sample(const dspark_verify_problem* p, int32_t* tokens_out, double* logq_out,
                                   void* ws, size_t ws_bytes, void* stream) {
   return walk_common(p, tokens_out, logq_out, ws, ws_bytes, stream);
+}
+
+dspark_status dspark_draft_launches(const dspark_verify_problem* p, int32_t* launches) {
+  if (launches == nullptr) return DSPARK_ERR_INVALID_ARG;
+  const dspark_status st = walk_check(p);
+  if (st != DSPARK_OK) return st;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DSPARK_ERR_HIP;
+  const int n = walk_launches(walk_args(p, nullptr));
+  if (n <= 0) return DSPARK_ERR_HIP;
+  *launches = n;
+  return DSPARK_OK;
 }
 
 size_t dspark_workspace_bytes(const dspark_verify_problem* p) {

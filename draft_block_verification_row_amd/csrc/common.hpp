@@ -250,6 +250,18 @@ struct Top2 {
   int32_t v2;
 };
 
+// The walk's race candidates: a row's best two (score, id) in a group, each with its
+// biased logit y = d + bias in fp64 (d exact; bias from the fp32 MFMA started from a
+// zero accumulator, absolute error of order 1e-9 for weights of the drafter's scale),
+// so that the draw scores them exactly without reading them again.
+struct WalkTop2 {
+  float s1;
+  int32_t v1;
+  float s2;
+  int32_t v2;
+  double y1, y2;
+};
+
 // ---------------------------------------------------------------------------
 // Workspace (carved on the host, 256-byte aligned regions).
 // ---------------------------------------------------------------------------
@@ -270,18 +282,22 @@ struct Workspace {
   Item* items;        // [B*k]         pass-2 list: residual rows from the front, bonus rows from the back
   int32_t* nitems;    // [kCounterInts] list counts and work counters (see kQueues)
   uint4* btile;       // [ceil(B*k/16)][R/32][64] W1 tiles of pass 2's rows in MFMA lane order
-  Top2* race;         // [NG][B*k]       race candidates of the pass-2 rows (by list index); the walk: [NG][B]
+  Top2* race;         // [NG][B*k]       race candidates of the pass-2 rows (by list index); the walk:
+                      //                 [NG][B] WalkTop2
   uint2* clk;         // [B][NG*64]      race clocks of sampled streams: log2 E in units of 2^-10 as
-                      //                 int16, four ids to a uint2 (ids 4i .. 4i+3 of the stream)
-  int32_t* sync;      // [kSyncInts]     fused launch: go word at [0], error word at [1], workgroup g's
+                      //                 int16, four ids to a uint2 (ids 4i .. 4i+3 of the stream);
+                      //                 the resident walk: its drawing workgroups' clocks
+  int32_t* sync;      // [kSyncInts]     fused launches: go word at [0], error word at [1], workgroup g's
                       //                 arrival word at [kSyncStride (1 + g)], go-word copies from
-                      //                 [kGoBase]; cleared by pack
+                      //                 [kGoBase]; cleared by pack (verify) or sync_clear_kernel (walk)
 };
 
 // The fused verify launch's barrier words: the go word at [0] and the error word at
 // [1], workgroup g's arrival word at [kSyncStride (1 + g)] (one 64-byte line each),
 // then kGoCopies copies of the go word, one 128-byte line apart (workgroup g waits on
 // copy g % kGoCopies, so that hundreds of waiting workgroups do not all poll one line).
+// Clock bytes of one resident-walk workgroup's block of rows (64 rows x 256 ids, int16).
+constexpr size_t kWalkClockBytes = 64 * 256 * 2;
 constexpr int kSyncStride = 16;
 constexpr int kMaxFusedGrid = 2048;
 constexpr int kGoCopies = 16;
@@ -356,6 +372,9 @@ constexpr size_t kMaxPassLds = 12 * 4096 + 16;
 // launchers (kernels.hip)
 hipError_t launch_verify(const Args& a, hipStream_t st, void* const* events);
 hipError_t launch_walk(const Args& a, int32_t* tokens_out, double* logq_out, hipStream_t st);
+// Launches a walk of this problem takes on the current device: 2 (the sync words are
+// cleared, then one resident launch) or 2 k (two per slot).
+int walk_launches(const Args& a);
 hipError_t launch_markov_bias(const BiasArgs& ba, int NG, hipStream_t st);
 hipError_t launch_adaptive(const AdaptArgs& aa, hipStream_t st);
 hipError_t launch_random_words(uint64_t seed, uint32_t b, uint32_t purpose, uint32_t step, uint32_t idx0, int n,

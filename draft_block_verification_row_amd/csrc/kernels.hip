@@ -159,6 +159,20 @@ __device__ __forceinline__ double wave_sum(double v) {
   v += dppd<0x140>(v);
   return swap_sum32(swap_sum16(v));
 }
+__device__ __forceinline__ double wave_max_f64(double v) {
+  v = fmax(v, dppd<0xB1>(v));
+  v = fmax(v, dppd<0x4E>(v));
+  v = fmax(v, dppd<0x141>(v));
+  v = fmax(v, dppd<0x140>(v));
+  {
+    const auto lo = __builtin_amdgcn_permlane16_swap(__double2loint(v), __double2loint(v), false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap(__double2hiint(v), __double2hiint(v), false, false);
+    v = fmax(__hiloint2double(hi[0], lo[0]), __hiloint2double(hi[1], lo[1]));
+  }
+  const auto lo = __builtin_amdgcn_permlane32_swap(__double2loint(v), __double2loint(v), false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap(__double2hiint(v), __double2hiint(v), false, false);
+  return fmax(__hiloint2double(hi[0], lo[0]), __hiloint2double(hi[1], lo[1]));
+}
 // (score, index) arg-max over the wave: larger score, then smaller index.
 __device__ __forceinline__ void take_better(double& s, int& i, double os, int oi) {
   if (os > s || (os == s && oi < i)) { s = os; i = oi; }
@@ -1196,98 +1210,16 @@ __device__ __forceinline__ Top2 top2_4lanes(Top2 t) {
   return swap_merge32(swap_merge16(t));
 }
 
-// A lane's best race candidate while its ids arrive in increasing order, as a ratio
-// w / E (0: none): a later id replaces an earlier one only with a strictly larger
-// ratio, so the smaller id wins ties without comparing ids.  Lanes keep one candidate
-// each and the best two of a row's lanes go on (top2_4lanes, then across waves): two
-// ids of one lane trade places only when their ratios agree to the fp32 rounding,
-// which the fp64 check of every candidate near the best does not need.
-struct LaneTop {
-  float s;
-  int32_t v;
-};
-__device__ __forceinline__ LaneTop lane_top_empty() { return LaneTop{0.f, INT_MAX}; }
-__device__ __forceinline__ void lane_top_add(LaneTop& t, float r, int v) {
-  const bool b = r > t.s;
-  t.s = b ? r : t.s;
-  t.v = b ? v : t.v;
-}
-// As a log2 score on the row's common scale: log2(w / E) + off, where the lane's
-// weights were w_v = 2^(log2 w_v - off).
-__device__ __forceinline__ Top2 lane_top_log2(const LaneTop& t, float off) {
-  Top2 r = top2_empty();
-  r.s1 = t.s > 0.f ? __builtin_amdgcn_logf(t.s) + off : -INFINITY;
-  r.v1 = t.s > 0.f ? t.v : INT_MAX;
-  return r;
-}
-
-// The race over this lane's ids c0 .. c0 + 15 (c0 a multiple of 4), one generator
-// block of four ids per step, from the lane's values parked in LDS (a private slot of
-// 4 float4: the race then needs none of the registers that produced them).
-// Ratios (EXP = false): the slot holds weights w >= 0 on the row's common scale.
-// Exponents (EXP = true): it holds y with weights 2^(y c) (y = -inf: none); they are
-// taken relative to the lane's largest y, m (so each lies in (0, 1]), and the result
-// is put back on the common scale, log2 w = y c.
-template <bool EXP>
-__device__ __forceinline__ Top2 race16(const float4* slot, float m, float c, int c0, uint32_t b, uint32_t purpose,
-                                       const Args& a) {
-  LaneTop t = lane_top_empty();
-#pragma unroll 1
-  for (int i = 0; i < 4; ++i) {
-    const float4 y4 = slot[i];
-    const float ys[4] = {y4.x, y4.y, y4.z, y4.w};
-    const uint4 x = philox4(b, (uint32_t)(c0 >> 2) + i, purpose, a.step, a.key0, a.key1);
-    const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float w = EXP ? __builtin_amdgcn_exp2f((ys[u] - m) * c) : ys[u];
-      lane_top_add(t, w * __builtin_amdgcn_rcpf(clock_f32(xs[u])), c0 + 4 * i + u);
-    }
-  }
-  return lane_top_log2(t, EXP ? m * c : 0.f);
-}
-
-__device__ __forceinline__ void park16(float4* slot, const float (&v)[16]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) slot[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-}
-
-__device__ __forceinline__ float max16(const float (&v)[16]) {
-  float m = v[0];
-#pragma unroll
-  for (int e = 1; e < 16; ++e) m = fmaxf(m, v[e]);
-  return m == -INFINITY ? 0.f : m;   // no weight in the lane: every ratio is 0
-}
-
-// A lane's best race score over its 16 ids c0 .. c0 + 15 in increasing order (a later
-// id replaces an earlier one only with a strictly larger score, so the smaller id wins
-// ties), from 16 clocks L (int16, units of 2^-10, two to a word).  Ratios (EXP =
-// false): y are weights w >= 0 and the score is log2 w - log2 E; exponents (EXP =
-// true): y are logits (-inf: none) with weights 2^(y c), and the score is y c - log2 E.
-// Either way the scores share the row's scale across lanes, waves and groups.
-template <bool EXP>
-__device__ __forceinline__ Top2 race16_clk(const float (&y)[16], const uint2 (&L)[4], float c, int c0) {
-  float best = -INFINITY;
-  int bv = INT_MAX;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const uint32_t word = (e & 2) ? L[e >> 2].y : L[e >> 2].x;
-    const int q = (e & 1) ? ((int32_t)word >> 16) : ((int32_t)(word << 16) >> 16);
-    const float lq = (float)q * 0x1.0p-10f;
-    const float sc = EXP ? fmaf(y[e], c, -lq) : (y[e] > 0.f ? __builtin_amdgcn_logf(y[e]) - lq : -INFINITY);
-    const bool better = sc > best;
-    best = better ? sc : best;
-    bv = better ? c0 + e : bv;
-  }
-  Top2 r = top2_empty();
-  r.s1 = best;
-  r.v1 = best > -INFINITY ? bv : INT_MAX;
-  return r;
-}
-
-// The race of pass 2's rows, listed or bonus (per lane): a listed row's y are residual
-// weights w >= 0 (score log2 w - log2 E), a bonus row's y are y = x c, the logits
-// scaled to log2 units (-inf: none; score y - log2 E).
+// The race of pass 2's rows, listed or bonus: a lane's best score over its 16 ids
+// c0 .. c0 + 15 in increasing order (a later id replaces an earlier one only with a
+// strictly larger score, so the smaller id wins ties), from 16 clocks L (int16, units
+// of 2^-10, two to a word).  A listed row's y are residual weights w >= 0 (score
+// log2 w - log2 E), a bonus row's y are y = x c, the logits scaled to log2 units
+// (-inf: none; score y - log2 E); either way the scores share the row's scale across
+// lanes, waves and groups.  Lanes keep one candidate each and the best two of a row's
+// lanes go on (top2_4lanes, then across waves): two ids of one lane trade places only
+// when their scores agree to the fp32 rounding, which the fp64 check of every
+// candidate near the best does not need.
 __device__ __forceinline__ Top2 race16_row(const float (&y)[16], const uint2 (&L)[4], bool bonus, int c0) {
   float best = -INFINITY;
   int bv = INT_MAX;
@@ -1590,14 +1522,18 @@ __device__ __forceinline__ float group_bias(const Args& a, int prev, int gsel, G
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int sl = l % SL, ri = l / SL;
   const uint4 w1 = *reinterpret_cast<const uint4*>(a.W1 + (size_t)prev * (32 * KS) + 8 * sl);
-  uint4 x[NI];
+  constexpr int NB = NI < 8 ? NI : 8;             // loads in flight per batch
+#pragma unroll 1
+  for (int n0 = 0; n0 < NI; n0 += NB) {
+    uint4 x[NB];
 #pragma unroll
-  for (int n = 0; n < NI; ++n) {
-    const int v = min(gsel * kGroup + w * 64 + n * RPI + ri, a.V - 1);   // rows past V: ignored
-    x[n] = *reinterpret_cast<const uint4*>(a.W2t + (size_t)v * (32 * KS) + 8 * sl);
+    for (int n = 0; n < NB; ++n) {
+      const int v = min(gsel * kGroup + w * 64 + (n0 + n) * RPI + ri, a.V - 1);   // rows past V: ignored
+      x[n] = *reinterpret_cast<const uint4*>(a.W2t + (size_t)v * (32 * KS) + 8 * sl);
+    }
+#pragma unroll
+    for (int n = 0; n < NB; ++n) sh.part[(w * 64 + (n0 + n) * RPI + ri) * (SL + 1) + sl] = dot8_bf16(w1, x[n]);
   }
-#pragma unroll
-  for (int n = 0; n < NI; ++n) sh.part[(w * 64 + n * RPI + ri) * (SL + 1) + sl] = dot8_bf16(w1, x[n]);
   __syncthreads();
   float acc = 0.f;
 #pragma unroll
@@ -1949,217 +1885,578 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(Args a) {
 
 // ---------------------------------------------------------------------------
 // The drafter's Markov walk [P2 §6 "Why the Markov Head Helps"; P1 §3 "The Markov
-// fix-up", Figure 2]: x_j ~ softmax((d_j + W1[x_{j-1}] . W2) / T), x_{-1} = anchor.
-// Slot j needs x_{j-1}, so each slot is two launches: group partials of the
-// biased logits of every stream (MFMA, like pass 1's draft rows), then one
-// workgroup per stream draws x_j with the two-level race (fp64 inside the group).
+// fix-up", Figure 2]: x_j ~ softmax((d_j + W1[x_{j-1}] . W2) / T), x_{-1} = anchor,
+// drawn by the exponential race over every id with the clocks of purpose 16 + j.
+// Slot j needs x_{j-1}, so a slot has two parts: the group partials and race
+// candidates of every stream's biased logits (one workgroup per 256-id group, MFMA
+// as in pass 1's draft rows), then one workgroup per stream that draws x_j (every
+// candidate near the best one scored again in fp64).  One resident launch runs all k
+// slots, with grid-wide waits between the parts, and every workgroup keeps its
+// group's W2 columns in registers throughout, so a walk reads W2 once; when the
+// workgroups cannot all be resident, the walk takes two launches per slot.
 // ---------------------------------------------------------------------------
-constexpr int kWalkRows = 64;   // streams per LDS block in the partial pass
+// threadIdx.x through an empty asm: values derived from it are computed where they are
+// used instead of being kept live (and spilled) across the walk's slot loop.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+constexpr int kWalkRows = 64;                      // streams per block of the partial part
+constexpr int kWalkChunks = kWalkRows / kChunk;    // MFMA chunks per block
 
-template <int DT, int KS, bool MARKOV, bool VEC>
-__global__ __launch_bounds__(kThreads, 2) void walk_partials_kernel(Args a, int j) {
-  __shared__ float2 part[kWalkRows][kWaves];
-  __shared__ Top2 rpart[kWalkRows][kWaves];
-  __shared__ float4 park[kThreads][4];   // a lane's 16 biased logits for the race
-  __shared__ int s_prev[kWalkRows];
-  __shared__ float s_c[kWalkRows];
-  __shared__ uint4 w1s[MARKOV ? kWalkRows * (4 * KS + 1) : 1];   // W1 rows, padded stride
-  const int g = blockIdx.x;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, q = l >> 4;
+template <int KS, bool MARKOV>
+struct WalkRowsLds {
+  float2 part[kWalkRows][kWaves];
+  WalkTop2 rpart[kWalkRows][kWaves];
+  int prev[kWalkRows];
+  float c[kWalkRows];
+  uint4 w1s[MARKOV ? kWalkRows * (4 * KS + 1) : 1];   // W1 rows, padded stride
+};
+
+// The race clocks of one block of rows, each thread's own: [cc][i][t] holds the int16
+// log2 clocks (units of 2^-10, two to a word) of the ids c0 + 4i .. c0 + 4i + 3 that
+// thread t covers in chunk cc.
+typedef uint2 WalkClocks[kWalkChunks][4][kThreads];
+
+// A thread's 16-id window in its group: ids c0 .. c0 + 15 (VEC: clamped inside the row,
+// its first `shift` ids belonging to the previous lane; rag: the wave's columns pass V).
+struct WalkLane {
+  int c0, shift;
+  bool rag;
+};
+template <bool VEC>
+__device__ __forceinline__ WalkLane walk_lane(const Args& a, int g) {
+  const int tid = opaque_tid(), w = tid >> 6, q = (tid & 63) >> 4;
   const int cb = g * kGroup + w * kWaveCols;
   const int cw = cb + 16 * q;
-  const int c0 = VEC ? min(cw, a.V - 16) : cw;
-  const int shift = VEC ? (cw >= a.V ? 16 : cw - c0) : 0;
-  const bool rag = VEC && cb + kWaveCols > a.V;
+  WalkLane r;
+  r.c0 = VEC ? min(cw, a.V - 16) : cw;
+  r.shift = VEC ? (cw >= a.V ? 16 : cw - r.c0) : 0;
+  r.rag = VEC && cb + kWaveCols > a.V;
+  return r;
+}
+
+// The slot-j draft logits of rows r0 .. r0 + 63 at this thread's window (rows past B
+// clamped to the last stream, their results unused).
+template <int DT, bool VEC>
+__device__ __forceinline__ void walk_load_rows(const Args& a, int j, int r0, int c0, Raw16<DT> (&xr)[kWalkChunks]) {
+  const int n = opaque_tid() & 15;
   const size_t rb = (size_t)a.V * (DT == kBF16 ? 2 : 4);
   const char* base = reinterpret_cast<const char*>(a.draft);
-  // A block's inputs (previous tokens, temperatures, the slot's logits rows) are loaded
-  // one block ahead; the first block's go out before the W2 slab, so that staging
-  // them waits only for them while the slab is in flight.
-  constexpr int NC = kWalkRows / kChunk;
-  // raw values, loaded without branches (a load under a branch makes the compiler wait
-  // for every load in flight where the paths join) and checked at use
-  int pv = -1;     // the anchor, or x_{j-1} from the previous slot
-  float T = 1.f;   // the stream's temperature
-  Raw16<DT> xr[NC];
-  auto load_block = [&](int r0) {
-    const int b = min(r0 + (tid & (kWalkRows - 1)), a.B - 1);
-    const int32_t* ps = j > 0 ? a.tokens + b * a.k + j - 1 : (a.anchor ? a.anchor + b : a.tokens + b * a.k);
-    const float* ts = a.temperature ? a.temperature + b : reinterpret_cast<const float*>(a.tokens + b * a.k);
-    pv = *ps;
-    T = *ts;
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc)
-      raw_load<DT, VEC>(xr[cc], base + ((size_t)min(r0 + cc * kChunk + n, a.B - 1) * a.k + j) * rb, c0, a.V);
-  };
-  load_block(0);
-  bf16x8 A[4][KS];
-  if (MARKOV) load_w2_slab<KS, VEC>(a, cb, n, q, A);
-  __builtin_amdgcn_sched_barrier(0);   // keep the uses of the block's inputs after the slab loads
-  for (int r0 = 0; r0 < a.B; r0 += kWalkRows) {
-    if (tid < kWalkRows) {
-      const bool has = j > 0 || a.anchor != nullptr;
-      s_prev[tid] = (has && pv >= 0 && pv < a.V) ? pv : -1;   // as draft_prev
-      const float Tb = a.temperature ? T : 1.f;                  // as stream_temp
-      s_c[tid] = Tb > 0.f ? (float)(kLog2e / (double)Tb) : 1e-30f;
-    }
-    __syncthreads();
-    if (MARKOV) {   // stage the block's W1 rows: whole rows per wave instruction
-      u32x4* d = reinterpret_cast<u32x4*>(w1s);
-      for (int u = tid; u < kWalkRows * 4 * KS; u += kThreads) {
-        const int row = u / (4 * KS), piece = u % (4 * KS);
-        const int pv = s_prev[row];
-        const u32x4 v = *reinterpret_cast<const u32x4*>(a.W1 + (size_t)(pv >= 0 ? pv : 0) * a.R + 8 * piece);
-        d[row * (4 * KS + 1) + piece] = pv >= 0 ? v : u32x4{0u, 0u, 0u, 0u};
-      }
-      __syncthreads();
-    }
+  for (int cc = 0; cc < kWalkChunks; ++cc)
+    raw_load<DT, VEC>(xr[cc], base + ((size_t)min(r0 + cc * kChunk + n, a.B - 1) * a.k + j) * rb, c0, a.V);
+}
+
+// The four clocks of one generator block, two to a word.
+__device__ __forceinline__ uint2 clock_words(const uint4& x) {
+  const uint32_t q0 = (uint32_t)clock_log2_q10(x.x) & 0xffffu, q1 = (uint32_t)clock_log2_q10(x.y) & 0xffffu;
+  const uint32_t q2 = (uint32_t)clock_log2_q10(x.z) & 0xffffu, q3 = (uint32_t)clock_log2_q10(x.w) & 0xffffu;
+  return make_uint2(q0 | (q1 << 16), q2 | (q3 << 16));
+}
+
+// The slot-j clocks of rows r0 .. r0 + 63 at this thread's window: they depend on
+// nothing the walk draws, so a resident walk computes them while it waits.
+__device__ __forceinline__ void walk_fill_clocks(const Args& a, int j, int r0, int c0, WalkClocks& clk) {
+  const int tid = opaque_tid(), n = tid & 15;
+#pragma unroll 1
+  for (int cc = 0; cc < kWalkChunks; ++cc) {
+    const uint32_t b = (uint32_t)min(r0 + cc * kChunk + n, a.B - 1);
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      const int rr = cc * kChunk + n;              // row within the block
-      float x[16];
-      raw_to_f32<DT>(xr[cc], x);
-      if (MARKOV) {
-        bf16x8 Bop[KS];
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-          Bop[kk] = __builtin_bit_cast(bf16x8, w1s[rr * (4 * KS + 1) + 4 * kk + q]);
-        markov_mma<KS>(A, Bop, x);
-      }
-      if (rag) mask_shift(x, shift);
-      const float2 pw = row_partial<0>(x, s_c[rr]);
-      // race candidates of q_j: log2 w = x log2(e) / T, a common scale for the row
-#pragma unroll
-      for (int e = 0; e < 16; ++e) x[e] = (VEC || c0 + e < a.V) ? x[e] : -INFINITY;
-      const uint32_t sb = (uint32_t)min(r0 + rr, a.B - 1);
-      park16(park[tid], x);
-      const Top2 rt = top2_4lanes(race16<true>(park[tid], max16(x), s_c[rr], c0, sb, walk_purpose(j), a));
-      if (q == 0) {
-        part[rr][w] = pw;
-        rpart[rr][w] = rt;
-      }
-    }
-    __syncthreads();
-    if (tid < kWalkRows && r0 + tid < a.B) {
-      float2 p[kWaves];
-#pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) p[ww] = part[tid][ww];
-      a.ws.tpart[(size_t)g * a.B + r0 + tid] = combine_waves(p, s_c[tid]);
-      Top2 r = rpart[tid][0];
-#pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) top2_merge(r, rpart[tid][ww]);
-      a.ws.race[(size_t)g * a.B + r0 + tid] = r;
-    }
-    if (r0 + kWalkRows < a.B) load_block(r0 + kWalkRows);   // uniform
-    __syncthreads();
+    for (int i = 0; i < 4; ++i)
+      clk[cc][i][tid] = clock_words(philox4(b, (uint32_t)(c0 >> 2) + i, walk_purpose(j), a.step, a.key0, a.key1));
   }
 }
 
-// (value, index) maximum over the workgroup, lowest index among equal values.
-__device__ __forceinline__ void block_max_index(double& val, int& idx, double* rs, int* ri) { block_argmax(val, idx, rs, ri); }
+// Chunk cc of the first block's slot-j clocks of another workgroup's group, at the
+// window thread t covers there (window start c0), into dst[i][t] (coherent stores).
+__device__ __forceinline__ void walk_clock_chunk(const Args& a, int j, int cc, int c0, uint2* dst) {
+  const int tid = opaque_tid(), n = tid & 15;
+  const uint32_t b = (uint32_t)min(cc * kChunk + n, a.B - 1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    st_c(&dst[i * kThreads + tid],
+         clock_words(philox4(b, (uint32_t)(c0 >> 2) + i, walk_purpose(j), a.step, a.key0, a.key1)));
+}
 
+// A lane's best race score y c - log2 E over its 16 ids c0 .. c0 + 15 in increasing
+// order (the smaller id wins ties), x = d + bias the biased logits (-inf: none), with
+// that id's d (exact, from the raw logits) + bias in fp64.
+struct WalkCand {
+  float s;
+  int32_t v;
+  double y;
+};
+template <int DT>
+__device__ __forceinline__ WalkCand walk_race16(const float (&x)[16], const float (&bias)[16], const Raw16<DT>& d,
+                                                const uint2 (&L)[4], float c, int c0) {
+  float best = -INFINITY, bd = 0.f, bb = 0.f;
+  int bv = INT_MAX;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const uint32_t word = (e & 2) ? L[e >> 2].y : L[e >> 2].x;
+    const int q = (e & 1) ? ((int32_t)word >> 16) : ((int32_t)(word << 16) >> 16);
+    const float sc = fmaf(x[e], c, -(float)q * 0x1.0p-10f);
+    const bool better = sc > best;
+    best = better ? sc : best;
+    bv = better ? c0 + e : bv;
+    bd = better ? raw_elem<DT>(d, e) : bd;
+    bb = better ? bias[e] : bb;
+  }
+  return WalkCand{best, best > -INFINITY ? bv : INT_MAX, (double)bd + (double)bb};
+}
+
+__device__ __forceinline__ WalkTop2 wtop2_empty() { return WalkTop2{-INFINITY, INT_MAX, -INFINITY, INT_MAX, 0.0, 0.0}; }
+// As top2_add, carrying each candidate's y.
+__device__ __forceinline__ void wtop2_add(WalkTop2& a, float s, int v, double y) {
+  const bool b1 = top_better(s, v, a.s1, a.v1);
+  const bool b2 = top_better(s, v, a.s2, a.v2);
+  const float s2 = b1 ? a.s1 : (b2 ? s : a.s2);
+  const int v2 = b1 ? a.v1 : (b2 ? v : a.v2);
+  const double y2 = b1 ? a.y1 : (b2 ? y : a.y2);
+  a.s1 = b1 ? s : a.s1;
+  a.v1 = b1 ? v : a.v1;
+  a.y1 = b1 ? y : a.y1;
+  a.s2 = s2;
+  a.v2 = v2;
+  a.y2 = y2;
+}
+__device__ __forceinline__ void wtop2_merge(WalkTop2& a, const WalkTop2& o) {
+  wtop2_add(a, o.s1, o.v1, o.y1);
+  wtop2_add(a, o.s2, o.v2, o.y2);
+}
+// The best two of the candidates of lanes {n, n+16, n+32, n+48} (row swaps, as
+// top2_4lanes); every lane of the four ends with the same result.
+__device__ __forceinline__ WalkTop2 walk_top2_4lanes(const WalkCand& c) {
+  auto sw16 = [](uint32_t x) { return __builtin_amdgcn_permlane16_swap(x, x, false, false); };
+  auto sw32 = [](uint32_t x) { return __builtin_amdgcn_permlane32_swap(x, x, false, false); };
+  WalkTop2 t = wtop2_empty();
+  {
+    const auto s = sw16(__float_as_uint(c.s));
+    const auto v = sw16((uint32_t)c.v);
+    const auto lo = sw16((uint32_t)__double2loint(c.y));
+    const auto hi = sw16((uint32_t)__double2hiint(c.y));
+    wtop2_add(t, __uint_as_float(s[0]), (int)v[0], __hiloint2double((int)hi[0], (int)lo[0]));
+    wtop2_add(t, __uint_as_float(s[1]), (int)v[1], __hiloint2double((int)hi[1], (int)lo[1]));
+  }
+  const auto s1 = sw32(__float_as_uint(t.s1));
+  const auto v1 = sw32((uint32_t)t.v1);
+  const auto s2 = sw32(__float_as_uint(t.s2));
+  const auto v2 = sw32((uint32_t)t.v2);
+  const auto y1l = sw32((uint32_t)__double2loint(t.y1)), y1h = sw32((uint32_t)__double2hiint(t.y1));
+  const auto y2l = sw32((uint32_t)__double2loint(t.y2)), y2h = sw32((uint32_t)__double2hiint(t.y2));
+  WalkTop2 r{__uint_as_float(s1[0]), (int)v1[0], __uint_as_float(s2[0]), (int)v2[0],
+             __hiloint2double((int)y1h[0], (int)y1l[0]), __hiloint2double((int)y2h[0], (int)y2l[0])};
+  wtop2_merge(r, WalkTop2{__uint_as_float(s1[1]), (int)v1[1], __uint_as_float(s2[1]), (int)v2[1],
+                          __hiloint2double((int)y1h[1], (int)y1l[1]), __hiloint2double((int)y2h[1], (int)y2l[1])});
+  return r;
+}
+
+// Group partials (max, sum) and race candidates of slot j for rows r0 .. r0 + 63 of
+// group g, from their draft logits xr and clocks clk; written to tpart / race [g][b].
+// Every thread of the workgroup calls it.
+template <int DT, int KS, bool MARKOV, bool VEC>
+__device__ __forceinline__ void walk_block(const Args& a, int g, int j, int r0, const WalkLane& wl,
+                                           const Raw16<DT> (&xr)[kWalkChunks], const bf16x8 (&A)[4][KS],
+                                           WalkRowsLds<KS, MARKOV>& L, const WalkClocks& clk) {
+  const int tid = opaque_tid(), w = tid >> 6, l = tid & 63, n = l & 15, q = l >> 4;
+  if (tid < kWalkRows) {
+    const int b = min(r0 + tid, a.B - 1);
+    // an absent input reads a stand-in word (the stream's first token slot), replaced
+    const int32_t* standin = a.tokens + (size_t)b * a.k;
+    const float T = *(a.temperature != nullptr ? a.temperature + b : reinterpret_cast<const float*>(standin));
+    // x_{j-1} was drawn by another workgroup (of this launch, or of the previous one)
+    const int pv = j > 0 ? ld_c(a.tokens + (size_t)b * a.k + j - 1) : *(a.anchor != nullptr ? a.anchor + b : standin);
+    const bool has = j > 0 || a.anchor != nullptr;
+    L.prev[tid] = (has && pv >= 0 && pv < a.V) ? pv : -1;   // as draft_prev
+    const float Tb = a.temperature != nullptr ? T : 1.f;      // as stream_temp
+    L.c[tid] = Tb > 0.f ? (float)(kLog2e / (double)Tb) : 1e-30f;
+  }
+  __syncthreads();
+  if (MARKOV) {   // the block's W1 rows: whole rows per wave instruction, all in flight
+    constexpr int kPer = kWalkRows * 4 * KS / kThreads;
+    u32x4* d = reinterpret_cast<u32x4*>(L.w1s);
+    u32x4 v[kPer];
+    int pv[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int u = tid + i * kThreads, row = u / (4 * KS), piece = u % (4 * KS);
+      pv[i] = L.prev[row];
+      v[i] = *reinterpret_cast<const u32x4*>(a.W1 + (size_t)(pv[i] >= 0 ? pv[i] : 0) * a.R + 8 * piece);
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int u = tid + i * kThreads, row = u / (4 * KS), piece = u % (4 * KS);
+      d[row * (4 * KS + 1) + piece] = pv[i] >= 0 ? v[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int cc = 0; cc < kWalkChunks; ++cc) {
+    const int rr = cc * kChunk + n;   // row within the block
+    float x[16], bias[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) bias[e] = 0.f;
+    if (MARKOV) {   // the bias alone (a zero accumulator, B operand read one k-step at a time)
+      f32x4 acc[4];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) acc[s4] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const bf16x8 bop = __builtin_bit_cast(bf16x8, L.w1s[rr * (4 * KS + 1) + 4 * kk + q]);
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+          acc[s4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[s4][kk], bop, acc[s4], 0, 0, 0);
+      }
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bias[4 * s4 + i] = acc[s4][i];
+    }
+    raw_to_f32<DT>(xr[cc], x);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) x[e] += bias[e];
+    if (wl.rag) mask_shift(x, wl.shift);
+    const float c = L.c[rr];
+    const float2 pw = row_partial<0>(x, c);
+    // race scores of q_j: y c - log2 E with y c = log2 of the weight on the row's scale
+#pragma unroll
+    for (int e = 0; e < 16; ++e) x[e] = (VEC || wl.c0 + e < a.V) ? x[e] : -INFINITY;
+    uint2 ck[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ck[i] = clk[cc][i][tid];
+    const WalkTop2 rt = walk_top2_4lanes(walk_race16<DT>(x, bias, xr[cc], ck, c, wl.c0));
+    if (q == 0) {
+      L.part[rr][w] = pw;
+      L.rpart[rr][w] = rt;
+    }
+    __builtin_amdgcn_sched_barrier(0);   // one chunk's values at a time
+  }
+  __syncthreads();
+  if (tid < kWalkRows && r0 + tid < a.B) {
+    float2 p[kWaves];
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) p[ww] = L.part[tid][ww];
+    st_c(&a.ws.tpart[(size_t)g * a.B + r0 + tid], combine_waves(p, L.c[tid]));
+    WalkTop2 r = L.rpart[tid][0];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) wtop2_merge(r, L.rpart[tid][ww]);
+    st_c(&reinterpret_cast<WalkTop2*>(a.ws.race)[(size_t)g * a.B + r0 + tid], r);
+  }
+  __syncthreads();
+}
+
+// ln x for x > 0 from x = f 2^e, f in [1/2, 1): (e + log2 f) ln 2 with the hardware
+// log2 of f, absolute error of order 1e-7; and e^d for d <= 0 with the hardware exp2,
+// relative error of order 1e-7 near 0 (2e-6 at d = -30).  The walk's normaliser of
+// log q takes these in place of library fp64 calls, far inside its 1e-5 budget.
+__device__ __forceinline__ double ln_split(float x) {
+  int e;
+  const float f = frexpf(x, &e);
+  return ((double)e + (double)__builtin_amdgcn_logf(f)) * kLn2;
+}
+__device__ __forceinline__ double exp_neg(double d) { return (double)__builtin_amdgcn_exp2f((float)(d * kLog2e)); }
+
+template <int KS>
+struct WalkPickLds {
+  GroupBiasLds<KS> gb;   // the greedy branch's group bias
+  int cand[kMaxCand];
+  double sc[kMaxCand];   // fp64 race scores of the candidates
+  double yv[kMaxCand];   // and their biased logits
+  int n;
+  float best[kWaves];
+  double lmax[kWaves], red[kWaves], rs[kWaves];
+  int ri[kWaves];
+};
+
+// x_j of stream b from the slot's group partials and race candidates (written by other
+// workgroups: coherent loads).  Sampled: the race winner, every candidate within
+// kRaceWindow of the best fp32 score scored again in fp64 as y c - log2 E from the y
+// its record carries and its exact clock; log q_j(x) = y_x / T - ln sum_v exp(y_v / T),
+// the sum from the fp32 group partials.  Greedy (T = 0): the largest biased logit, the
+// smallest id among equals.  err: the resident walk's error word, or null; once set,
+// the slot's outputs are marked invalid (token -1, log q NaN).  Every thread of the
+// workgroup calls it.
 template <int DT, int KS>
-__global__ __launch_bounds__(kThreads) void walk_pick_kernel(Args a, int j, int32_t* tokens_out, double* logq_out) {
-  __shared__ GroupBiasLds<KS> gb;
-  __shared__ RaceLds rl;
-  __shared__ double rs[kWaves];
-  __shared__ int ri[kWaves];
-  __shared__ double red[kWaves];
-  __shared__ double s_xv;
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void walk_pick_body(const Args& a, int b, int j, int32_t* tokens_out, double* logq_out,
+                                               WalkPickLds<KS>& L, const int32_t* err) {
+  const int tid = opaque_tid(), w = tid >> 6, l = tid & 63;
   const int NG = a.NG;
-  // the stream's draft count, temperature and previous token, and a thread's first
-  // two group partials, go out together: branch-free addresses (the tokens drawn so
-  // far stand in for an absent input, whose value is then replaced)
-  const int graw = *(a.num_drafts != nullptr ? a.num_drafts + b : a.tokens);
-  const float traw = *(a.temperature != nullptr ? a.temperature + b : reinterpret_cast<const float*>(a.tokens));
-  const int praw = *(j > 0 ? a.tokens + b * a.k + j - 1 : (a.anchor != nullptr ? a.anchor + b : a.tokens));
-  const float2 p0 = a.ws.tpart[(size_t)min(tid, NG - 1) * a.B + b];
-  const float2 p1 = a.ws.tpart[(size_t)min(tid + kThreads, NG - 1) * a.B + b];
+  const size_t ND = (size_t)a.B;
+  const WalkTop2* race = reinterpret_cast<const WalkTop2*>(a.ws.race);
+  const int g0 = min(tid, NG - 1), g1 = min(tid + kThreads, NG - 1);
+  // the stream's inputs and a thread's first two groups go out together: branch-free
+  // addresses (a stand-in word for an absent input, replaced after)
+  const int32_t* standin = a.tokens + (size_t)b * a.k;
+  const int graw = *(a.num_drafts != nullptr ? a.num_drafts + b : standin);
+  const float traw = *(a.temperature != nullptr ? a.temperature + b : reinterpret_cast<const float*>(standin));
+  const int praw = j > 0 ? ld_c(a.tokens + (size_t)b * a.k + j - 1) : *(a.anchor != nullptr ? a.anchor + b : standin);
+  float2 p0 = ld_c(&a.ws.tpart[(size_t)g0 * ND + b]), p1 = ld_c(&a.ws.tpart[(size_t)g1 * ND + b]);
+  WalkTop2 t0 = ld_c(&race[(size_t)g0 * ND + b]), t1 = ld_c(&race[(size_t)g1 * ND + b]);
+  const int failed = err != nullptr ? ld_c(err) : 0;
   __builtin_amdgcn_sched_barrier(0);
   const int gamma = a.num_drafts != nullptr ? (graw < 0 ? 0 : (graw > a.k ? a.k : graw)) : a.k;
-  if (j >= gamma) {
+  if (j >= gamma || failed != 0) {   // uniform
     if (tid == 0) {
-      tokens_out[b * a.k + j] = -1;
-      if (logq_out != nullptr) logq_out[b * a.k + j] = NAN;
+      st_c(&tokens_out[(size_t)b * a.k + j], -1);
+      if (logq_out != nullptr) logq_out[(size_t)b * a.k + j] = NAN;
     }
     return;
   }
+  if (tid >= NG) {
+    p0 = make_float2(-INFINITY, 0.f);
+    t0 = wtop2_empty();
+  }
+  if (tid + kThreads >= NG) {
+    p1 = make_float2(-INFINITY, 0.f);
+    t1 = wtop2_empty();
+  }
   const float Tf = a.temperature != nullptr ? traw : 1.0f;
-  const bool greedy = Tf == 0.f;
-  const int pr = (j > 0 || a.anchor != nullptr) ? praw : -1;
-  const int prev = (a.W1 != nullptr && pr >= 0 && pr < a.V) ? pr : -1;
-  const size_t esz = DT == kBF16 ? 2 : 4;
-  const char* drow = reinterpret_cast<const char*>(a.draft) + ((size_t)b * a.k + j) * a.V * esz;
   int x;
-  if (greedy) {
-    // the largest biased logit: the group with the largest maximum, then inside it the
-    // biased logits in fp64 (the group's Markov bias from one cooperative pass over its
-    // W2t rows), the first id among equal values
+  if (Tf == 0.f) {
+    // the group with the largest maximum, then inside it the biased logits in fp64 (the
+    // group's Markov bias from one cooperative pass over its W2t rows)
+    const int pr = (j > 0 || a.anchor != nullptr) ? praw : -1;
+    const int prev = (a.W1 != nullptr && pr >= 0 && pr < a.V) ? pr : -1;
+    const size_t esz = DT == kBF16 ? 2 : 4;
+    const char* drow = reinterpret_cast<const char*>(a.draft) + ((size_t)b * a.k + j) * a.V * esz;
     double best = -INFINITY;
     int gbest = 0x7fffffff;
     auto max_group = [&](int gi, float2 p) {
-      if (gi < NG && p.x != -INFINITY && (double)p.x > best) { best = (double)p.x; gbest = gi; }
+      if (p.x != -INFINITY && (double)p.x > best) { best = (double)p.x; gbest = gi; }
     };
     max_group(tid, p0);
     max_group(tid + kThreads, p1);
-    for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) max_group(gi, a.ws.tpart[(size_t)gi * a.B + b]);
-    block_max_index(best, gbest, rs, ri);
+    for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) max_group(gi, ld_c(&a.ws.tpart[(size_t)gi * ND + b]));
+    block_argmax(best, gbest, L.rs, L.ri);
     const int gsel = gbest < NG ? gbest : 0;
     const int v = gsel * kGroup + tid;
-    const float bias = prev >= 0 ? group_bias<KS>(a, prev, gsel, gb) : 0.f;
+    const float bias = prev >= 0 ? group_bias<KS>(a, prev, gsel, L.gb) : 0.f;
     double xv = v < a.V ? (double)load1<DT>(drow, v) + (double)bias : -INFINITY;
     int vbest = v < a.V ? v : 0x7fffffff;
-    block_max_index(xv, vbest, rs, ri);
+    block_argmax(xv, vbest, L.rs, L.ri);
     x = vbest < a.V ? vbest : gsel * kGroup;
-    if (tid == 0 && logq_out != nullptr) logq_out[b * a.k + j] = NAN;
+    if (tid == 0 && logq_out != nullptr) logq_out[(size_t)b * a.k + j] = NAN;
   } else {
-    // the race over q_j from the per-group candidates, re-scored in fp64:
-    // log2 w - log2 E with log2 w = (d_j(v) + bias(v)) log2(e) / T
     const double invT = 1.0 / (double)Tf;
     const double c = kLog2e * invT;
-    auto biased = [&](int v) {   // whole wave
-      const double bias = prev >= 0 ? bias_f64_wave(a, prev, v) : 0.0;
-      return (double)load1<DT>(drow, v) + bias;
-    };
-    x = race_pick(a, b, a.B, rl, rs, ri, [&](int v) {
-      const double y = biased(v);
-      const uint32_t xw = stream_word(a.key0, a.key1, (uint32_t)b, (uint32_t)v, walk_purpose(j), a.step);
-      return y != -INFINITY ? y * c - clock_log2_f64(xw) : -INFINITY;
-    });
-    if (x < 0) x = 0;   // a row with no finite logit (excluded by the caller's contract)
-    if (logq_out != nullptr) {
-      // log q_j(x) = y_x / T - ln sum_g W_g, the sum from the fp32 group partials
-      if (tid < 64) {
-        const double y = biased(x);
-        if (tid == 0) s_xv = y;
+    // a group's log weight for the normaliser: m_g / T + ln s_g
+    auto lw = [&](float2 p) { return p.x != -INFINITY ? (double)p.x * invT + ln_split(p.y) : -INFINITY; };
+    const double lw0 = lw(p0), lw1 = lw(p1);
+    float best = fmaxf(t0.s1, t1.s1);
+    double lm = fmax(lw0, lw1);
+    for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) {
+      best = fmaxf(best, ld_c(&race[(size_t)gi * ND + b]).s1);
+      lm = fmax(lm, lw(ld_c(&a.ws.tpart[(size_t)gi * ND + b])));
+    }
+    best = wave_max_dpp(best);
+    lm = wave_max_f64(lm);
+    if (tid == 0) L.n = 0;
+    if (l == 0) {
+      L.best[w] = best;
+      L.lmax[w] = lm;
+    }
+    __syncthreads();
+    best = fmaxf(fmaxf(L.best[0], L.best[1]), fmaxf(L.best[2], L.best[3]));
+    lm = fmax(fmax(L.lmax[0], L.lmax[1]), fmax(L.lmax[2], L.lmax[3]));
+    // candidates within the window of the best fp32 score; the normaliser's terms
+    const float floor_ = best - kRaceWindow;
+    auto offer = [&](float s, int v, double y) {
+      if (s >= floor_ && v >= 0 && v < a.V) {
+        const int k = atomicAdd(&L.n, 1);
+        if (k < kMaxCand) {
+          L.cand[k] = v;
+          L.yv[k] = y;
+        }
       }
-      double lmax = -INFINITY;
-      auto lw_group = [&](int gi, float2 p) {
-        return (gi < NG && p.x != -INFINITY) ? (double)p.x * invT + log((double)p.y) : -INFINITY;
-      };
-      lmax = fmax(lw_group(tid, p0), lw_group(tid + kThreads, p1));
-      for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads)
-        lmax = fmax(lmax, lw_group(gi, a.ws.tpart[(size_t)gi * a.B + b]));
-      double m = lmax;
-      for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off));
-      if ((tid & 63) == 0) red[tid >> 6] = m;
+    };
+    offer(t0.s1, t0.v1, t0.y1);
+    offer(t0.s2, t0.v2, t0.y2);
+    offer(t1.s1, t1.v1, t1.y1);
+    offer(t1.s2, t1.v2, t1.y2);
+    double sum = (lw0 != -INFINITY ? exp_neg(lw0 - lm) : 0.0) + (lw1 != -INFINITY ? exp_neg(lw1 - lm) : 0.0);
+    for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) {
+      const WalkTop2 t = ld_c(&race[(size_t)gi * ND + b]);
+      offer(t.s1, t.v1, t.y1);
+      offer(t.s2, t.v2, t.y2);
+      const double lg = lw(ld_c(&a.ws.tpart[(size_t)gi * ND + b]));
+      if (lg != -INFINITY) sum += exp_neg(lg - lm);
+    }
+    sum = wave_sum(sum);
+    if (l == 0) L.red[w] = sum;
+    __syncthreads();
+    const int nc = min(L.n, kMaxCand);
+    sum = (L.red[0] + L.red[1]) + (L.red[2] + L.red[3]);
+    int bv = nc == 1 ? L.cand[0] : 0x7fffffff;
+    // A lone candidate is the winner: every id whose exact score could reach the best
+    // fp32 score's lies within the window, and so does any id of its group that ranks
+    // above it.  Otherwise each candidate's exact score, one per thread.
+    if (nc > 1) {   // uniform
+      for (int ci = tid; ci < nc; ci += kThreads) {
+        const double y = L.yv[ci];
+        const uint32_t xw = stream_word(a.key0, a.key1, (uint32_t)b, (uint32_t)L.cand[ci], walk_purpose(j), a.step);
+        L.sc[ci] = y != -INFINITY ? y * c - clock_log2_f64(xw) : -INFINITY;
+      }
       __syncthreads();
-      m = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
-      __syncthreads();
-      double sum = 0.0;
-      auto add_group = [&](int gi, float2 p) {
-        if (gi < NG && p.x != -INFINITY) sum += exp((double)p.x * invT + log((double)p.y) - m);
-      };
-      add_group(tid, p0);
-      add_group(tid + kThreads, p1);
-      for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) add_group(gi, a.ws.tpart[(size_t)gi * a.B + b]);
-      sum = block_sum(sum, red);
-      if (tid == 0) logq_out[b * a.k + j] = s_xv * invT - (m + log(sum));
+      double bs = -INFINITY;
+      for (int ci = tid; ci < nc; ci += kThreads) take_better(bs, bv, L.sc[ci], L.cand[ci]);
+      block_argmax(bs, bv, L.rs, L.ri);
+    }
+    x = bv < a.V ? bv : 0;   // 0: a row with no finite logit (excluded by the caller's contract)
+    if (tid == 0 && logq_out != nullptr) {
+      double y = NAN;
+      for (int ci = 0; ci < nc; ++ci)
+        if (L.cand[ci] == bv) y = L.yv[ci];
+      logq_out[(size_t)b * a.k + j] = y * invT - (lm + ln_split((float)sum));
     }
   }
-  if (tid == 0) tokens_out[b * a.k + j] = x;
+  if (tid == 0) st_c(&tokens_out[(size_t)b * a.k + j], x);
+}
+
+// Two launches per slot: the partial part (one workgroup per group), then the draws.
+template <int DT, int KS, bool MARKOV, bool VEC>
+__global__ __launch_bounds__(kThreads, 2) void walk_partials_kernel(Args a, int j) {
+  __shared__ WalkRowsLds<KS, MARKOV> L;
+  __shared__ WalkClocks clk;
+  const int g = blockIdx.x;
+  const int tid = opaque_tid();
+  const WalkLane wl = walk_lane<VEC>(a, g);
+  Raw16<DT> xr[kWalkChunks];
+  walk_load_rows<DT, VEC>(a, j, 0, wl.c0, xr);   // before the slab: staged while it is in flight
+  bf16x8 A[4][KS];
+  if (MARKOV) load_w2_slab<KS, VEC>(a, g * kGroup + (tid >> 6) * kWaveCols, tid & 15, (tid & 63) >> 4, A);
+  walk_fill_clocks(a, j, 0, wl.c0, clk);
+  for (int r0 = 0; r0 < a.B; r0 += kWalkRows) {
+    if (r0 > 0) {
+      walk_load_rows<DT, VEC>(a, j, r0, wl.c0, xr);
+      walk_fill_clocks(a, j, r0, wl.c0, clk);
+    }
+    walk_block<DT, KS, MARKOV, VEC>(a, g, j, r0, wl, xr, A, L, clk);
+  }
+}
+
+template <int DT, int KS>
+__global__ __launch_bounds__(kThreads) void walk_pick_kernel(Args a, int j, int32_t* tokens_out, double* logq_out) {
+  __shared__ WalkPickLds<KS> L;
+  walk_pick_body<DT, KS>(a, blockIdx.x, j, tokens_out, logq_out, L, nullptr);
+}
+
+// The resident walk's split grid-wide wait: a workgroup announces that its part of a
+// phase is done (walk_arrive), may do work that depends on no other workgroup, then
+// waits until every workgroup has announced (walk_wait).  The last workgroup collects
+// the announcements and writes the go words; waits are bounded as in the fused verify
+// launch (an expired wait sets the error word).
+__device__ __forceinline__ void walk_arrive(const Args& a, int phase) {
+  wait_memory();
+  __syncthreads();
+  if (opaque_tid() == 0) st_c(&a.ws.sync[kSyncStride * (1 + blockIdx.x)], phase);
+}
+
+__device__ __forceinline__ void walk_wait(const Args& a, int phase) {
+  int* sync = a.ws.sync;
+  const int g = blockIdx.x, G = gridDim.x;
+  if (g == G - 1) {
+    for (int i = opaque_tid(); i < G; i += kThreads) spin_until_ge(&sync[kSyncStride * (1 + i)], phase, &sync[1]);
+    __syncthreads();
+    if (opaque_tid() < kGoCopies) st_c(&sync[kGoBase + kGoStride * opaque_tid()], phase);
+  } else if (opaque_tid() == 0) {
+    spin_until_ge(&sync[kGoBase + kGoStride * (g % kGoCopies)], phase, &sync[1]);
+  }
+  __syncthreads();
+}
+
+// The go and error words and the arrival words of a G-workgroup resident launch.
+__global__ __launch_bounds__(kThreads) void sync_clear_kernel(int32_t* sync, int G) {
+  const int t = opaque_tid();
+  if (t == 0) st_c(&sync[1], 0);
+  if (t < kGoCopies) st_c(&sync[kGoBase + kGoStride * t], 0);
+  for (int i = t; i <= G; i += kThreads) st_c(&sync[kSyncStride * i], 0);
+}
+
+template <int KS, bool MARKOV>
+__host__ __device__ constexpr size_t walk_lds_bytes() {
+  const size_t m = sizeof(WalkRowsLds<KS, MARKOV>) > sizeof(WalkPickLds<KS>) ? sizeof(WalkRowsLds<KS, MARKOV>)
+                                                                             : sizeof(WalkPickLds<KS>);
+  return (m + 15) / 16 * 16;
+}
+
+// The whole walk in one launch of NG workgroups (all resident).  Slot j: every
+// workgroup computes its group's partials and candidates (phase 2j + 1); the first
+// P = min(B, NG) workgroups then wait for all of them and draw (workgroup g draws
+// streams g, g + NG, ...), while the others compute the drawing workgroups' clocks
+// for slot j + 1 (their first block of rows, into the clock region, one buffer per
+// slot parity: a slot's buffer is written only after every reader of its previous
+// contents has passed a wait) and then their own; everyone waits for the draws
+// (phase 2j + 2).  The last workgroup collects the arrivals.
+template <int DT, int KS, bool MARKOV, bool VEC>
+__global__ __launch_bounds__(kThreads, 2) void walk_fused_kernel(Args a, int32_t* tokens_out, double* logq_out) {
+  __shared__ __align__(16) char lds[walk_lds_bytes<KS, MARKOV>()];
+  __shared__ WalkClocks clk;
+  auto& L = *reinterpret_cast<WalkRowsLds<KS, MARKOV>*>(lds);
+  auto& P = *reinterpret_cast<WalkPickLds<KS>*>(lds);
+  const int g = blockIdx.x, G = gridDim.x;
+  const int tid = opaque_tid();
+  const int NP = a.B < G ? a.B : G;   // drawing workgroups
+  const int NO = G - NP;              // the others
+  const bool picker = g < NP, master = g == G - 1;
+  // [2][NP][kWalkChunks][4][kThreads]: the drawing workgroups' clocks by slot parity
+  uint2* const pclk = a.ws.clk;
+  auto pbuf = [&](int slot, int pg) { return pclk + ((size_t)(slot & 1) * NP + pg) * kWalkChunks * 4 * kThreads; };
+  const WalkLane wl = walk_lane<VEC>(a, g);
+  Raw16<DT> xr[kWalkChunks];
+  walk_load_rows<DT, VEC>(a, 0, 0, wl.c0, xr);
+  bf16x8 A[4][KS];
+  if (MARKOV) load_w2_slab<KS, VEC>(a, g * kGroup + (tid >> 6) * kWaveCols, tid & 15, (tid & 63) >> 4, A);
+  walk_fill_clocks(a, 0, 0, wl.c0, clk);
+  for (int j = 0; j < a.k; ++j) {
+    if (picker && j > 0 && NO > 0) {   // this slot's clocks, computed by the others
+      const uint2* src = pbuf(j, g);
+#pragma unroll
+      for (int cc = 0; cc < kWalkChunks; ++cc)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) clk[cc][i][tid] = ld_c(&src[(cc * 4 + i) * kThreads + tid]);
+    }
+    for (int r0 = 0; r0 < a.B; r0 += kWalkRows) {
+      if (r0 > 0) {
+        walk_load_rows<DT, VEC>(a, j, r0, wl.c0, xr);
+        walk_fill_clocks(a, j, r0, wl.c0, clk);
+      }
+      walk_block<DT, KS, MARKOV, VEC>(a, g, j, r0, wl, xr, A, L, clk);
+    }
+    const int ph1 = 2 * j + 1, ph2 = 2 * j + 2;
+    const bool last = j + 1 == a.k;
+    walk_arrive(a, ph1);
+    if (picker) {
+      walk_wait(a, ph1);
+      for (int b = g; b < a.B; b += G) {
+        walk_pick_body<DT, KS>(a, b, j, tokens_out, logq_out, P, &a.ws.sync[1]);
+        __syncthreads();
+      }
+      if (!last) {
+        walk_arrive(a, ph2);
+        // the draws took the slab's registers: it comes back while the others finish
+        // (W2 is read again by the drawing workgroups only)
+        if (MARKOV) load_w2_slab<KS, VEC>(a, g * kGroup + (tid >> 6) * kWaveCols, tid & 15, (tid & 63) >> 4, A);
+        walk_load_rows<DT, VEC>(a, j + 1, 0, wl.c0, xr);
+        if (NO == 0) walk_fill_clocks(a, j + 1, 0, wl.c0, clk);
+        walk_wait(a, ph2);
+      }
+    } else {
+      if (master) walk_wait(a, ph1);
+      if (!last) {
+        // a share of the drawing workgroups' clocks (task t: workgroup t / 4, chunk t % 4)
+        for (int t = g - NP; t < NP * kWalkChunks; t += NO) {
+          const int pg = t / kWalkChunks, cc = t % kWalkChunks;
+          walk_clock_chunk(a, j + 1, cc, walk_lane<VEC>(a, pg).c0, pbuf(j + 1, pg) + cc * 4 * kThreads);
+        }
+        walk_arrive(a, ph2);
+        walk_load_rows<DT, VEC>(a, j + 1, 0, wl.c0, xr);
+        walk_fill_clocks(a, j + 1, 0, wl.c0, clk);
+        walk_wait(a, ph2);
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -2171,7 +2468,7 @@ __global__ __launch_bounds__(kThreads) void walk_pick_kernel(Args a, int j, int3
 __global__ __launch_bounds__(kThreads) void random_words_kernel(uint32_t k0, uint32_t k1, uint32_t b, uint32_t purpose,
                                                                 uint32_t step, uint32_t idx0, int n, int kind,
                                                                 uint32_t* out) {
-  const int i = blockIdx.x * kThreads + threadIdx.x;
+  const int i = blockIdx.x * kThreads + opaque_tid();
   if (i >= n) return;
   const uint32_t idx = idx0 + (uint32_t)i;
   out[i] = kind == 0 ? philox_word0(b, idx, purpose, step, k0, k1) : stream_word(k0, k1, b, idx, purpose, step);
@@ -2194,7 +2491,7 @@ __global__ __launch_bounds__(kThreads) void w2_transpose_kernel(const uint16_t* 
                                                                  uint16_t* __restrict__ w2t) {
   __shared__ uint32_t tile[kTrTile][kTrTile + 1];   // +1: column reads spread over banks
   const int v0 = blockIdx.x * kTrTile, r0 = blockIdx.y * kTrTile;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int tx = opaque_tid() & 63, ty = opaque_tid() >> 6;
 #pragma unroll
   for (int i = 0; i < kTrTile / kWaves; ++i) {
     const int r = r0 + ty + kWaves * i, v = v0 + tx;
@@ -2222,7 +2519,7 @@ hipError_t launch_w2_transpose(const uint16_t* w2, int R, int V, uint16_t* w2t, 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void fill_ninf_kernel(void* out, size_t n) {
   const size_t stride = (size_t)gridDim.x * kThreads;
-  for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
+  for (size_t i = (size_t)blockIdx.x * kThreads + opaque_tid(); i < n; i += stride) {
     if (DT == kBF16) reinterpret_cast<uint16_t*>(out)[i] = 0xFF80u;   // bf16 -inf
     else reinterpret_cast<float*>(out)[i] = -INFINITY;
   }
@@ -2233,7 +2530,7 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const void* in, const
                                                            void* out) {
   const size_t n = (size_t)rows * K;
   const size_t stride = (size_t)gridDim.x * kThreads;
-  for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
+  for (size_t i = (size_t)blockIdx.x * kThreads + opaque_tid(); i < n; i += stride) {
     const int r = (int)(i / K), c = (int)(i - (size_t)r * K);
     const int v = ids[c];
     if (v < 0 || v >= V) continue;   // ids are the caller's: out-of-range ones are dropped
@@ -2252,7 +2549,7 @@ __global__ __launch_bounds__(kThreads) void markov_bias_kernel(BiasArgs ba) {
   Args a{};
   a.V = ba.V; a.R = ba.R; a.W1 = ba.W1; a.W2t = ba.W2t;
   const int g = blockIdx.x;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, q = l >> 4;
+  const int tid = opaque_tid(), w = tid >> 6, l = tid & 63, n = l & 15, q = l >> 4;
   const int cb = g * kGroup + w * kWaveCols;
   const int c0 = cb + 16 * q;
   bf16x8 A[4][KS];
@@ -2298,7 +2595,7 @@ __global__ __launch_bounds__(kThreads) void adaptive_kernel(AdaptArgs aa) {
   __shared__ double s_part[kWaves][kMaxK];
   __shared__ double s_c[kMaxK];
   const int b = blockIdx.x;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int tid = opaque_tid(), w = tid >> 6, l = tid & 63;
   // w . h for every slot: the whole workgroup splits H, each wave sums its share in
   // fp64 and the 4 wave sums meet in LDS
   for (int j0 = 0; j0 < aa.k; j0 += kSlots) {
@@ -2474,8 +2771,52 @@ hipError_t launch_verify(const Args& a, hipStream_t st, void* const* ev) {
   return a.dtype == kBF16 ? launch_dt<kBF16>(a, st, ev) : launch_dt<kF32>(a, st, ev);
 }
 
+// Workgroups of the resident walk (NG) when they can all be resident on the current
+// device, else 0 (two launches per slot).  DSPARK_WALK_LAUNCH=separate in the
+// environment forces the two launches per slot.
 template <int DT, int KS, bool MARKOV, bool VEC>
-static hipError_t launch_walk_t(const Args& a, int32_t* tokens_out, double* logq_out, hipStream_t st) {
+static int walk_grid_for(const Args& a) {
+  const char* env = getenv("DSPARK_WALK_LAUNCH");
+  if (env != nullptr && strcmp(env, "separate") == 0) return 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  static int cus[64], occ[64];   // occ: resident workgroups per CU, + 1 once computed
+  static std::mutex mu;
+  int resident;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0 && hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    if (occ[dev] == 0) {
+      int o = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, walk_fused_kernel<DT, KS, MARKOV, VEC>, kThreads, 0) !=
+          hipSuccess)
+        return 0;
+      occ[dev] = o + 1;
+    }
+    resident = (occ[dev] - 1) * cus[dev];
+  }
+  return (a.NG <= resident && a.NG <= kMaxFusedGrid) ? a.NG : 0;
+}
+
+template <int DT, int KS, bool MARKOV, bool VEC>
+static hipError_t launch_walk_t(const Args& a, int32_t* tokens_out, double* logq_out, hipStream_t st, int* launches) {
+  const int G = walk_grid_for<DT, KS, MARKOV, VEC>(a);
+  if (launches != nullptr) {   // the plan only
+    *launches = G > 0 ? 2 : 2 * a.k;
+    return hipSuccess;
+  }
+  if (G > 0) {
+    // the resident walk writes its wait words and, when some workgroups draw nothing,
+    // the drawing workgroups' clocks
+    if (a.ws.sync == nullptr || a.ws.clk == nullptr || a.ws.tpart == nullptr || a.ws.race == nullptr)
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL(sync_clear_kernel, dim3(1), dim3(kThreads), 0, st, a.ws.sync, G);
+    hipLaunchKernelGGL((walk_fused_kernel<DT, KS, MARKOV, VEC>), dim3(G), dim3(kThreads), 0, st, a, tokens_out,
+                       logq_out);
+    return hipGetLastError();
+  }
+  if (a.ws.tpart == nullptr || a.ws.race == nullptr) return hipErrorInvalidValue;
   for (int j = 0; j < a.k; ++j) {
     hipLaunchKernelGGL((walk_partials_kernel<DT, KS, MARKOV, VEC>), dim3(a.NG), dim3(kThreads), 0, st, a, j);
     hipLaunchKernelGGL((walk_pick_kernel<DT, KS>), dim3(a.B), dim3(kThreads), 0, st, a, j, tokens_out, logq_out);
@@ -2484,24 +2825,32 @@ static hipError_t launch_walk_t(const Args& a, int32_t* tokens_out, double* logq
 }
 
 template <int DT, bool VEC>
-static hipError_t launch_walk_vec(const Args& a, int32_t* t, double* lq, hipStream_t st) {
-  if (a.W1 == nullptr) return launch_walk_t<DT, 1, false, VEC>(a, t, lq, st);
+static hipError_t launch_walk_vec(const Args& a, int32_t* t, double* lq, hipStream_t st, int* n) {
+  if (a.W1 == nullptr) return launch_walk_t<DT, 1, false, VEC>(a, t, lq, st, n);
   switch (a.R) {
-    case 32: return launch_walk_t<DT, 1, true, VEC>(a, t, lq, st);
-    case 64: return launch_walk_t<DT, 2, true, VEC>(a, t, lq, st);
-    case 128: return launch_walk_t<DT, 4, true, VEC>(a, t, lq, st);
-    default: return launch_walk_t<DT, 8, true, VEC>(a, t, lq, st);
+    case 32: return launch_walk_t<DT, 1, true, VEC>(a, t, lq, st, n);
+    case 64: return launch_walk_t<DT, 2, true, VEC>(a, t, lq, st, n);
+    case 128: return launch_walk_t<DT, 4, true, VEC>(a, t, lq, st, n);
+    default: return launch_walk_t<DT, 8, true, VEC>(a, t, lq, st, n);
   }
 }
 
 template <int DT>
-static hipError_t launch_walk_dt(const Args& a, int32_t* t, double* lq, hipStream_t st) {
-  return (a.vec_ok && a.V >= 16) ? launch_walk_vec<DT, true>(a, t, lq, st) : launch_walk_vec<DT, false>(a, t, lq, st);
+static hipError_t launch_walk_dt(const Args& a, int32_t* t, double* lq, hipStream_t st, int* n) {
+  return (a.vec_ok && a.V >= 16) ? launch_walk_vec<DT, true>(a, t, lq, st, n)
+                                 : launch_walk_vec<DT, false>(a, t, lq, st, n);
 }
 
 hipError_t launch_walk(const Args& a, int32_t* tokens_out, double* logq_out, hipStream_t st) {
-  return a.dtype == kBF16 ? launch_walk_dt<kBF16>(a, tokens_out, logq_out, st)
-                          : launch_walk_dt<kF32>(a, tokens_out, logq_out, st);
+  return a.dtype == kBF16 ? launch_walk_dt<kBF16>(a, tokens_out, logq_out, st, nullptr)
+                          : launch_walk_dt<kF32>(a, tokens_out, logq_out, st, nullptr);
+}
+
+int walk_launches(const Args& a) {
+  int n = 0;
+  const hipError_t e = a.dtype == kBF16 ? launch_walk_dt<kBF16>(a, nullptr, nullptr, nullptr, &n)
+                                        : launch_walk_dt<kF32>(a, nullptr, nullptr, nullptr, &n);
+  return e == hipSuccess ? n : 0;
 }
 
 size_t verify_lds_bytes(int B) { return stream_table_bytes(B); }

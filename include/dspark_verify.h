@@ -197,12 +197,28 @@ dspark_status dspark_verify_noalloc(const dspark_verify_problem* problem, const 
  * anchor_tokens, seed, step; target_logits and draft_tokens are ignored and may be
  * NULL.  tokens_out: device int32 [B, k], -1 past gamma_b; it may be passed as the
  * verify call's draft_tokens.  logq_out: device fp64 [B, k] of log q_j(x_j) (NaN for
- * T_b = 0 and past gamma_b), or NULL.  workspace: as dspark_workspace_bytes(problem).
- * 2k launches on `stream` (slot j needs x_{j-1}).
+ * T_b = 0 and past gamma_b), or NULL.  workspace: as dspark_workspace_bytes(problem);
+ * as for the verifiers, calls that may overlap need workspaces of their own.
+ * Slot j needs x_{j-1}: when the walk's workgroups (one per 256 ids) can all be
+ * resident on the device, one launch runs every slot with grid-wide waits between
+ * them and reads W2 once (a small launch first clears its wait words); otherwise 2k
+ * launches, two per slot (see dspark_draft_launches).  Both give the same outputs.
+ * A wait that expires (possible only if other work holds the device's compute units)
+ * marks the slots from there on invalid: tokens -1, log q NaN.
  */
 dspark_status dspark_draft_sample(const dspark_verify_problem* problem, int32_t* tokens_out,
                                   double* logq_out, void* workspace, size_t workspace_bytes,
                                   void* stream);
+
+/* Launches dspark_draft_sample makes for this problem on the current device: 2 (wait
+ * words cleared, then the one resident launch) or 2k.  The choice depends on V (at
+ * most 512 groups of 256 ids on a 256-CU device), the Markov rank, the dtype, the
+ * draft logits' 16-byte alignment and the device's occupancy; setting
+ * DSPARK_WALK_LAUNCH=separate in the environment forces 2k.  Host only; reads no
+ * device memory.  Errors: DSPARK_ERR_INVALID_ARG (invalid sizes, NULL draft logits
+ * or out), DSPARK_ERR_UNSUPPORTED (Markov rank or alignment), DSPARK_ERR_HIP (device
+ * query failed). */
+dspark_status dspark_draft_launches(const dspark_verify_problem* problem, int32_t* launches);
 
 /*
  * Reduced draft vocabulary [P1 §3 "The Markov fix-up": the drafter scores a reduced

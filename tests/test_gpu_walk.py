@@ -104,3 +104,59 @@ def _subset(wl, ok):
     import dataclasses
     return dataclasses.replace(wl, B=int(ok.sum()), temperature=wl.temperature[ok],
                                num_drafts=None if wl.num_drafts is None else wl.num_drafts[ok])
+
+
+PLAN_CASES = [
+    # (B, k, V, dtype, R (0: no Markov head), greedy_every, ragged counts)
+    (64, 5, 129280, "bf16", 256, 0, False),   # the headline shape
+    (100, 4, 50000, "bf16", 128, 7, True),    # two blocks of streams, mixed greedy, ragged counts
+    (6, 5, 1000, "bf16", 256, 0, False),      # fewer groups than streams
+    (9, 3, 4099, "f32", 64, 4, True),         # rows not 16-byte aligned
+    (16, 5, 3000, "f32", 0, 0, False),        # no Markov head
+]
+
+
+def _plan_inputs(B, k, V, dtype, R, greedy_every, ragged, seed):
+    g = torch.Generator().manual_seed(seed)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kw = dict(draft=(torch.randn(B, k, V, generator=g) * 3.0).to(tdt).to(dev))
+    T = torch.rand(B, generator=g) * 0.4 + 0.6
+    if greedy_every:
+        T[::greedy_every] = 0.0
+    kw["temperature"] = T.to(dev)
+    kw["anchor"] = torch.randint(0, V, (B,), generator=g, dtype=torch.int32).to(dev)
+    if R:
+        kw["W1"] = (torch.randn(V, R, generator=g) * 0.02).to(torch.bfloat16).to(dev)
+        kw["W2t"] = (torch.randn(V, R, generator=g) * 0.02).to(torch.bfloat16).to(dev)
+    if ragged:
+        kw["num_drafts"] = torch.randint(0, k + 1, (B,), generator=g, dtype=torch.int32).to(dev)
+    return kw
+
+
+@pytest.mark.parametrize("B,k,V,dtype,R,greedy_every,ragged", PLAN_CASES)
+def test_walk_launch_plans_agree(mod, monkeypatch, B, k, V, dtype, R, greedy_every, ragged):
+    """The resident walk (one launch for every slot) and the two launches per slot give
+    the same tokens and log q, bit for bit, on two steps."""
+    kw = _plan_inputs(B, k, V, dtype, R, greedy_every, ragged, seed=B * 1000 + V)
+    plan_kw = {n: kw[n] for n in ("num_drafts", "temperature", "W1", "W2t", "anchor") if n in kw}
+    for step in (0, 7):
+        got = {}
+        for plan in ("resident", "separate"):
+            if plan == "separate":
+                monkeypatch.setenv("DSPARK_WALK_LAUNCH", "separate")
+            else:
+                monkeypatch.delenv("DSPARK_WALK_LAUNCH", raising=False)
+            n = mod.draft_launches(kw["draft"], **plan_kw)
+            toks, lq = mod.draft_sample(seed=11, step=step, logq=True, **kw)
+            torch.cuda.synchronize()
+            got[plan] = (n, toks.cpu(), lq.cpu())
+        assert got["resident"][0] == 2, got["resident"][0]
+        assert got["separate"][0] == 2 * k
+        assert torch.equal(got["resident"][1], got["separate"][1]), (step, got["resident"][1], got["separate"][1])
+        torch.testing.assert_close(got["resident"][2], got["separate"][2], rtol=0, atol=0, equal_nan=True)
+        gam = kw["num_drafts"].cpu() if "num_drafts" in kw else torch.full((B,), k)
+        drawn = got["resident"][1]
+        for b in range(B):
+            assert bool((drawn[b, :int(gam[b])] >= 0).all()) and bool((drawn[b, int(gam[b]):] == -1).all())
+        print(f"[walk-plans B={B} k={k} V={V} {dtype} R={R}] step {step}: identical", flush=True)
