@@ -530,9 +530,8 @@ def main() -> int:
         walk_launches = dv.draft_launches(s["draft"], temperature=s["temp"], W1=s["W1"], W2t=s["W2t"],
                                           anchor=s["anchor"])
         walk_alg = 2.0 * V * B * k + 2.0 * R * V + 2.0 * R * B * k   # draft rows once, W2 once, W1 rows
-        # by design: the resident walk reads W2 once, plus the B drawing workgroups' slabs
-        # again after each slot's draws; two launches per slot read W2 in every slot
-        w2_reads = 1.0 + (k - 1) * min(B, (V + 255) // 256) / ((V + 255) // 256) if walk_launches == 2 else float(k)
+        # by design: the resident walk reads W2 once; two launches per slot read it in every slot
+        w2_reads = 1.0 if walk_launches == 2 else float(k)
         walk_read = 2.0 * V * B * k + w2_reads * 2.0 * R * V + 2.0 * R * B * k
         result["draft_walk"] = {
             "ms_per_call": round(walk_ms, 5),

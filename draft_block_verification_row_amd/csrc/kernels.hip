@@ -1170,7 +1170,11 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
 constexpr float kRaceWindow = 0x1.0p-6f;   // log2 units: far above the fp32 ranking error (~1e-5)
 
 __device__ __forceinline__ Top2 top2_empty() { return Top2{-INFINITY, INT_MAX, -INFINITY, INT_MAX}; }
-__device__ __forceinline__ bool top_better(float s, int v, float t, int u) { return s > t || (s == t && v < u); }
+// Bitwise, not short-circuit: the comparisons become lane masks combined on the scalar
+// unit, with no branch.
+__device__ __forceinline__ bool top_better(float s, int v, float t, int u) {
+  return (int)(s > t) | ((int)(s == t) & (int)(v < u));
+}
 // Branch-free (selects only): (-inf, INT_MAX) is never inserted.
 __device__ __forceinline__ void top2_add(Top2& a, float s, int v) {
   const bool b1 = top_better(s, v, a.s1, a.v1);
@@ -1960,6 +1964,7 @@ __device__ __forceinline__ uint2 clock_words(const uint4& x) {
 // nothing the walk draws, so a resident walk computes them while it waits.
 __device__ __forceinline__ void walk_fill_clocks(const Args& a, int j, int r0, int c0, WalkClocks& clk) {
   const int tid = opaque_tid(), n = tid & 15;
+  asm volatile("" : "+v"(c0));   // computed here, not kept from the kernel's start
 #pragma unroll 1
   for (int cc = 0; cc < kWalkChunks; ++cc) {
     const uint32_t b = (uint32_t)min(r0 + cc * kChunk + n, a.B - 1);
@@ -1973,6 +1978,7 @@ __device__ __forceinline__ void walk_fill_clocks(const Args& a, int j, int r0, i
 // window thread t covers there (window start c0), into dst[i][t] (coherent stores).
 __device__ __forceinline__ void walk_clock_chunk(const Args& a, int j, int cc, int c0, uint2* dst) {
   const int tid = opaque_tid(), n = tid & 15;
+  asm volatile("" : "+v"(c0));
   const uint32_t b = (uint32_t)min(cc * kChunk + n, a.B - 1);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -2055,23 +2061,35 @@ __device__ __forceinline__ WalkTop2 walk_top2_4lanes(const WalkCand& c) {
 
 // Group partials (max, sum) and race candidates of slot j for rows r0 .. r0 + 63 of
 // group g, from their draft logits xr and clocks clk; written to tpart / race [g][b].
+// csrc: when not null, the clocks are first copied into clk from there (another
+// workgroup computed them: coherent loads, issued with the block's other loads).
 // Every thread of the workgroup calls it.
 template <int DT, int KS, bool MARKOV, bool VEC>
 __device__ __forceinline__ void walk_block(const Args& a, int g, int j, int r0, const WalkLane& wl,
                                            const Raw16<DT> (&xr)[kWalkChunks], const bf16x8 (&A)[4][KS],
-                                           WalkRowsLds<KS, MARKOV>& L, const WalkClocks& clk) {
+                                           WalkRowsLds<KS, MARKOV>& L, WalkClocks& clk,
+                                           const uint2* csrc = nullptr) {
   const int tid = opaque_tid(), w = tid >> 6, l = tid & 63, n = l & 15, q = l >> 4;
+  uint2 cw[kWalkChunks * 4];
+  if (csrc != nullptr) {   // uniform
+#pragma unroll
+    for (int u = 0; u < kWalkChunks * 4; ++u) cw[u] = ld_c(&csrc[u * kThreads + tid]);
+  }
   if (tid < kWalkRows) {
     const int b = min(r0 + tid, a.B - 1);
     // an absent input reads a stand-in word (the stream's first token slot), replaced
     const int32_t* standin = a.tokens + (size_t)b * a.k;
     const float T = *(a.temperature != nullptr ? a.temperature + b : reinterpret_cast<const float*>(standin));
     // x_{j-1} was drawn by another workgroup (of this launch, or of the previous one)
-    const int pv = j > 0 ? ld_c(a.tokens + (size_t)b * a.k + j - 1) : *(a.anchor != nullptr ? a.anchor + b : standin);
+    const int pv = ld_c(j > 0 ? a.tokens + (size_t)b * a.k + j - 1 : (a.anchor != nullptr ? a.anchor + b : standin));
     const bool has = j > 0 || a.anchor != nullptr;
     L.prev[tid] = (has && pv >= 0 && pv < a.V) ? pv : -1;   // as draft_prev
     const float Tb = a.temperature != nullptr ? T : 1.f;      // as stream_temp
     L.c[tid] = Tb > 0.f ? (float)(kLog2e / (double)Tb) : 1e-30f;
+  }
+  if (csrc != nullptr) {
+#pragma unroll
+    for (int u = 0; u < kWalkChunks * 4; ++u) clk[u >> 2][u & 3][tid] = cw[u];
   }
   __syncthreads();
   if (MARKOV) {   // the block's W1 rows: whole rows per wave instruction, all in flight
@@ -2191,7 +2209,6 @@ __device__ __forceinline__ void walk_pick_body(const Args& a, int b, int j, int3
   const int32_t* standin = a.tokens + (size_t)b * a.k;
   const int graw = *(a.num_drafts != nullptr ? a.num_drafts + b : standin);
   const float traw = *(a.temperature != nullptr ? a.temperature + b : reinterpret_cast<const float*>(standin));
-  const int praw = j > 0 ? ld_c(a.tokens + (size_t)b * a.k + j - 1) : *(a.anchor != nullptr ? a.anchor + b : standin);
   float2 p0 = ld_c(&a.ws.tpart[(size_t)g0 * ND + b]), p1 = ld_c(&a.ws.tpart[(size_t)g1 * ND + b]);
   WalkTop2 t0 = ld_c(&race[(size_t)g0 * ND + b]), t1 = ld_c(&race[(size_t)g1 * ND + b]);
   const int failed = err != nullptr ? ld_c(err) : 0;
@@ -2216,7 +2233,9 @@ __device__ __forceinline__ void walk_pick_body(const Args& a, int b, int j, int3
   int x;
   if (Tf == 0.f) {
     // the group with the largest maximum, then inside it the biased logits in fp64 (the
-    // group's Markov bias from one cooperative pass over its W2t rows)
+    // group's Markov bias from one cooperative pass over its W2t rows); x_{j-1} was
+    // drawn by this launch or the previous one (a coherent load)
+    const int praw = ld_c(j > 0 ? a.tokens + (size_t)b * a.k + j - 1 : (a.anchor != nullptr ? a.anchor + b : standin));
     const int pr = (j > 0 || a.anchor != nullptr) ? praw : -1;
     const int prev = (a.W1 != nullptr && pr >= 0 && pr < a.V) ? pr : -1;
     const size_t esz = DT == kBF16 ? 2 : 4;
@@ -2344,34 +2363,49 @@ __global__ __launch_bounds__(kThreads) void walk_pick_kernel(Args a, int j, int3
 
 // The resident walk's split grid-wide wait: a workgroup announces that its part of a
 // phase is done (walk_arrive), may do work that depends on no other workgroup, then
-// waits until every workgroup has announced (walk_wait).  The last workgroup collects
-// the announcements and writes the go words; waits are bounded as in the fused verify
-// launch (an expired wait sets the error word).
+// waits until every workgroup has announced (walk_wait).  Announcing is an atomic
+// increment of one of kWalkSubs counters of the phase's parity (workgroup g: counter
+// g % kWalkSubs; each on its own line, so that no one address serialises the whole
+// grid's increments); the increment that completes a counter's count increments the
+// parity's top counter, and the one that completes the top count writes the go words,
+// so no workgroup polls the others.  Every workgroup announces every phase once and
+// none can announce phase p + 2 before all have announced p, so after phase
+// p = 2j + 1 or 2j + 2 a counter holds (j + 1) times its workgroup count.  A later
+// announcement by any workgroup begins by waiting for its own stores, so the go words
+// of phase p have landed before those of p + 1 are written.  Waits are bounded as in
+// the fused verify launch (an expired wait sets the error word).
+constexpr int kWalkSubs = 16;
+constexpr int kWalkCountLines = 2 * (kWalkSubs + 1);   // sync lines 1 .. 34 (a line: kSyncStride words)
+
 __device__ __forceinline__ void walk_arrive(const Args& a, int phase) {
   wait_memory();
   __syncthreads();
-  if (opaque_tid() == 0) st_c(&a.ws.sync[kSyncStride * (1 + blockIdx.x)], phase);
+  if (threadIdx.x == 0) {
+    int* sync = a.ws.sync;
+    const int G = (int)gridDim.x, g = (int)blockIdx.x, rounds = (phase + 1) >> 1;
+    const int nsub = G < kWalkSubs ? G : kWalkSubs, sub = g % kWalkSubs;
+    int* base = sync + kSyncStride * (1 + (phase & 1) * (kWalkSubs + 1));
+    const int members = (G - sub + kWalkSubs - 1) / kWalkSubs;
+    if (claim_add(base + kSyncStride * sub) == members * rounds - 1 &&
+        claim_add(base + kSyncStride * kWalkSubs) == nsub * rounds - 1)
+      for (int c = 0; c < kGoCopies; ++c) st_c(&sync[kGoBase + kGoStride * c], phase);
+  }
 }
 
 __device__ __forceinline__ void walk_wait(const Args& a, int phase) {
   int* sync = a.ws.sync;
-  const int g = blockIdx.x, G = gridDim.x;
-  if (g == G - 1) {
-    for (int i = opaque_tid(); i < G; i += kThreads) spin_until_ge(&sync[kSyncStride * (1 + i)], phase, &sync[1]);
-    __syncthreads();
-    if (opaque_tid() < kGoCopies) st_c(&sync[kGoBase + kGoStride * opaque_tid()], phase);
-  } else if (opaque_tid() == 0) {
-    spin_until_ge(&sync[kGoBase + kGoStride * (g % kGoCopies)], phase, &sync[1]);
-  }
+  if (threadIdx.x == 0) spin_until_ge(&sync[kGoBase + kGoStride * (blockIdx.x % kGoCopies)], phase, &sync[1]);
   __syncthreads();
 }
 
-// The go and error words and the arrival words of a G-workgroup resident launch.
+// The go and error words and the first max(G, kWalkCountLines) + 1 lines of counters
+// and arrival words of a G-workgroup resident launch.
 __global__ __launch_bounds__(kThreads) void sync_clear_kernel(int32_t* sync, int G) {
-  const int t = opaque_tid();
-  if (t == 0) st_c(&sync[1], 0);
+  const int t = threadIdx.x;
+  if (t < 4) st_c(&sync[t], 0);
   if (t < kGoCopies) st_c(&sync[kGoBase + kGoStride * t], 0);
-  for (int i = t; i <= G; i += kThreads) st_c(&sync[kSyncStride * i], 0);
+  const int lines = G > kWalkCountLines ? G : kWalkCountLines;
+  for (int i = t; i <= lines; i += kThreads) st_c(&sync[kSyncStride * i], 0);
 }
 
 template <int KS, bool MARKOV>
@@ -2388,7 +2422,7 @@ __host__ __device__ constexpr size_t walk_lds_bytes() {
 // for slot j + 1 (their first block of rows, into the clock region, one buffer per
 // slot parity: a slot's buffer is written only after every reader of its previous
 // contents has passed a wait) and then their own; everyone waits for the draws
-// (phase 2j + 2).  The last workgroup collects the arrivals.
+// (phase 2j + 2).
 template <int DT, int KS, bool MARKOV, bool VEC>
 __global__ __launch_bounds__(kThreads, 2) void walk_fused_kernel(Args a, int32_t* tokens_out, double* logq_out) {
   __shared__ __align__(16) char lds[walk_lds_bytes<KS, MARKOV>()];
@@ -2399,7 +2433,7 @@ __global__ __launch_bounds__(kThreads, 2) void walk_fused_kernel(Args a, int32_t
   const int tid = opaque_tid();
   const int NP = a.B < G ? a.B : G;   // drawing workgroups
   const int NO = G - NP;              // the others
-  const bool picker = g < NP, master = g == G - 1;
+  const bool picker = g < NP;
   // [2][NP][kWalkChunks][4][kThreads]: the drawing workgroups' clocks by slot parity
   uint2* const pclk = a.ws.clk;
   auto pbuf = [&](int slot, int pg) { return pclk + ((size_t)(slot & 1) * NP + pg) * kWalkChunks * 4 * kThreads; };
@@ -2410,19 +2444,14 @@ __global__ __launch_bounds__(kThreads, 2) void walk_fused_kernel(Args a, int32_t
   if (MARKOV) load_w2_slab<KS, VEC>(a, g * kGroup + (tid >> 6) * kWaveCols, tid & 15, (tid & 63) >> 4, A);
   walk_fill_clocks(a, 0, 0, wl.c0, clk);
   for (int j = 0; j < a.k; ++j) {
-    if (picker && j > 0 && NO > 0) {   // this slot's clocks, computed by the others
-      const uint2* src = pbuf(j, g);
-#pragma unroll
-      for (int cc = 0; cc < kWalkChunks; ++cc)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) clk[cc][i][tid] = ld_c(&src[(cc * 4 + i) * kThreads + tid]);
-    }
     for (int r0 = 0; r0 < a.B; r0 += kWalkRows) {
       if (r0 > 0) {
         walk_load_rows<DT, VEC>(a, j, r0, wl.c0, xr);
         walk_fill_clocks(a, j, r0, wl.c0, clk);
       }
-      walk_block<DT, KS, MARKOV, VEC>(a, g, j, r0, wl, xr, A, L, clk);
+      // the first block's clocks of a drawing workgroup were computed by the others
+      walk_block<DT, KS, MARKOV, VEC>(a, g, j, r0, wl, xr, A, L, clk,
+                                      (picker && j > 0 && NO > 0 && r0 == 0) ? pbuf(j, g) : nullptr);
     }
     const int ph1 = 2 * j + 1, ph2 = 2 * j + 2;
     const bool last = j + 1 == a.k;
@@ -2435,26 +2464,20 @@ __global__ __launch_bounds__(kThreads, 2) void walk_fused_kernel(Args a, int32_t
       }
       if (!last) {
         walk_arrive(a, ph2);
-        // the draws took the slab's registers: it comes back while the others finish
-        // (W2 is read again by the drawing workgroups only)
-        if (MARKOV) load_w2_slab<KS, VEC>(a, g * kGroup + (tid >> 6) * kWaveCols, tid & 15, (tid & 63) >> 4, A);
         walk_load_rows<DT, VEC>(a, j + 1, 0, wl.c0, xr);
         if (NO == 0) walk_fill_clocks(a, j + 1, 0, wl.c0, clk);
         walk_wait(a, ph2);
       }
-    } else {
-      if (master) walk_wait(a, ph1);
-      if (!last) {
-        // a share of the drawing workgroups' clocks (task t: workgroup t / 4, chunk t % 4)
-        for (int t = g - NP; t < NP * kWalkChunks; t += NO) {
-          const int pg = t / kWalkChunks, cc = t % kWalkChunks;
-          walk_clock_chunk(a, j + 1, cc, walk_lane<VEC>(a, pg).c0, pbuf(j + 1, pg) + cc * 4 * kThreads);
-        }
-        walk_arrive(a, ph2);
-        walk_load_rows<DT, VEC>(a, j + 1, 0, wl.c0, xr);
-        walk_fill_clocks(a, j + 1, 0, wl.c0, clk);
-        walk_wait(a, ph2);
+    } else if (!last) {
+      // a share of the drawing workgroups' clocks (task t: workgroup t / 4, chunk t % 4)
+      for (int t = g - NP; t < NP * kWalkChunks; t += NO) {
+        const int pg = t / kWalkChunks, cc = t % kWalkChunks;
+        walk_clock_chunk(a, j + 1, cc, walk_lane<VEC>(a, pg).c0, pbuf(j + 1, pg) + cc * 4 * kThreads);
       }
+      walk_arrive(a, ph2);
+      walk_load_rows<DT, VEC>(a, j + 1, 0, wl.c0, xr);
+      walk_fill_clocks(a, j + 1, 0, wl.c0, clk);
+      walk_wait(a, ph2);
     }
   }
 }

@@ -22,6 +22,7 @@ K_SYNC_STRIDE, K_MAX_FUSED, K_GO_COPIES, K_GO_STRIDE = 16, 2048, 16, 32
 K_GO_BASE = K_SYNC_STRIDE * (1 + K_MAX_FUSED)
 K_SYNC_INTS = K_GO_BASE + K_GO_COPIES * K_GO_STRIDE
 K_WALK_CLOCK_BYTES = 64 * 256 * 2
+K_WALK_SUBS = 16
 TID = np.arange(K_THREADS)
 
 
@@ -59,12 +60,14 @@ class Walk:
         self.drawn = np.where(np.arange(k)[None, :] < gam[:, None], rng.integers(0, V, size=(B, k)), -1)
         self.anchor = rng.integers(-1, V, size=B) if anchors else None
         NG, ND, NT = self.NG, B * k, B * (k + 1)
+        # race: the walk's 32-byte candidate records in a region laid out for the
+        # verifiers' 16-byte ones or these, whichever is larger
         clk_bytes = max(B * NG * K_GROUP * 2, 2 * min(B, NG) * K_WALK_CLOCK_BYTES)
         self.mem = Mem(dict(
             draft=ND * V, tokens=ND, logq=ND,
             num_drafts=None if counts is None else B, temperature=B if temps else None,
             anchor=B if anchors else None, W1=V * R if R else None, W2t=V * R if R else None,
-            tpart=NG * NT, race=NG * ND, clk=clk_bytes // 8, sync=K_SYNC_INTS))
+            tpart=NG * NT, race=max(ND * NG * 16, B * NG * 32) // 32, clk=clk_bytes // 8, sync=K_SYNC_INTS))
 
     # window of each thread in group g
     def lane(self, g):
@@ -197,12 +200,22 @@ def replay_resident(p: Walk, greedy=False):
     NP, NO = min(B, G), G - min(B, G)
     slot_words = K_WALK_CHUNKS * 4 * K_THREADS
     # the wait words cleared before the launch
-    p.mem.at("sync", 1)
+    p.mem.at("sync", np.arange(4))
     p.mem.at("sync", K_GO_BASE + K_GO_STRIDE * np.arange(K_GO_COPIES))
-    p.mem.at("sync", K_SYNC_STRIDE * np.arange(G + 1))
+    p.mem.at("sync", K_SYNC_STRIDE * np.arange(max(G, 2 * (K_WALK_SUBS + 1)) + 1))
+
+    def arrive(phase):   # a sub-counter, the parity's top counter, then every go copy
+        base = K_SYNC_STRIDE * (1 + (phase & 1) * (K_WALK_SUBS + 1))
+        p.mem.at("sync", base + K_SYNC_STRIDE * np.arange(K_WALK_SUBS + 1))
+        p.mem.at("sync", K_GO_BASE + K_GO_STRIDE * np.arange(K_GO_COPIES))
+
+    def wait(g):
+        p.mem.at("sync", K_GO_BASE + K_GO_STRIDE * (g % K_GO_COPIES))
+        p.mem.at("sync", 1)
+
     for g in range(G):
         c0 = p.lane(g)
-        picker, master = g < NP, g == G - 1
+        picker = g < NP
         p.load_rows(0, 0, c0)
         p.slab(g)
         for j in range(k):
@@ -213,26 +226,24 @@ def replay_resident(p: Walk, greedy=False):
                     p.load_rows(j, r0, c0)
                 p.block(g, j, r0)
             last = j + 1 == k
-            p.mem.at("sync", K_SYNC_STRIDE * (1 + g))            # arrival
-            if picker or master:
-                if master:
-                    p.mem.at("sync", K_SYNC_STRIDE * (1 + np.arange(G)))
-                    p.mem.at("sync", K_GO_BASE + K_GO_STRIDE * np.arange(K_GO_COPIES))
-                else:
-                    p.mem.at("sync", K_GO_BASE + K_GO_STRIDE * (g % K_GO_COPIES))
+            arrive(2 * j + 1)
             if picker:
+                wait(g)
                 for b in range(g, B, G):
                     p.pick(b, j, NG, greedy)
                 if not last:
-                    p.slab(g)
+                    arrive(2 * j + 2)
                     p.load_rows(j + 1, 0, c0)
+                    wait(g)
             elif not last:
                 for t in range(g - NP, NP * K_WALK_CHUNKS, NO):
                     pg, cc = divmod(t, K_WALK_CHUNKS)
                     base = ((j + 1) & 1) * NP + pg
                     p.mem.at("clk", base * slot_words + cc * 4 * K_THREADS + TID[None, :]
                              + K_THREADS * np.arange(4)[:, None])
+                arrive(2 * j + 2)
                 p.load_rows(j + 1, 0, c0)
+                wait(g)
 
 
 def replay_separate(p: Walk, greedy=False):
