@@ -287,22 +287,25 @@ struct Workspace {
   uint2* clk;         // [B][NG*64]      race clocks of sampled streams: log2 E in units of 2^-10 as
                       //                 int16, four ids to a uint2 (ids 4i .. 4i+3 of the stream);
                       //                 the resident walk: its drawing workgroups' clocks
-  int32_t* sync;      // [kSyncInts]     fused launches: go word at [0], error word at [1], workgroup g's
-                      //                 arrival word at [kSyncStride (1 + g)], go-word copies from
-                      //                 [kGoBase]; cleared by pack (verify) or sync_clear_kernel (walk)
+  int32_t* sync;      // [kSyncInts]     resident launches: error word at [1], arrival counters on
+                      //                 lines 1 .. kGridCountLines, go-word copies from [kGoBase];
+                      //                 cleared by pack (verify) or sync_clear_kernel (walk)
 };
 
-// The fused verify launch's barrier words: the go word at [0] and the error word at
-// [1], workgroup g's arrival word at [kSyncStride (1 + g)] (one 64-byte line each),
-// then kGoCopies copies of the go word, one 128-byte line apart (workgroup g waits on
-// copy g % kGoCopies, so that hundreds of waiting workgroups do not all poll one line).
 // Clock bytes of one resident-walk workgroup's block of rows (64 rows x 256 ids, int16).
 constexpr size_t kWalkClockBytes = 64 * 256 * 2;
+// The resident launches' wait words: the error word at [1]; the arrival counters,
+// kGridSubs per phase parity and a top counter each, one 64-byte line apiece (lines
+// 1 .. kGridCountLines of kSyncStride words); then kGoCopies copies of the go word, one
+// 128-byte line apart (workgroup g waits on copy g % kGoCopies, so that hundreds of
+// waiting workgroups do not all poll one line).
 constexpr int kSyncStride = 16;
-constexpr int kMaxFusedGrid = 2048;
+constexpr int kGridSubs = 16;
+constexpr int kGridCountLines = 2 * (kGridSubs + 1);
+constexpr int kMaxFusedGrid = 2048;   // workgroups of a resident launch, at most
 constexpr int kGoCopies = 16;
 constexpr int kGoStride = 32;
-constexpr int kGoBase = kSyncStride * (1 + kMaxFusedGrid);
+constexpr int kGoBase = kSyncStride * (1 + kGridCountLines);
 constexpr int kSyncInts = kGoBase + kGoCopies * kGoStride;
 
 struct Args {

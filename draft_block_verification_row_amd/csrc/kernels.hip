@@ -318,10 +318,10 @@ __global__ __launch_bounds__(64) void pack_kernel(Args a) {
   const int c = blockIdx.x, l = threadIdx.x, n = l & 15, q = l >> 4;
   if (c == 0 && l < 2) st_c(&a.ws.nitems[l], 0);
   if (c == 0 && l < kQueues) st_c(&a.ws.nitems[kQueueStride * (1 + l)], 0);
-  if (a.fused_grid > 0) {   // the fused launch's go and error words, and every arrival word
-    if (c == 0 && l == 0) st_c(&a.ws.sync[1], 0);
-    if (c == 0 && l < kGoCopies) st_c(&a.ws.sync[kGoBase + kGoStride * l], 0);
-    for (int i = c * 64 + l; i <= a.fused_grid; i += gridDim.x * 64) st_c(&a.ws.sync[kSyncStride * i], 0);
+  if (a.fused_grid > 0 && c == 0) {   // the fused launch's go and error words and counters
+    if (l < 4) st_c(&a.ws.sync[l], 0);
+    if (l < kGoCopies) st_c(&a.ws.sync[kGoBase + kGoStride * l], 0);
+    for (int i = l; i <= kGridCountLines; i += 64) st_c(&a.ws.sync[kSyncStride * i], 0);
   }
   if (a.W1 == nullptr) return;
   const int ND = a.B * a.k;
@@ -1814,20 +1814,42 @@ __device__ __forceinline__ void spin_until_ge(int* p, int v, int* err) {
   }
 }
 
-__device__ __forceinline__ void grid_barrier(const Args& a, int phase) {
+// A workgroup announces that its part of a phase is done (grid_arrive), may do work
+// that depends on no other workgroup, then waits until every workgroup has announced
+// (grid_wait).  Announcing is an atomic increment of one of kGridSubs counters of the
+// phase's parity (workgroup g: counter g % kGridSubs, each on its own line, so that
+// no one address serialises the whole grid's increments); the increment that
+// completes a counter's count increments the parity's top counter, and the one that
+// completes the top count writes the go words, so no workgroup polls the others.
+// Every workgroup announces every phase once and none can announce phase p + 2
+// before all have announced p, so after phase p = 2j + 1 or 2j + 2 a counter holds
+// (j + 1) times its workgroup count.  A later announcement by any workgroup begins by
+// waiting for its own stores, so the go words of phase p have landed before those of
+// p + 1 are written.
+__device__ __forceinline__ void grid_arrive(const Args& a, int phase) {
   wait_memory();
   __syncthreads();
-  int* sync = a.ws.sync;
-  const int g = blockIdx.x, G = gridDim.x;
-  if (threadIdx.x == 0) st_c(&sync[kSyncStride * (1 + g)], phase);
-  if (g == 0) {
-    for (int i = threadIdx.x; i < G; i += kThreads) spin_until_ge(&sync[kSyncStride * (1 + i)], phase, &sync[1]);
-    __syncthreads();
-    if (threadIdx.x < kGoCopies) st_c(&sync[kGoBase + kGoStride * threadIdx.x], phase);
-  } else if (threadIdx.x == 0) {
-    spin_until_ge(&sync[kGoBase + kGoStride * (g % kGoCopies)], phase, &sync[1]);
+  if (threadIdx.x == 0) {
+    int* sync = a.ws.sync;
+    const int G = (int)gridDim.x, g = (int)blockIdx.x, rounds = (phase + 1) >> 1;
+    const int nsub = G < kGridSubs ? G : kGridSubs, sub = g % kGridSubs;
+    int* base = sync + kSyncStride * (1 + (phase & 1) * (kGridSubs + 1));
+    const int members = (G - sub + kGridSubs - 1) / kGridSubs;
+    if (claim_add(base + kSyncStride * sub) == members * rounds - 1 &&
+        claim_add(base + kSyncStride * kGridSubs) == nsub * rounds - 1)
+      for (int c = 0; c < kGoCopies; ++c) st_c(&sync[kGoBase + kGoStride * c], phase);
   }
+}
+
+__device__ __forceinline__ void grid_wait(const Args& a, int phase) {
+  int* sync = a.ws.sync;
+  if (threadIdx.x == 0) spin_until_ge(&sync[kGoBase + kGoStride * (blockIdx.x % kGoCopies)], phase, &sync[1]);
   __syncthreads();
+}
+
+__device__ __forceinline__ void grid_barrier(const Args& a, int phase) {
+  grid_arrive(a, phase);
+  grid_wait(a, phase);
 }
 
 template <int KS, bool MARKOV>
@@ -2361,51 +2383,12 @@ __global__ __launch_bounds__(kThreads) void walk_pick_kernel(Args a, int j, int3
   walk_pick_body<DT, KS>(a, blockIdx.x, j, tokens_out, logq_out, L, nullptr);
 }
 
-// The resident walk's split grid-wide wait: a workgroup announces that its part of a
-// phase is done (walk_arrive), may do work that depends on no other workgroup, then
-// waits until every workgroup has announced (walk_wait).  Announcing is an atomic
-// increment of one of kWalkSubs counters of the phase's parity (workgroup g: counter
-// g % kWalkSubs; each on its own line, so that no one address serialises the whole
-// grid's increments); the increment that completes a counter's count increments the
-// parity's top counter, and the one that completes the top count writes the go words,
-// so no workgroup polls the others.  Every workgroup announces every phase once and
-// none can announce phase p + 2 before all have announced p, so after phase
-// p = 2j + 1 or 2j + 2 a counter holds (j + 1) times its workgroup count.  A later
-// announcement by any workgroup begins by waiting for its own stores, so the go words
-// of phase p have landed before those of p + 1 are written.  Waits are bounded as in
-// the fused verify launch (an expired wait sets the error word).
-constexpr int kWalkSubs = 16;
-constexpr int kWalkCountLines = 2 * (kWalkSubs + 1);   // sync lines 1 .. 34 (a line: kSyncStride words)
-
-__device__ __forceinline__ void walk_arrive(const Args& a, int phase) {
-  wait_memory();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int* sync = a.ws.sync;
-    const int G = (int)gridDim.x, g = (int)blockIdx.x, rounds = (phase + 1) >> 1;
-    const int nsub = G < kWalkSubs ? G : kWalkSubs, sub = g % kWalkSubs;
-    int* base = sync + kSyncStride * (1 + (phase & 1) * (kWalkSubs + 1));
-    const int members = (G - sub + kWalkSubs - 1) / kWalkSubs;
-    if (claim_add(base + kSyncStride * sub) == members * rounds - 1 &&
-        claim_add(base + kSyncStride * kWalkSubs) == nsub * rounds - 1)
-      for (int c = 0; c < kGoCopies; ++c) st_c(&sync[kGoBase + kGoStride * c], phase);
-  }
-}
-
-__device__ __forceinline__ void walk_wait(const Args& a, int phase) {
-  int* sync = a.ws.sync;
-  if (threadIdx.x == 0) spin_until_ge(&sync[kGoBase + kGoStride * (blockIdx.x % kGoCopies)], phase, &sync[1]);
-  __syncthreads();
-}
-
-// The go and error words and the first max(G, kWalkCountLines) + 1 lines of counters
-// and arrival words of a G-workgroup resident launch.
-__global__ __launch_bounds__(kThreads) void sync_clear_kernel(int32_t* sync, int G) {
+// The go and error words and the counter lines of a resident launch.
+__global__ __launch_bounds__(kThreads) void sync_clear_kernel(int32_t* sync) {
   const int t = threadIdx.x;
   if (t < 4) st_c(&sync[t], 0);
   if (t < kGoCopies) st_c(&sync[kGoBase + kGoStride * t], 0);
-  const int lines = G > kWalkCountLines ? G : kWalkCountLines;
-  for (int i = t; i <= lines; i += kThreads) st_c(&sync[kSyncStride * i], 0);
+  for (int i = t; i <= kGridCountLines; i += kThreads) st_c(&sync[kSyncStride * i], 0);
 }
 
 template <int KS, bool MARKOV>
@@ -2455,18 +2438,18 @@ __global__ __launch_bounds__(kThreads, 2) void walk_fused_kernel(Args a, int32_t
     }
     const int ph1 = 2 * j + 1, ph2 = 2 * j + 2;
     const bool last = j + 1 == a.k;
-    walk_arrive(a, ph1);
+    grid_arrive(a, ph1);
     if (picker) {
-      walk_wait(a, ph1);
+      grid_wait(a, ph1);
       for (int b = g; b < a.B; b += G) {
         walk_pick_body<DT, KS>(a, b, j, tokens_out, logq_out, P, &a.ws.sync[1]);
         __syncthreads();
       }
       if (!last) {
-        walk_arrive(a, ph2);
+        grid_arrive(a, ph2);
         walk_load_rows<DT, VEC>(a, j + 1, 0, wl.c0, xr);
         if (NO == 0) walk_fill_clocks(a, j + 1, 0, wl.c0, clk);
-        walk_wait(a, ph2);
+        grid_wait(a, ph2);
       }
     } else if (!last) {
       // a share of the drawing workgroups' clocks (task t: workgroup t / 4, chunk t % 4)
@@ -2474,10 +2457,10 @@ __global__ __launch_bounds__(kThreads, 2) void walk_fused_kernel(Args a, int32_t
         const int pg = t / kWalkChunks, cc = t % kWalkChunks;
         walk_clock_chunk(a, j + 1, cc, walk_lane<VEC>(a, pg).c0, pbuf(j + 1, pg) + cc * 4 * kThreads);
       }
-      walk_arrive(a, ph2);
+      grid_arrive(a, ph2);
       walk_load_rows<DT, VEC>(a, j + 1, 0, wl.c0, xr);
       walk_fill_clocks(a, j + 1, 0, wl.c0, clk);
-      walk_wait(a, ph2);
+      grid_wait(a, ph2);
     }
   }
 }
@@ -2834,7 +2817,7 @@ static hipError_t launch_walk_t(const Args& a, int32_t* tokens_out, double* logq
     // the drawing workgroups' clocks
     if (a.ws.sync == nullptr || a.ws.clk == nullptr || a.ws.tpart == nullptr || a.ws.race == nullptr)
       return hipErrorInvalidValue;
-    hipLaunchKernelGGL(sync_clear_kernel, dim3(1), dim3(kThreads), 0, st, a.ws.sync, G);
+    hipLaunchKernelGGL(sync_clear_kernel, dim3(1), dim3(kThreads), 0, st, a.ws.sync);
     hipLaunchKernelGGL((walk_fused_kernel<DT, KS, MARKOV, VEC>), dim3(G), dim3(kThreads), 0, st, a, tokens_out,
                        logq_out);
     return hipGetLastError();

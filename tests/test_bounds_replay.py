@@ -24,7 +24,10 @@ K_GROUP, K_WAVE_COLS, K_WAVES, K_THREADS, K_CHUNK, K_MAX_K = 256, 64, 4, 256, 16
 K_SCAN_ROWS, K_SCAN_GROUPS, K_LOADS = 6, 256, 8
 K_STAGE_ITER = K_SCAN_ROWS * K_SCAN_GROUPS // K_THREADS
 K_QUEUES, K_QUEUE_STRIDE = 8, 32
-K_SYNC_STRIDE, K_MAX_FUSED = 16, 2048
+K_SYNC_STRIDE, K_GRID_SUBS, K_GO_COPIES, K_GO_STRIDE = 16, 16, 16, 32
+K_GRID_COUNT_LINES = 2 * (K_GRID_SUBS + 1)
+K_GO_BASE = K_SYNC_STRIDE * (1 + K_GRID_COUNT_LINES)
+K_SYNC_INTS = K_GO_BASE + K_GO_COPIES * K_GO_STRIDE
 
 
 class Mem:
@@ -66,7 +69,7 @@ class Problem:
             tpart=self.NG * self.NT, dpart=self.NG * self.ND, wgrp=self.NG * self.ND,
             tm=self.NT, tl2s=self.NT, dm=self.ND, dl2s=self.ND, logP=self.NT, lpx=self.ND, lqx=self.ND,
             info=4 * B, info2=4 * B, rowmask=B, items=self.ND, nitems=K_QUEUE_STRIDE * (1 + K_QUEUES),
-            btile=tiles * 8 * 64, race=self.NG * self.ND, sync=K_SYNC_STRIDE * (1 + K_MAX_FUSED),
+            btile=tiles * 8 * 64, race=self.NG * self.ND, sync=K_SYNC_INTS,
             accepted_len=B, out_tokens=self.NT, diag=self.NT * 5))
 
     # the device's per-stream readers ---------------------------------------------
@@ -120,10 +123,12 @@ def replay_pack(p: Problem, fused_grid: int):
                 p.mem.at("nitems", l)
             if c == 0 and l < K_QUEUES:
                 p.mem.at("nitems", K_QUEUE_STRIDE * (1 + l))
-            if fused_grid > 0:
-                if c == 0 and l == 0:
-                    p.mem.at("sync", 1)
-                for i in range(c * 64 + l, fused_grid + 1, nchd * 64):
+            if fused_grid > 0 and c == 0:   # error word, counters, go copies
+                if l < 4:
+                    p.mem.at("sync", l)
+                if l < K_GO_COPIES:
+                    p.mem.at("sync", K_GO_BASE + K_GO_STRIDE * l)
+                for i in range(l, K_GRID_COUNT_LINES + 1, 64):
                     p.mem.at("sync", K_SYNC_STRIDE * i)
             if p.R == 0:
                 continue

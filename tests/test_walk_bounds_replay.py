@@ -18,11 +18,12 @@ import pytest
 
 K_GROUP, K_WAVE_COLS, K_THREADS, K_CHUNK, K_WAVES = 256, 64, 256, 16, 4
 K_WALK_ROWS, K_WALK_CHUNKS = 64, 4
-K_SYNC_STRIDE, K_MAX_FUSED, K_GO_COPIES, K_GO_STRIDE = 16, 2048, 16, 32
-K_GO_BASE = K_SYNC_STRIDE * (1 + K_MAX_FUSED)
+K_SYNC_STRIDE, K_GO_COPIES, K_GO_STRIDE = 16, 16, 32
+K_WALK_SUBS = 16
+K_GRID_COUNT_LINES = 2 * (K_WALK_SUBS + 1)
+K_GO_BASE = K_SYNC_STRIDE * (1 + K_GRID_COUNT_LINES)
 K_SYNC_INTS = K_GO_BASE + K_GO_COPIES * K_GO_STRIDE
 K_WALK_CLOCK_BYTES = 64 * 256 * 2
-K_WALK_SUBS = 16
 TID = np.arange(K_THREADS)
 
 
@@ -202,7 +203,7 @@ def replay_resident(p: Walk, greedy=False):
     # the wait words cleared before the launch
     p.mem.at("sync", np.arange(4))
     p.mem.at("sync", K_GO_BASE + K_GO_STRIDE * np.arange(K_GO_COPIES))
-    p.mem.at("sync", K_SYNC_STRIDE * np.arange(max(G, 2 * (K_WALK_SUBS + 1)) + 1))
+    p.mem.at("sync", K_SYNC_STRIDE * np.arange(K_GRID_COUNT_LINES + 1))
 
     def arrive(phase):   # a sub-counter, the parity's top counter, then every go copy
         base = K_SYNC_STRIDE * (1 + (phase & 1) * (K_WALK_SUBS + 1))
