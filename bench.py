@@ -37,11 +37,11 @@ HBM_PEAK_GBS = 8000.0
 STAGE_NAMES = ["pack W1 tiles", "pass1 row statistics", "scan", "pass2 residual masses", "finalize/sampler"]
 
 # HBM traffic of one fused verify launch at this workload, from two rocprofv3 --pmc runs
-# (FETCH_SIZE, then WRITE_SIZE; profiles/verify_fused_headline_b64_k5_v129280_hbm_bytes.md),
+# (FETCH_SIZE, then WRITE_SIZE; profiles/verify_and_walk_headline_b64_k5_v129280_hbm_bytes.md),
 # each scaled by what the same counter reads for a plain device copy of known size.
 # Valid only for the kernel sources it was measured on (hash below); otherwise null.
-FUSED_TRAFFIC = {"src_sha256_16": "92e84a609f7de20c", "fetch_bytes": 151113.4 * 1024 * 2.0,
-                 "write_bytes": 21703.0 * 1024 * 1.0}
+FUSED_TRAFFIC = {"src_sha256_16": "ba41b28e263557b1", "fetch_bytes": 150993.3 * 1024 * 2.0,
+                 "write_bytes": 22212.1 * 1024 * 1.0}
 
 
 def kernel_src_hash() -> str:
