@@ -50,3 +50,24 @@ def oracle_steps(name, method, steps, B=None, num_drafts=None):
         return [_one(j) for j in jobs]
     with ProcessPoolExecutor(n, mp_context=mp.get_context("spawn"), initializer=_single_threaded) as ex:
         return list(ex.map(_one, jobs))
+
+
+
+def _walk(args):
+    name, step = args
+    from oracle import dspark as odsp
+    wl = _workload(name, None)
+    o = odsp.draft_walk(wl.draft, wl.dtype, wl.temperature, wl.anchor, wl.W1, wl.W2t, num_drafts=wl.num_drafts,
+                        seed=wl.seed, step=step)
+    return {k: o[k] for k in ("tokens", "logq", "margin")}
+
+
+def walk_steps(name, steps):
+    """oracle.draft_walk of workload ``name`` at every step, one worker per step."""
+    steps = list(steps)
+    jobs = [(name, s) for s in steps]
+    n = min(workers(), len(jobs))
+    if n <= 1:
+        return [_walk(j) for j in jobs]
+    with ProcessPoolExecutor(n, mp_context=mp.get_context("spawn"), initializer=_single_threaded) as ex:
+        return list(ex.map(_walk, jobs))

@@ -4,7 +4,8 @@ verifier (more than 10^4 decisions, so the near-decision budget of 10^-4 is enfo
 without a floor), the headline shape without the Markov head, the over-long drafts
 (B=64, k=9) over 5 steps, and the adaptive ragged configuration at its full B=256:
 confidence head -> per-stream counts -> ragged block verification, and confidence
-head -> batch scheduler -> ragged block verification."""
+head -> batch scheduler -> ragged block verification; and the drafter's walk at the
+headline shape (the resident launch) over 4 steps."""
 import numpy as np
 import pytest
 import torch
@@ -13,7 +14,7 @@ import workloads
 from oracle import dspark as odsp
 from oracle import schedule as osch
 from tests import harness as H
-from tests.oracle_pool import oracle_steps
+from tests.oracle_pool import oracle_steps, walk_steps
 
 pytestmark = pytest.mark.gpu
 
@@ -112,3 +113,35 @@ def test_scheduled_ragged_full_batch(mod):
     print(f"[c5 scheduled B=256] m={ref['m']} total={int(total.item())} "
           f"n histogram {np.bincount(n_g, minlength=6).tolist()} {t.summary()}", flush=True)
     H.assert_clean(t)
+
+
+def test_walk_headline_shape(mod):
+    """The drafter's Markov walk at B=64, k=5, V=129280, bf16, rank 256 (one resident
+    launch for the five slots): tokens bit-exact except on streams whose smallest race
+    margin in the oracle is below the near-decision threshold; log q within tolerance."""
+    wl = workloads.make("h")
+    dev = H.to_dev(wl)
+    assert mod.draft_launches(dev["draft"], temperature=dev["temperature"], W1=dev["W1"], W2t=dev["W2t"],
+                              anchor=dev["anchor"]) == 2
+    steps = range(4)
+    got = []
+    for s in steps:
+        toks, lq = mod.draft_sample(dev["draft"], temperature=dev["temperature"], W1=dev["W1"], W2t=dev["W2t"],
+                                    anchor=dev["anchor"], seed=wl.seed, step=s, logq=True)
+        torch.cuda.synchronize()
+        got.append((toks.cpu().numpy(), lq.cpu().numpy()))
+    del dev
+    draws = near = 0
+    worst = 0.0
+    for s, (g_t, g_lq), o in zip(steps, got, walk_steps("h", steps)):
+        for b in range(wl.B):
+            draws += wl.k
+            if o["margin"][b] < H.NEAR:
+                near += 1
+                continue
+            assert np.array_equal(g_t[b], o["tokens"][b]), (s, b, g_t[b], o["tokens"][b])
+            err = float(np.max(np.abs(g_lq[b] - o["logq"][b])))
+            worst = max(worst, err)
+            assert err <= H.TOL_LOGPROB, (s, b, g_lq[b], o["logq"][b])
+    print(f"[walk-h] draws={draws} near_streams={near} max|dlogq|={worst:.2e}", flush=True)
+    assert near <= max(1, int(1e-4 * draws))
