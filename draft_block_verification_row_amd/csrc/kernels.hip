@@ -1389,6 +1389,15 @@ __device__ __forceinline__ void pass2_body(const Args& a, int g, Pass2Lds& L, bf
   fetch(rows_of(1), tr1, dr1);
   const int nch = (NV + kChunk - 1) / kChunk;
   auto step = [&](int c, Raw16<DT>& tb, Raw16<DT>& db) {
+    // Two workgroups share a CU and run the same number of chunks; the older one's waves
+    // win the issue arbitration and finish first, leaving the other to finish alone.
+    // Waves take a priority that falls with each chunk done, so the one behind catches up.
+    // (levels 3, 2, 1, 0 over the first chunks, so that they differ from the start)
+    const int lvl = c;   // uniform
+    if (lvl == 0) __builtin_amdgcn_s_setprio(3);
+    else if (lvl == 1) __builtin_amdgcn_s_setprio(2);
+    else if (lvl == 2) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
     store_words(c + 2);   // loaded a chunk ago: the registers are free for the products
     if (MARKOV) {
       __syncthreads();
@@ -1876,15 +1885,15 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(Args a) {
   const bool spare = G > nscan;
   if (g < a.B) {
     // a workgroup with streams to scan gives its slab's registers to the scan and loads
-    // the slab again afterwards (at B = 64 of 505 groups: 8 MB of W2); the others keep
-    // theirs through phase 2
+    // the slab again afterwards (at B = 64 of 505 groups: 8 MB of W2), while it waits for
+    // the others; the others keep theirs through phase 2
     for (int b = g; b < a.B; b += G) {
       scan_body<DT>(a, b, *reinterpret_cast<ScanPhaseLds*>(lds), has_table ? stream_table_T(a, table) : nullptr,
                     has_table ? stream_table_gam(a, table) : nullptr);
       __syncthreads();
     }
     if (!spare) clock_rows(a, g, G);
-    grid_barrier(a, 2);
+    grid_arrive(a, 2);
     if (MARKOV) {   // A is defined on every path here, so the old slab is dead during the scan
       if (g < a.NG) {
         const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
@@ -1896,6 +1905,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(Args a) {
           for (int kk = 0; kk < KS; ++kk) A[s4][kk] = zero_bf16x8();
       }
     }
+    grid_wait(a, 2);
   } else {
     clock_rows(a, g - nscan, G - nscan);
     grid_barrier(a, 2);
@@ -2016,23 +2026,26 @@ struct WalkCand {
   int32_t v;
   double y;
 };
+// (Scores are formed in units of 2^-10, x (1024 c) - q, and scaled back once: scaling by
+// a power of two commutes with the rounding, so the result is bit for bit the same.)
 template <int DT>
 __device__ __forceinline__ WalkCand walk_race16(const float (&x)[16], const float (&bias)[16], const Raw16<DT>& d,
                                                 const uint2 (&L)[4], float c, int c0) {
   float best = -INFINITY, bd = 0.f, bb = 0.f;
   int bv = INT_MAX;
+  const float c10 = c * 1024.f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const uint32_t word = (e & 2) ? L[e >> 2].y : L[e >> 2].x;
     const int q = (e & 1) ? ((int32_t)word >> 16) : ((int32_t)(word << 16) >> 16);
-    const float sc = fmaf(x[e], c, -(float)q * 0x1.0p-10f);
+    const float sc = fmaf(x[e], c10, -(float)q);
     const bool better = sc > best;
     best = better ? sc : best;
     bv = better ? c0 + e : bv;
     bd = better ? raw_elem<DT>(d, e) : bd;
     bb = better ? bias[e] : bb;
   }
-  return WalkCand{best, best > -INFINITY ? bv : INT_MAX, (double)bd + (double)bb};
+  return WalkCand{best * 0x1.0p-10f, best > -INFINITY ? bv : INT_MAX, (double)bd + (double)bb};
 }
 
 __device__ __forceinline__ WalkTop2 wtop2_empty() { return WalkTop2{-INFINITY, INT_MAX, -INFINITY, INT_MAX, 0.0, 0.0}; }
