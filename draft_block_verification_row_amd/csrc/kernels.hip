@@ -2098,11 +2098,13 @@ __device__ __forceinline__ WalkTop2 walk_top2_4lanes(const WalkCand& c) {
 // group g, from their draft logits xr and clocks clk; written to tpart / race [g][b].
 // csrc: when not null, the clocks are first copied into clk from there (another
 // workgroup computed them: coherent loads, issued with the block's other loads).
+// sums: whether the partials' sums are formed (only log q needs them; the race and the
+// greedy branch's maxima do not); without, a partial is (max, 1).
 // Every thread of the workgroup calls it.
 template <int DT, int KS, bool MARKOV, bool VEC>
 __device__ __forceinline__ void walk_block(const Args& a, int g, int j, int r0, const WalkLane& wl,
                                            const Raw16<DT> (&xr)[kWalkChunks], const bf16x8 (&A)[4][KS],
-                                           WalkRowsLds<KS, MARKOV>& L, WalkClocks& clk,
+                                           WalkRowsLds<KS, MARKOV>& L, WalkClocks& clk, bool sums,
                                            const uint2* csrc = nullptr) {
   const int tid = opaque_tid(), w = tid >> 6, l = tid & 63, n = l & 15, q = l >> 4;
   uint2 cw[kWalkChunks * 4];
@@ -2172,7 +2174,15 @@ __device__ __forceinline__ void walk_block(const Args& a, int g, int j, int r0, 
     for (int e = 0; e < 16; ++e) x[e] += bias[e];
     if (wl.rag) mask_shift(x, wl.shift);
     const float c = L.c[rr];
-    const float2 pw = row_partial<0>(x, c);
+    float2 pw;
+    if (sums) {   // uniform
+      pw = row_partial<0>(x, c);
+    } else {
+      float m = x[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) m = fmaxf(m, x[e]);
+      pw = make_float2(max4lanes(m), 1.f);
+    }
     // race scores of q_j: y c - log2 E with y c = log2 of the weight on the row's scale
 #pragma unroll
     for (int e = 0; e < 16; ++e) x[e] = (VEC || wl.c0 + e < a.V) ? x[e] : -INFINITY;
@@ -2295,17 +2305,18 @@ __device__ __forceinline__ void walk_pick_body(const Args& a, int b, int j, int3
   } else {
     const double invT = 1.0 / (double)Tf;
     const double c = kLog2e * invT;
+    const bool want = logq_out != nullptr;   // the normaliser is for log q only
     // a group's log weight for the normaliser: m_g / T + ln s_g
     auto lw = [&](float2 p) { return p.x != -INFINITY ? (double)p.x * invT + ln_split(p.y) : -INFINITY; };
-    const double lw0 = lw(p0), lw1 = lw(p1);
+    const double lw0 = want ? lw(p0) : -INFINITY, lw1 = want ? lw(p1) : -INFINITY;
     float best = fmaxf(t0.s1, t1.s1);
     double lm = fmax(lw0, lw1);
     for (int gi = tid + 2 * kThreads; gi < NG; gi += kThreads) {
       best = fmaxf(best, ld_c(&race[(size_t)gi * ND + b]).s1);
-      lm = fmax(lm, lw(ld_c(&a.ws.tpart[(size_t)gi * ND + b])));
+      if (want) lm = fmax(lm, lw(ld_c(&a.ws.tpart[(size_t)gi * ND + b])));
     }
     best = wave_max_dpp(best);
-    lm = wave_max_f64(lm);
+    if (want) lm = wave_max_f64(lm);
     if (tid == 0) L.n = 0;
     if (l == 0) {
       L.best[w] = best;
@@ -2334,10 +2345,12 @@ __device__ __forceinline__ void walk_pick_body(const Args& a, int b, int j, int3
       const WalkTop2 t = ld_c(&race[(size_t)gi * ND + b]);
       offer(t.s1, t.v1, t.y1);
       offer(t.s2, t.v2, t.y2);
-      const double lg = lw(ld_c(&a.ws.tpart[(size_t)gi * ND + b]));
-      if (lg != -INFINITY) sum += exp_neg(lg - lm);
+      if (want) {
+        const double lg = lw(ld_c(&a.ws.tpart[(size_t)gi * ND + b]));
+        if (lg != -INFINITY) sum += exp_neg(lg - lm);
+      }
     }
-    sum = wave_sum(sum);
+    if (want) sum = wave_sum(sum);
     if (l == 0) L.red[w] = sum;
     __syncthreads();
     const int nc = min(L.n, kMaxCand);
@@ -2370,7 +2383,7 @@ __device__ __forceinline__ void walk_pick_body(const Args& a, int b, int j, int3
 
 // Two launches per slot: the partial part (one workgroup per group), then the draws.
 template <int DT, int KS, bool MARKOV, bool VEC>
-__global__ __launch_bounds__(kThreads, 2) void walk_partials_kernel(Args a, int j) {
+__global__ __launch_bounds__(kThreads, 2) void walk_partials_kernel(Args a, int j, bool sums) {
   __shared__ WalkRowsLds<KS, MARKOV> L;
   __shared__ WalkClocks clk;
   const int g = blockIdx.x;
@@ -2386,7 +2399,7 @@ __global__ __launch_bounds__(kThreads, 2) void walk_partials_kernel(Args a, int 
       walk_load_rows<DT, VEC>(a, j, r0, wl.c0, xr);
       walk_fill_clocks(a, j, r0, wl.c0, clk);
     }
-    walk_block<DT, KS, MARKOV, VEC>(a, g, j, r0, wl, xr, A, L, clk);
+    walk_block<DT, KS, MARKOV, VEC>(a, g, j, r0, wl, xr, A, L, clk, sums);
   }
 }
 
@@ -2446,7 +2459,7 @@ __global__ __launch_bounds__(kThreads, 2) void walk_fused_kernel(Args a, int32_t
         walk_fill_clocks(a, j, r0, wl.c0, clk);
       }
       // the first block's clocks of a drawing workgroup were computed by the others
-      walk_block<DT, KS, MARKOV, VEC>(a, g, j, r0, wl, xr, A, L, clk,
+      walk_block<DT, KS, MARKOV, VEC>(a, g, j, r0, wl, xr, A, L, clk, logq_out != nullptr,
                                       (picker && j > 0 && NO > 0 && r0 == 0) ? pbuf(j, g) : nullptr);
     }
     const int ph1 = 2 * j + 1, ph2 = 2 * j + 2;
@@ -2837,7 +2850,8 @@ static hipError_t launch_walk_t(const Args& a, int32_t* tokens_out, double* logq
   }
   if (a.ws.tpart == nullptr || a.ws.race == nullptr) return hipErrorInvalidValue;
   for (int j = 0; j < a.k; ++j) {
-    hipLaunchKernelGGL((walk_partials_kernel<DT, KS, MARKOV, VEC>), dim3(a.NG), dim3(kThreads), 0, st, a, j);
+    hipLaunchKernelGGL((walk_partials_kernel<DT, KS, MARKOV, VEC>), dim3(a.NG), dim3(kThreads), 0, st, a, j,
+                       logq_out != nullptr);
     hipLaunchKernelGGL((walk_pick_kernel<DT, KS>), dim3(a.B), dim3(kThreads), 0, st, a, j, tokens_out, logq_out);
   }
   return hipGetLastError();

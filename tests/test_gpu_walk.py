@@ -151,6 +151,13 @@ def test_walk_launch_plans_agree(mod, monkeypatch, B, k, V, dtype, R, greedy_eve
             toks, lq = mod.draft_sample(seed=11, step=step, logq=True, **kw)
             torch.cuda.synchronize()
             got[plan] = (n, toks.cpu(), lq.cpu())
+        # without log q the partials skip their sums: the draws must not change (either plan)
+        for plan in ("separate", "resident"):
+            if plan == "resident":
+                monkeypatch.delenv("DSPARK_WALK_LAUNCH", raising=False)
+            toks_nolq, none = mod.draft_sample(seed=11, step=step, logq=False, **kw)
+            torch.cuda.synchronize()
+            assert none is None and torch.equal(toks_nolq.cpu(), got[plan][1]), (plan, step)
         assert got["resident"][0] == 2, got["resident"][0]
         assert got["separate"][0] == 2 * k
         assert torch.equal(got["resident"][1], got["separate"][1]), (step, got["resident"][1], got["separate"][1])
