@@ -281,7 +281,7 @@ struct Workspace {
   uint32_t* rowmask;  // [B]           pass-2 rows of each stream (bit i = slot i)
   Item* items;        // [B*k]         pass-2 list: residual rows from the front, bonus rows from the back
   int32_t* nitems;    // [kCounterInts] list counts and work counters (see kQueues)
-  uint4* btile;       // [ceil(B*k/16)][R/32][64] W1 tiles of pass 2's rows in MFMA lane order
+  uint4* btile;       // [ceil(B*k/16)][R/32][64] W1 tiles of every draft row in MFMA lane order (pass 1)
   Top2* race;         // [NG][B*k]       race candidates of the pass-2 rows (by list index); the walk:
                       //                 [NG][B] WalkTop2
   uint2* clk;         // [B][NG*64]      race clocks of sampled streams: log2 E in units of 2^-10 as

@@ -1,14 +1,15 @@
-// gfx950 kernels of the DSpark verify sampler.
+// gfx950 kernels of the DSpark verify sampler and the drafter's walk.
 //
 // Sources (page titles): [P1] "MTP, DSpark and Block Verification, Explained";
 // [P2] "MTP Heads and Confidence Heads"; [P3] "Teaching the Speculator What a Draft Costs".
 //
-// A call is five launches on one stream:
+// A verify call is a pack launch and then either one resident launch of one workgroup
+// per 256-id group (all resident; its four phases below are separated by grid-wide
+// waits) or the same four phases as four launches:
 //   pack      the B operand of the Markov product [P2 §6; P1 §3 "The Markov fix-up"]:
 //             W1[prev] of every draft row, 16 rows per tile, stored in MFMA lane
 //             order so that a wave reads one k-step of a tile as one contiguous
-//             1 KB load (gathering W1 rows per wave is the slow part otherwise);
-//             clears the counters of the launches below.
+//             1 KB load; clears the counters of the launches below.
 //   pass1     one workgroup per 256-id vocabulary group g.  Draft rows (slots
 //             0..gamma_b-1): each wave keeps its 64 columns of W2 as MFMA A operands,
 //             streams the packed W1 tiles through the B operand (staged in LDS) and
@@ -19,14 +20,19 @@
 //   scan      one workgroup per stream: the logits at the draft tokens (bias in
 //             fp64), row normalisers from the partials (fp64), log p_j(x_j),
 //             log q_j(x_j), the token-wise stop and the clipped prefix P_i [P1 §4],
-//             and the rows whose residual mass is needed.  Block verification needs
-//             R_i only where u_{i-1} <= P_i (h_i <= P_i always), plus the row the
-//             sampler may land on.  The scan also packs the W1 tiles of those rows.
+//             and the list of rows pass 2 needs.  Block verification needs R_i only
+//             where u_{i-1} <= P_i (h_i <= P_i always), plus the row the sampler may
+//             land on.  The workgroups without a stream compute the race clocks
+//             meanwhile (int16 log2 E of every id of every sampled stream).
 //   pass2     like the draft half of pass1 over the listed rows only: per group,
-//             the residual mass sum max(0, P_i p_i - q_i) (Markov bias recomputed).
-//   finalize  one workgroup per stream: R_i, h_i, tau (top-down), then the
-//             two-level exponential race over group masses and within the winning
-//             group (weights recomputed in fp64), and the outputs.
+//             the residual mass sum max(0, P_i p_i - q_i) (Markov bias recomputed)
+//             and the two best race candidates (score log2 w - log2 E).
+//   finalize  one workgroup per stream: R_i, h_i, tau (top-down), then the one-level
+//             exponential race: the best group candidate, every candidate within a
+//             window of it scored again in fp64; the outputs.
+// The walk is one resident launch for its k slots (or two launches per slot): per
+// slot, group partials and race candidates of the biased draft logits, then one
+// workgroup per stream draws x_j.
 //
 // Partials are group-major ([group or segment][row]): a stream's rows are adjacent,
 // so the per-stream scan and finalize read short contiguous runs.  Full windows take
@@ -339,15 +345,6 @@ __global__ __launch_bounds__(64) void pack_kernel(Args a) {
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk)
     if (kk < ks) dst[kk * 64] = pv >= 0 ? v[kk] : make_uint4(0, 0, 0, 0);
-}
-
-// One k-step slice of a packed tile per lane: the B operand of 16 rows (tiles the scan
-// wrote for pass 2: coherent loads).
-template <int KS>
-__device__ __forceinline__ void load_btile(const Args& a, int c, int l, bf16x8 (&B)[KS]) {
-  const uint4* t = a.ws.btile + (size_t)c * KS * 64 + l;
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) B[kk] = __builtin_bit_cast(bf16x8, ld_c(&t[kk * 64]));
 }
 
 // x + bias at the lane's row and 16 columns: A = this wave's W2 slab, B = a packed
