@@ -585,9 +585,11 @@ __device__ __forceinline__ int claim_add(int* p) {
   return __hip_atomic_fetch_add(reinterpret_cast<global_int*>(v), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// An item is 16 U rows of one group: 32 rows (measured at the headline shape: 64-row
+// items end the phase less evenly, 16-row items keep too few loads in flight).
 template <int DT>
 struct TargetQueue {
-  static constexpr int U = DT == kBF16 ? 4 : 2;
+  static constexpr int U = 2;
   static constexpr int kRS = kThreads / 16;      // rows per step
   static constexpr int kItemRows = kRS * U;
   int* slot;   // LDS [2]: the claimed index, seen by the whole workgroup
