@@ -1231,7 +1231,10 @@ __device__ __forceinline__ Top2 race16_row(const float (&y)[16], const uint2 (&L
     const uint32_t word = (e & 2) ? L[e >> 2].y : L[e >> 2].x;
     const int q = (e & 1) ? ((int32_t)word >> 16) : ((int32_t)(word << 16) >> 16);
     const float lq = (float)q * 0x1.0p-10f;
-    const float sc = bonus ? y[e] - lq : (y[e] > 0.f ? __builtin_amdgcn_logf(y[e]) - lq : -INFINITY);
+    // computed on every lane and selected (a branch per id costs more than the log):
+    // a residual weight is +0 or positive and log2(+0) = -inf
+    const float lg = __builtin_amdgcn_logf(y[e]);
+    const float sc = (bonus ? y[e] : lg) - lq;
     const bool better = sc > best;
     best = better ? sc : best;
     bv = better ? c0 + e : bv;
