@@ -69,7 +69,7 @@ class Problem:
             tpart=self.NG * self.NT, dpart=self.NG * self.ND, wgrp=self.NG * self.ND,
             tm=self.NT, tl2s=self.NT, dm=self.ND, dl2s=self.ND, logP=self.NT, lpx=self.ND, lqx=self.ND,
             info=4 * B, info2=4 * B, rowmask=B, items=self.ND, nitems=K_QUEUE_STRIDE * (1 + K_QUEUES),
-            btile=tiles * 8 * 64, race=self.NG * self.ND, sync=K_SYNC_INTS,
+            btile=tiles * 8 * 64, race=self.NG * self.ND, sync=K_SYNC_INTS, clk=B * self.NG * 64,
             accepted_len=B, out_tokens=self.NT, diag=self.NT * 5))
 
     # the device's per-stream readers ---------------------------------------------
@@ -416,6 +416,42 @@ def replay_finalize(p: Problem, b, method, stop_mask, s_base, bonus_slot, diag=T
 
 
 # ---------------------------------------------------------------------------
+# race clocks: written by the workgroups with no stream to scan, read by pass 2
+# ---------------------------------------------------------------------------
+def replay_clock_rows(p: Problem, nslots):
+    """clock_rows of every slot: an equal share of the B NG rows, 4 rows per wave per turn."""
+    rows = p.B * p.NG
+    per = (rows + nslots - 1) // nslots
+    for slot in range(nslots):
+        r0, r1 = slot * per, min(slot * per + per, rows)
+        for w in range(K_WAVES):
+            for rb in range(r0 + 4 * w, r1, 4 * K_WAVES):
+                b, grp = divmod(rb, p.NG)
+                for u in range(4):
+                    if u > 0:
+                        grp += 1
+                        while grp >= p.NG:
+                            grp -= p.NG
+                            b += 1
+                    if rb + u < r1:
+                        for l in range(64):
+                            p.mem.at("clk", min(b, p.B - 1) * p.NG * 64 + grp * 64 + l)
+
+
+def replay_pass2_clocks(p: Problem, streams):
+    """load_clocks of every lane of every group, for the streams pass 2 races."""
+    for b in streams:
+        sb = min(max(b, 0), p.B - 1)
+        for g in range(p.NG):
+            for w in range(K_WAVES):
+                for q in range(4):
+                    cw = (g * K_WAVES + w) * K_WAVE_COLS + 16 * q
+                    c0 = min(cw, p.V - 16) if p.vec else cw
+                    for i in range(4):
+                        p.mem.at("clk", sb * p.NG * 64 + (c0 >> 2) + i)
+
+
+# ---------------------------------------------------------------------------
 # a whole call: list slots assigned as the scan's atomics would, worst cases first
 # ---------------------------------------------------------------------------
 def replay_call(p: Problem, method, rng, fused_grid=0):
@@ -446,6 +482,10 @@ def replay_call(p: Problem, method, rng, fused_grid=0):
         replay_scan(p, b, method, (s, m), base, bonus)
         base += bin(m).count("1")
     replay_pass2(p, NI, NB, item_rows)
+    replay_clock_rows(p, p.NG)   # the separate scan launch: NG workgroups past the B scanning ones
+    if fused_grid > 0:           # the fused launch: the workgroups with no stream, else all of them
+        replay_clock_rows(p, fused_grid - p.B if fused_grid > p.B else fused_grid)
+    replay_pass2_clocks(p, [-1, 0, p.B - 1, p.B + 3])   # the record's stream is clamped
     for b, (s, m) in enumerate(choices):
         replay_finalize(p, b, method, (s, m), slots[b][0], slots[b][1])
     return p.mem
