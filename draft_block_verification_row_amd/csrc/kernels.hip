@@ -1159,6 +1159,15 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(Args a) {
   scan_body<DT>(a, blockIdx.x, L);
 }
 
+// threadIdx.x through a register the compiler cannot see into: index math formed from
+// it inside a loop is recomputed there (a few VALU) instead of being kept live across
+// the loop, where it would take registers or spill.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // ---------------------------------------------------------------------------
 // Race candidates.  The sampler draws Y = argmax_v w_v / E_v over the whole
 // vocabulary, one Exp(1) clock per id (an exponential race picks v with probability
@@ -1320,9 +1329,10 @@ __device__ __forceinline__ void pass2_body(const Args& a, int g, Pass2Lds& L, bf
   int32_t words[3];
   const int32_t* item_words = reinterpret_cast<const int32_t*>(a.ws.items);
   auto load_words = [&](int c) {
+    const int lo = opaque_tid() & 63;
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
-      const int e = l + 64 * u;   // record e / 12 of the chunk, word e % 12 (compile-time per u and l range)
+      const int e = lo + 64 * u;   // record e / 12 of the chunk, word e % 12
       const int r = min(c * kChunk + e / kItemWords, ND - 1);
       words[u] = ld_c(item_words + (size_t)item_of(r) * kItemWords + e % kItemWords);
     }
@@ -1428,6 +1438,11 @@ __device__ __forceinline__ void pass2_body(const Args& a, int g, Pass2Lds& L, bf
     // row: y = x log2(e) / T (unnormalised: every group of the row uses the same scale,
     // which is all the race needs).  Straight from the raw logits (the buffers are
     // refilled after); then the race over them.
+    // The sum takes every lane's weight times 0 or 1 (a bonus row's sum is never read),
+    // so that the weight is needed on every lane and is computed without a branch on
+    // the kind of row: the lanes of a chunk mix kinds, and a branch per id costs more
+    // than the work it would skip.
+    const float res = bonus ? 0.f : 1.f;
     float s = 0.f;
     float y[16];
 #pragma unroll
@@ -1442,14 +1457,15 @@ __device__ __forceinline__ void pass2_body(const Args& a, int g, Pass2Lds& L, bf
       const bool in = VEC || c0 + e < a.V;
       const float wr = (in && wv > 0.f) ? wv : 0.f;
       y[e] = bonus ? (in ? xte * (k0.z + k0.w) : -INFINITY) : wr;
-      s += bonus ? 0.f : wr;
+      s = fmaf(res, wr, s);
     }
     fetch(rows_of(c + 2), tb, db);
     s = sum4lanes(s);
     const Top2 rt = top2_4lanes(race16_row(y, ck, bonus, c0));
     if (q == 0) {
-      part[(c % kFlush) * kChunk + n][w] = s;
-      rpart[(c % kFlush) * kChunk + n][w] = rt;
+      const int t = opaque_tid(), rr = (c % kFlush) * kChunk + (t & 15), ww = t >> 6;
+      part[rr][ww] = s;
+      rpart[rr][ww] = rt;
     }
     if (c % kFlush == kFlush - 1 || c == nch - 1) {
       __syncthreads();
@@ -1935,11 +1951,6 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(Args a) {
 // ---------------------------------------------------------------------------
 // threadIdx.x through an empty asm: values derived from it are computed where they are
 // used instead of being kept live (and spilled) across the walk's slot loop.
-__device__ __forceinline__ int opaque_tid() {
-  int t = threadIdx.x;
-  asm volatile("" : "+v"(t));
-  return t;
-}
 constexpr int kWalkRows = 64;                      // streams per block of the partial part
 constexpr int kWalkChunks = kWalkRows / kChunk;    // MFMA chunks per block
 
