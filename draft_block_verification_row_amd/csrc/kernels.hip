@@ -1953,11 +1953,11 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(Args a) {
 // used instead of being kept live (and spilled) across the walk's slot loop.
 constexpr int kWalkRows = 64;                      // streams per block of the partial part
 constexpr int kWalkChunks = kWalkRows / kChunk;    // MFMA chunks per block
+static_assert(kThreads == 4 * kWalkRows, "a block's candidates are merged by one quad of threads per row");
 
 template <int KS, bool MARKOV>
 struct WalkRowsLds {
   float2 part[kWalkRows][kWaves];
-  WalkTop2 rpart[kWalkRows][kWaves];
   int prev[kWalkRows];
   float c[kWalkRows];
   uint4 w1s[MARKOV ? kWalkRows * (4 * KS + 1) : 1];   // W1 rows, padded stride
@@ -2080,31 +2080,17 @@ __device__ __forceinline__ void wtop2_merge(WalkTop2& a, const WalkTop2& o) {
   wtop2_add(a, o.s1, o.v1, o.y1);
   wtop2_add(a, o.s2, o.v2, o.y2);
 }
-// The best two of the candidates of lanes {n, n+16, n+32, n+48} (row swaps, as
-// top2_4lanes); every lane of the four ends with the same result.
-__device__ __forceinline__ WalkTop2 walk_top2_4lanes(const WalkCand& c) {
-  auto sw16 = [](uint32_t x) { return __builtin_amdgcn_permlane16_swap(x, x, false, false); };
-  auto sw32 = [](uint32_t x) { return __builtin_amdgcn_permlane32_swap(x, x, false, false); };
-  WalkTop2 t = wtop2_empty();
-  {
-    const auto s = sw16(__float_as_uint(c.s));
-    const auto v = sw16((uint32_t)c.v);
-    const auto lo = sw16((uint32_t)__double2loint(c.y));
-    const auto hi = sw16((uint32_t)__double2hiint(c.y));
-    wtop2_add(t, __uint_as_float(s[0]), (int)v[0], __hiloint2double((int)hi[0], (int)lo[0]));
-    wtop2_add(t, __uint_as_float(s[1]), (int)v[1], __hiloint2double((int)hi[1], (int)lo[1]));
-  }
-  const auto s1 = sw32(__float_as_uint(t.s1));
-  const auto v1 = sw32((uint32_t)t.v1);
-  const auto s2 = sw32(__float_as_uint(t.s2));
-  const auto v2 = sw32((uint32_t)t.v2);
-  const auto y1l = sw32((uint32_t)__double2loint(t.y1)), y1h = sw32((uint32_t)__double2hiint(t.y1));
-  const auto y2l = sw32((uint32_t)__double2loint(t.y2)), y2h = sw32((uint32_t)__double2hiint(t.y2));
-  WalkTop2 r{__uint_as_float(s1[0]), (int)v1[0], __uint_as_float(s2[0]), (int)v2[0],
-             __hiloint2double((int)y1h[0], (int)y1l[0]), __hiloint2double((int)y2h[0], (int)y2l[0])};
-  wtop2_merge(r, WalkTop2{__uint_as_float(s1[1]), (int)v1[1], __uint_as_float(s2[1]), (int)v2[1],
-                          __hiloint2double((int)y1h[1], (int)y1l[1]), __hiloint2double((int)y2h[1], (int)y2l[1])});
-  return r;
+// The best two of a quad's best twos (lanes 4r .. 4r + 3: DPP xor 1, then xor 2); every
+// lane of the quad ends with the same set.
+template <int CTRL>
+__device__ __forceinline__ WalkTop2 wtop2_dpp(const WalkTop2& t) {
+  return WalkTop2{dppf<CTRL>(t.s1), dppi<CTRL>(t.v1), dppf<CTRL>(t.s2), dppi<CTRL>(t.v2), dppd<CTRL>(t.y1),
+                  dppd<CTRL>(t.y2)};
+}
+__device__ __forceinline__ WalkTop2 walk_top2_quad(WalkTop2 t) {
+  wtop2_merge(t, wtop2_dpp<0xB1>(t));
+  wtop2_merge(t, wtop2_dpp<0x4E>(t));
+  return t;
 }
 
 // Group partials (max, sum) and race candidates of slot j for rows r0 .. r0 + 63 of
@@ -2202,23 +2188,33 @@ __device__ __forceinline__ void walk_block(const Args& a, int g, int j, int r0, 
     uint2 ck[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) ck[i] = clk[cc][i][tid];
-    const WalkTop2 rt = walk_top2_4lanes(walk_race16<DT>(x, bias, xr[cc], ck, c, wl.c0));
-    if (q == 0) {
-      L.part[rr][w] = pw;
-      L.rpart[rr][w] = rt;
-    }
+    // the lane's best id of the chunk goes into two of its own clock slots, read above
+    // and dead from here: (score, id) and y
+    const WalkCand wc = walk_race16<DT>(x, bias, xr[cc], ck, c, wl.c0);
+    clk[cc][0][tid] = make_uint2(__float_as_uint(wc.s), (uint32_t)wc.v);
+    clk[cc][1][tid] = make_uint2((uint32_t)__double2loint(wc.y), (uint32_t)__double2hiint(wc.y));
+    if (q == 0) L.part[rr][w] = pw;
     __builtin_amdgcn_sched_barrier(0);   // one chunk's values at a time
   }
   __syncthreads();
+  {   // a row's 16 lane candidates (lanes n + 16 q of the 4 waves): 4 per thread of a quad,
+      // then across the quad; the quad's first thread stores the row's best two
+    const int row = tid >> 2, wv = tid & 3, cc = row >> 4, n = row & 15;
+    WalkTop2 r = wtop2_empty();
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int t = 64 * wv + 16 * qq + n;
+      const uint2 sv = clk[cc][0][t], yy = clk[cc][1][t];
+      wtop2_add(r, __uint_as_float(sv.x), (int)sv.y, __hiloint2double((int)yy.y, (int)yy.x));
+    }
+    r = walk_top2_quad(r);
+    if (wv == 0 && r0 + row < a.B) st_c(&reinterpret_cast<WalkTop2*>(a.ws.race)[(size_t)g * a.B + r0 + row], r);
+  }
   if (tid < kWalkRows && r0 + tid < a.B) {
     float2 p[kWaves];
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) p[ww] = L.part[tid][ww];
     st_c(&a.ws.tpart[(size_t)g * a.B + r0 + tid], combine_waves(p, L.c[tid]));
-    WalkTop2 r = L.rpart[tid][0];
-#pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) wtop2_merge(r, L.rpart[tid][ww]);
-    st_c(&reinterpret_cast<WalkTop2*>(a.ws.race)[(size_t)g * a.B + r0 + tid], r);
   }
   __syncthreads();
 }
