@@ -1198,30 +1198,6 @@ __device__ __forceinline__ void top2_merge(Top2& a, const Top2& o) {
   top2_add(a, o.s1, o.v1);
   top2_add(a, o.s2, o.v2);
 }
-// The best two of the 4 lanes {n, n+16, n+32, n+48} (row swaps as in max4lanes); every
-// lane of the four ends with the same result.
-__device__ __forceinline__ Top2 top2_4lanes(Top2 t) {
-  auto swap_merge16 = [](Top2 x) {
-    const auto s1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x.s1), __float_as_uint(x.s1), false, false);
-    const auto v1 = __builtin_amdgcn_permlane16_swap((uint32_t)x.v1, (uint32_t)x.v1, false, false);
-    const auto s2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x.s2), __float_as_uint(x.s2), false, false);
-    const auto v2 = __builtin_amdgcn_permlane16_swap((uint32_t)x.v2, (uint32_t)x.v2, false, false);
-    Top2 r{__uint_as_float(s1[0]), (int)v1[0], __uint_as_float(s2[0]), (int)v2[0]};
-    top2_merge(r, Top2{__uint_as_float(s1[1]), (int)v1[1], __uint_as_float(s2[1]), (int)v2[1]});
-    return r;
-  };
-  auto swap_merge32 = [](Top2 x) {
-    const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x.s1), __float_as_uint(x.s1), false, false);
-    const auto v1 = __builtin_amdgcn_permlane32_swap((uint32_t)x.v1, (uint32_t)x.v1, false, false);
-    const auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x.s2), __float_as_uint(x.s2), false, false);
-    const auto v2 = __builtin_amdgcn_permlane32_swap((uint32_t)x.v2, (uint32_t)x.v2, false, false);
-    Top2 r{__uint_as_float(s1[0]), (int)v1[0], __uint_as_float(s2[0]), (int)v2[0]};
-    top2_merge(r, Top2{__uint_as_float(s1[1]), (int)v1[1], __uint_as_float(s2[1]), (int)v2[1]});
-    return r;
-  };
-  return swap_merge32(swap_merge16(t));
-}
-
 // The race of pass 2's rows, listed or bonus: a lane's best score over its 16 ids
 // c0 .. c0 + 15 in increasing order (a later id replaces an earlier one only with a
 // strictly larger score, so the smaller id wins ties), from 16 clocks L (int16, units
@@ -1229,7 +1205,7 @@ __device__ __forceinline__ Top2 top2_4lanes(Top2 t) {
 // log2 w - log2 E), a bonus row's y are y = x c, the logits scaled to log2 units
 // (-inf: none; score y - log2 E); either way the scores share the row's scale across
 // lanes, waves and groups.  Lanes keep one candidate each and the best two of a row's
-// lanes go on (top2_4lanes, then across waves): two ids of one lane trade places only
+// 16 lanes go on (merged at the flush): two ids of one lane trade places only
 // when their scores agree to the fp32 rounding, which the fp64 check of every
 // candidate near the best does not need.
 __device__ __forceinline__ Top2 race16_row(const float (&y)[16], const uint2 (&L)[4], bool bonus, int c0) {
@@ -1274,7 +1250,7 @@ static_assert(kItemWords == 12, "Item is 12 words: dr, tr, prev, b, Mt, Md, chi,
 constexpr int kStageWords = kChunk * kItemWords;   // one chunk's items: 192 words, 3 per lane
 struct Pass2Lds {
   float part[kFlush * kChunk][kWaves];
-  Top2 rpart[kFlush * kChunk][kWaves];
+  uint2 cand[kFlush * kChunk][17];   // a row's 16 lane candidates (score bits, id); padded
   int32_t items[kWaves][4][kStageWords];    // per wave, the items of chunks c .. c + 2 (ring of 4)
   uint4 btile[2][8 * 64];                   // the W1 tiles of chunks c and c + 1 (R <= 256)
 };
@@ -1302,7 +1278,7 @@ __device__ __forceinline__ void markov_mma_lds(const bf16x8 (&A)[4][KS], const u
 template <int DT, int KS, bool MARKOV, bool VEC>
 __device__ __forceinline__ void pass2_body(const Args& a, int g, Pass2Lds& L, bf16x8 (&A)[4][KS], bool slab_loaded) {
   auto& part = L.part;
-  auto& rpart = L.rpart;
+  auto& cand = L.cand;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, q = l >> 4;
   const int cb = (g * kWaves + w) * kWaveCols;
   const int cw = cb + 16 * q;
@@ -1461,11 +1437,12 @@ __device__ __forceinline__ void pass2_body(const Args& a, int g, Pass2Lds& L, bf
     }
     fetch(rows_of(c + 2), tb, db);
     s = sum4lanes(s);
-    const Top2 rt = top2_4lanes(race16_row(y, ck, bonus, c0));
-    if (q == 0) {
+    // every lane's best id of the chunk goes to LDS; a row's 16 are merged at the flush
+    const Top2 rt = race16_row(y, ck, bonus, c0);
+    {
       const int t = opaque_tid(), rr = (c % kFlush) * kChunk + (t & 15), ww = t >> 6;
-      part[rr][ww] = s;
-      rpart[rr][ww] = rt;
+      cand[rr][4 * ww + ((t & 63) >> 4)] = make_uint2(__float_as_uint(rt.s1), (uint32_t)rt.v1);
+      if (q == 0) part[rr][ww] = s;
     }
     if (c % kFlush == kFlush - 1 || c == nch - 1) {
       __syncthreads();
@@ -1476,9 +1453,12 @@ __device__ __forceinline__ void pass2_body(const Args& a, int g, Pass2Lds& L, bf
           const int dr = min(max(ld_c(&a.ws.items[it].dr), 0), ND - 1);
           st_c(&a.ws.wgrp[(size_t)g * ND + dr], (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]));
         }
-        Top2 r = rpart[tid][0];
+        Top2 r = top2_empty();
 #pragma unroll
-        for (int ww = 1; ww < kWaves; ++ww) top2_merge(r, rpart[tid][ww]);
+        for (int u = 0; u < 16; ++u) {
+          const uint2 e = cand[tid][u];
+          top2_add(r, __uint_as_float(e.x), (int)e.y);
+        }
         st_c(&a.ws.race[(size_t)g * ND + it], r);
       }
       __syncthreads();
