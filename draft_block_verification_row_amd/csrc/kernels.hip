@@ -1446,17 +1446,18 @@ __device__ __forceinline__ void pass2_body(const Args& a, int g, Pass2Lds& L, bf
     }
     if (c % kFlush == kFlush - 1 || c == nch - 1) {
       __syncthreads();
-      const int i = (c - c % kFlush) * kChunk + tid;
-      if (tid < (c % kFlush + 1) * kChunk && i < NV) {
+      const int t = opaque_tid();   // addresses formed here, not kept through the loop
+      const int i = (c - c % kFlush) * kChunk + t;
+      if (t < (c % kFlush + 1) * kChunk && i < NV) {
         const int it = item_of(i);
         if (i < NI) {
           const int dr = min(max(ld_c(&a.ws.items[it].dr), 0), ND - 1);
-          st_c(&a.ws.wgrp[(size_t)g * ND + dr], (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]));
+          st_c(&a.ws.wgrp[(size_t)g * ND + dr], (part[t][0] + part[t][1]) + (part[t][2] + part[t][3]));
         }
         Top2 r = top2_empty();
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-          const uint2 e = cand[tid][u];
+          const uint2 e = cand[t][u];
           top2_add(r, __uint_as_float(e.x), (int)e.y);
         }
         st_c(&a.ws.race[(size_t)g * ND + it], r);
