@@ -688,7 +688,7 @@ __device__ __forceinline__ void pass1_target(const Args& a, const StreamTable& s
 }
 
 
-// LDS of pass 1: the wave partials of a flush, the staged W1 tiles (64 KB at R = 256)
+// LDS of pass 1: the wave partials of a flush, the staged W1 tiles (32 KB at R = 256)
 // and the item claim slots; the per-stream table (8 bytes a stream) lives in the
 // launch's dynamic LDS.
 template <int KS, bool MARKOV>
