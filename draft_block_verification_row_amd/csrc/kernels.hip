@@ -2136,6 +2136,12 @@ __device__ __forceinline__ void walk_block(const Args& a, int g, int j, int r0, 
 #pragma unroll
   for (int cc = 0; cc < kWalkChunks; ++cc) {
     const int rr = cc * kChunk + n;   // row within the block
+    // two workgroups share a CU with the same chunks: the waves' issue priority falls
+    // with each chunk done, so the one behind catches up (as in pass 2)
+    if (cc == 0) __builtin_amdgcn_s_setprio(3);
+    else if (cc == 1) __builtin_amdgcn_s_setprio(2);
+    else if (cc == 2) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
     float x[16], bias[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) bias[e] = 0.f;
@@ -2183,6 +2189,7 @@ __device__ __forceinline__ void walk_block(const Args& a, int g, int j, int r0, 
     if (q == 0) L.part[rr][w] = pw;
     __builtin_amdgcn_sched_barrier(0);   // one chunk's values at a time
   }
+  __builtin_amdgcn_s_setprio(0);
   __syncthreads();
   {   // a row's 16 lane candidates (lanes n + 16 q of the 4 waves): 4 per thread of a quad,
       // then across the quad; the quad's first thread stores the row's best two
