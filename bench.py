@@ -40,8 +40,8 @@ STAGE_NAMES = ["pack W1 tiles", "pass1 row statistics", "scan", "pass2 residual 
 # (FETCH_SIZE, then WRITE_SIZE; profiles/verify_and_walk_headline_b64_k5_v129280_hbm_bytes.md),
 # each scaled by what the same counter reads for a plain device copy of known size.
 # Valid only for the kernel sources it was measured on (hash below); otherwise null.
-FUSED_TRAFFIC = {"src_sha256_16": "777125b63abef686", "fetch_bytes": 150751.7 * 1024 * 2.0,
-                 "write_bytes": 22279.2 * 1024 * 1.0}
+FUSED_TRAFFIC = {"src_sha256_16": "c4fe6c6e194a7707", "fetch_bytes": 150728.2 * 1024 * 2.0,
+                 "write_bytes": 22296.3 * 1024 * 1.0}
 
 
 def kernel_src_hash() -> str:
