@@ -325,7 +325,7 @@ def main() -> int:
     ap.add_argument("--sets", type=int, default=3, help="rotating copies of the input set")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration table")
-    ap.add_argument("--config-calls", type=int, default=100)
+    ap.add_argument("--config-calls", type=int, default=200)
     ap.add_argument("--verify-only", action="store_true",
                     help="time the verify calls only (no read ceiling, walk, scheduler, table or host "
                          "baseline): for profiler runs")
@@ -399,7 +399,7 @@ def main() -> int:
     # per-launch times: a pass with the library's stage events around every launch of
     # each call (pack, then the fused verify launch, or the four separate launches)
     hip = HipEvents()
-    nprof = min(args.steps, 50)
+    nprof = min(args.steps, 200)
     s0 = sets[0]
     plan = dv.verify_launches(s0["target"], s0["draft"], s0["tokens"], temperature=s0["temp"], W1=s0["W1"],
                               W2t=s0["W2t"], anchor=s0["anchor"])
